@@ -1,0 +1,85 @@
+"""Pure-Python brute force of the MoE layer for tiny inputs (no NumPy arithmetic).
+
+TEST INFRASTRUCTURE (see the package docstring).
+
+It evaluates the "wasteful" form that Zero to Frontier §13.1 uses to check its
+worked example ("A worked example small enough to check by hand"): run every
+expert on every token and multiply the unchosen ones by a zero gate.  It is an
+independent second implementation of the same definition: nested loops over
+Python floats, ``math.exp``, a selection loop for the top-k, and a per-expert
+arrival counter for the capacity rule, so a NumPy slip in the main oracle (a
+transposed operand, a wrong axis, a dropped term) cannot repeat here.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _matvec(W, v):
+    """W [out][in] times v [in]."""
+    return [sum(W[o][i] * v[i] for i in range(len(v))) for o in range(len(W))]
+
+
+def _silu(z):
+    return z / (1.0 + math.exp(-z)) if z > -700 else 0.0
+
+
+def _expert(Wg, Wu, Wd, x):
+    a = _matvec(Wg, x)
+    b = _matvec(Wu, x)
+    h = [_silu(a[n]) * b[n] for n in range(len(a))]
+    return _matvec(Wd, h)
+
+
+def moe_dense_bruteforce(x, w_r, experts, k, cap=-1, b_r=None, renormalize=True, shared=None):
+    """Returns (y, idx, gates) as nested lists.
+
+    x [T][d]; w_r [E][d]; experts[e] = (Wg [d_e][d], Wu [d_e][d], Wd [d][d_e]);
+    b_r [E] or None.  cap < 0: unlimited.
+    """
+    T = len(x)
+    E = len(w_r)
+    d = len(x[0]) if T else 0
+    ys, idxs, gs = [], [], []
+    seen = [0] * E
+    for t in range(T):
+        logits = [sum(w_r[e][i] * x[t][i] for i in range(d)) + (b_r[e] if b_r is not None else 0.0)
+                  for e in range(E)]
+        mx = max(logits)
+        ex = [math.exp(v - mx) for v in logits]
+        s = sum(ex)
+        p = [v / s for v in ex]
+        chosen = []
+        for _ in range(k):                        # selection, lowest index on ties
+            best = -1
+            for e in range(E):
+                if e in chosen:
+                    continue
+                if best < 0 or p[e] > p[best]:
+                    best = e
+            chosen.append(best)
+        if renormalize:
+            z = sum(p[e] for e in chosen)
+            g_sel = [p[e] / z for e in chosen]
+        else:
+            g_sel = [p[e] for e in chosen]
+        # dense gate vector: zero for unchosen experts and for dropped assignments
+        gate_full = [0.0] * E
+        for j, e in enumerate(chosen):
+            rank = seen[e]
+            seen[e] += 1
+            if cap < 0 or rank < cap:
+                gate_full[e] = g_sel[j]
+        y = [0.0] * d
+        for e in range(E):                        # every expert runs
+            out = _expert(*experts[e], x[t])
+            for i in range(d):
+                y[i] += gate_full[e] * out[i]
+        if shared is not None:
+            out = _expert(*shared, x[t])
+            for i in range(d):
+                y[i] += out[i]
+        ys.append(y)
+        idxs.append(chosen)
+        gs.append(g_sel)
+    return ys, idxs, gs

@@ -1,0 +1,309 @@
+"""Float64 oracle of the forward pass of one sparse MoE FFN layer.
+
+TEST INFRASTRUCTURE (see the package docstring): only tests, the smoke check and
+the benchmark's CPU-baseline leg use this module.
+
+The layer, in the notation of Zero to Frontier §13.1 "Why MoE", section "The MoE
+layer": for a token row x (the output of the pre-FFN norm), a linear router
+gives one logit per expert, r = x W_r; the k largest logits form the set K; the
+chosen experts get weights g_i that sum to one; the layer returns
+sum_{i in K} g_i FFN_i(x), where each expert is a SwiGLU network
+FFN_i(x) = (SiLU(x W_g^i) * x W_u^i) W_d^i.  Unchosen experts are never run.
+
+Storage follows the PyTorch layer of the kevinluzbetak.com "Mixture-Of-Experts"
+page (nn.Linear keeps [out, in]): W_r is [E, d], W_g and W_u are [d_e, d] per
+expert, W_d is [d, d_e] per expert, so r = x @ W_r.T and so on.
+
+Readings taken where the pages leave a step open (each is listed with its reason
+in the design notes of the repository):
+  * top-k ties: the lower expert index wins; slots are ordered by descending
+    probability (the PyTorch layer's ``topk`` order), so slot 0 is the top-1 choice.
+  * softmax over all E, then top-k, then renormalise over the k (the
+    kevinluzbetak.com routing paragraph) -- equal in exact arithmetic to the
+    softmax over the k chosen logits of the "The MoE layer" gate equation.
+  * ``renormalize=False`` keeps the raw softmax probability as the gate (the
+    Switch top-1 variant, and the "skip the renormalisation" remark of the
+    kevinluzbetak.com router worked example).
+  * capacity: each expert keeps at most ``cap`` assignments; assignments are
+    taken in arrival order t*k + j and the rest are dropped.  A dropped
+    assignment contributes nothing; a surviving gate is not renormalised; a
+    token whose every assignment is dropped gets y = 0 (plus the shared expert),
+    the caller's residual carrying it through.
+  * f_e counts every one of the k choices before capacity, divided by T*k;
+    P_e is the mean over all T tokens of the full softmax; aux = E * sum f_e P_e
+    (the auxiliary-loss code of the kevinluzbetak.com layer, without alpha).
+  * SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)) (the pages name it, not define it).
+  * a shared expert is added with weight one, outside routing, capacity and
+    the statistics.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+NEAR_TIE = 1e-6
+
+
+# --------------------------------------------------------------------------- router
+
+def router_logits(x: np.ndarray, w_r: np.ndarray, b_r: np.ndarray | None = None) -> np.ndarray:
+    """r = x W_r (+ b): one logit per expert per token.
+
+    Zero to Frontier §13.1, "The MoE layer": the router is one linear map d -> E.
+    The optional per-expert bias b (float32 in storage) is added to the logits
+    before the softmax; it is part of the logits for selection, gates and P.
+    """
+    r = np.asarray(x, np.float64) @ np.asarray(w_r, np.float64).T
+    if b_r is not None:
+        r = r + np.asarray(b_r, np.float64)[None, :]
+    return r
+
+
+def softmax(r: np.ndarray) -> np.ndarray:
+    """p = softmax(r) over the expert axis, computed with the row max subtracted.
+
+    kevinluzbetak.com "Mixture-Of-Experts", routing paragraph: p = softmax(h W_r)
+    over the E experts.  Subtracting the row maximum changes nothing in exact
+    arithmetic and keeps exp finite.
+    """
+    m = r.max(axis=1, keepdims=True)
+    e = np.exp(r - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def top_k(p: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k most probable experts per token, int32 [T, k].
+
+    A stable sort on -p keeps equal probabilities in ascending expert order, so
+    the lower index wins a tie and slot 0 is the most probable expert.
+    """
+    order = np.argsort(-p, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def gates(p: np.ndarray, idx: np.ndarray, renormalize: bool = True) -> np.ndarray:
+    """g[t, j] for the chosen experts idx[t, j].
+
+    renormalize: g = p_i / sum_{j in K} p_j (kevinluzbetak.com routing paragraph;
+    Zero to Frontier "The MoE layer" gate equation, e^{r_i} / sum_K e^{r_j}).
+    Otherwise g = p_i (the raw-probability variant).
+    """
+    sel = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    if renormalize:
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    return sel
+
+
+def near_ties(p: np.ndarray, k: int, threshold: float = NEAR_TIE) -> np.ndarray:
+    """Tokens whose k-th and (k+1)-th largest probabilities differ by < threshold.
+
+    For these tokens the choice between the two experts is decided by rounding,
+    so a different but equally valid order is accepted and only reported.
+    """
+    T, E = p.shape
+    if k >= E:
+        return np.zeros(0, dtype=np.int64)
+    s = -np.sort(-p, axis=1)
+    return np.nonzero(s[:, k - 1] - s[:, k] < threshold)[0]
+
+
+# --------------------------------------------------------------------------- statistics
+
+def load_balance_stats(p: np.ndarray, idx: np.ndarray, E: int):
+    """(counts, f, P, aux) of the Switch auxiliary term.
+
+    kevinluzbetak.com "Mixture-Of-Experts", load-balancing fixes and the PyTorch
+    layer's auxiliary-loss lines: f_e is the fraction of assignments dispatched
+    to e, P_e the mean router probability of e, aux = E * sum_e f_e P_e, which is
+    smallest under uniform routing and equals 1 when routing is balanced.
+    counts are taken over all k choices, before any capacity drop.
+    """
+    T, k = idx.shape
+    counts = np.bincount(idx.ravel().astype(np.int64), minlength=E).astype(np.int64)
+    R = T * k
+    f = counts / R if R > 0 else np.zeros(E)
+    P = p.mean(axis=0) if T > 0 else np.zeros(E)
+    aux = float(E * np.sum(f * P))
+    return counts, f, P, aux
+
+
+def capacity(T: int, k: int, E: int, C: float) -> int:
+    """Per-expert slot count floor(C * T * k / E).
+
+    Capacity is tokens per batch over experts times a factor (AI Engineering
+    Illustrated, "The safety valve is a capacity limit"; "A hard limit" on the
+    jacopoparretti.dev page).  The kevinluzbetak.com capacity worked example
+    counts top-k slots, C * T * k / E; at k = 1 the two agree.  A non-integer
+    product is rounded down.
+    """
+    return int(math.floor(C * T * k / E))
+
+
+# --------------------------------------------------------------------------- dispatch
+
+@dataclass
+class Dispatch:
+    counts: np.ndarray     # int64 [E] assignments per expert, before capacity
+    kept: np.ndarray       # int64 [E] assignments kept
+    offsets: np.ndarray    # int64 [E+1] exclusive scan of kept
+    row_token: np.ndarray  # int64 [sum kept] token of each expert-ordered row
+    row_of: np.ndarray     # int64 [T, k] row of assignment (t, j), or -1 if dropped
+
+    @property
+    def dropped(self) -> np.ndarray:
+        """Flat indices t*k + j of dropped assignments, ascending."""
+        return np.nonzero(self.row_of.ravel() < 0)[0]
+
+
+def dispatch(idx: np.ndarray, E: int, cap: int = -1) -> Dispatch:
+    """Group assignments by expert in arrival order, keeping at most cap per expert.
+
+    The layer's per-expert token lists (the PyTorch layer's ``nonzero`` per
+    expert) laid out as one expert-contiguous list.  Within an expert, rows are in
+    ascending t*k + j.  cap < 0 means no limit.
+    """
+    T, k = idx.shape
+    flat = idx.ravel().astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    kept = counts.copy() if cap < 0 else np.minimum(counts, cap)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    row_of = np.full(T * k, -1, dtype=np.int64)
+    row_token = np.full(int(offsets[-1]), -1, dtype=np.int64)
+    seen = np.zeros(E, dtype=np.int64)
+    for a in range(T * k):                      # arrival order
+        e = flat[a]
+        rank = seen[e]
+        seen[e] += 1
+        if cap < 0 or rank < cap:
+            row = offsets[e] + rank
+            row_of[a] = row
+            row_token[row] = a // k
+    return Dispatch(counts, kept, offsets, row_token, row_of.reshape(T, k))
+
+
+# --------------------------------------------------------------------------- experts
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z})."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(X: np.ndarray, w_g: np.ndarray, w_u: np.ndarray, w_d: np.ndarray) -> np.ndarray:
+    """FFN(X) = (SiLU(X W_g) * (X W_u)) W_d for rows X [m, d]; weights stored [out, in].
+
+    Zero to Frontier §13.1, "The MoE layer" (each expert is a SwiGLU network);
+    the kevinluzbetak.com layer's SwiGLU module (w1 = gate, w3 = up, w2 = down).
+    """
+    X = np.asarray(X, np.float64)
+    a = X @ np.asarray(w_g, np.float64).T
+    b = X @ np.asarray(w_u, np.float64).T
+    return (silu(a) * b) @ np.asarray(w_d, np.float64).T
+
+
+# --------------------------------------------------------------------------- layer
+
+@dataclass
+class Result:
+    y: np.ndarray          # [T, d] layer output (without the residual)
+    logits: np.ndarray     # [T, E]
+    p: np.ndarray          # [T, E]
+    idx: np.ndarray        # int32 [T, k]
+    gate: np.ndarray       # [T, k]
+    counts: np.ndarray
+    f: np.ndarray
+    P: np.ndarray
+    aux: float
+    disp: Dispatch
+    near_tie: np.ndarray   # token indices
+
+
+def route(x, w_r, k: int, b_r=None, renormalize: bool = True, idx=None):
+    """Router half of the layer: logits, p, idx, gates (idx may be forced)."""
+    r = router_logits(x, w_r, b_r)
+    p = softmax(r)
+    if idx is None:
+        idx = top_k(p, k)
+    g = gates(p, idx, renormalize)
+    return r, p, np.asarray(idx, np.int32), g
+
+
+def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: bool = True,
+                shared=None, idx=None) -> Result:
+    """The whole layer.
+
+    experts: sequence (or any object with ``__getitem__`` and ``__len__``) whose
+    item e is (W_g, W_u, W_d) of expert e in float64-convertible form.  The loop
+    runs over experts, one batch of that expert's kept rows at a time, the shape
+    of the readable PyTorch layer (Zero to Frontier, "In PyTorch").
+    shared: (W_g, W_u, W_d) of an always-on expert added with weight 1, or None.
+    idx: forced routing (int [T, k]); when given, gates are computed for it.
+    """
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    E = len(experts)
+    r, p, idx, g = route(x, w_r, k, b_r, renormalize, idx)
+    counts, f, P, aux = load_balance_stats(p, idx, E)
+    disp = dispatch(idx, E, cap)
+    R_kept = int(disp.offsets[-1])
+    O = np.zeros((R_kept, d), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(disp.offsets[e]), int(disp.offsets[e + 1])
+        if hi == lo:
+            continue                              # unchosen experts never run
+        toks = disp.row_token[lo:hi]
+        wg, wu, wd = experts[e]
+        O[lo:hi] = swiglu_ffn(x[toks], wg, wu, wd)
+    y = np.zeros((T, d), dtype=np.float64)
+    for j in range(k):                            # fixed slot order
+        rows = disp.row_of[:, j]
+        keep = rows >= 0
+        y[keep] += g[keep, j:j + 1] * O[rows[keep]]
+    if shared is not None:
+        y += swiglu_ffn(x, *shared)
+    return Result(y=y, logits=r, p=p, idx=idx, gate=g, counts=counts, f=f, P=P, aux=aux,
+                  disp=disp, near_tie=near_ties(p, k))
+
+
+def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared=None) -> np.ndarray:
+    """y for a few tokens, one token at a time, from their routing.
+
+    x_rows [n, d]; idx_rows, gate_rows, kept_rows [n, k] (kept: bool).  expert_of(e)
+    returns (W_g, W_u, W_d).  Evaluates sum_j kept * g_j FFN_{idx_j}(x) directly:
+    the per-token form of the layer, used to check sampled rows at full size.
+    """
+    x_rows = np.asarray(x_rows, np.float64)
+    n, d = x_rows.shape
+    y = np.zeros((n, d))
+    need: dict[int, list] = {}
+    for t in range(n):
+        for j in range(idx_rows.shape[1]):
+            if kept_rows[t, j]:
+                need.setdefault(int(idx_rows[t, j]), []).append((t, j))
+    contrib = np.zeros((n, idx_rows.shape[1], d))
+    for e, tj in sorted(need.items()):
+        wg, wu, wd = expert_of(e)
+        ts = [t for t, _ in tj]
+        out = swiglu_ffn(x_rows[ts], wg, wu, wd)
+        for (t, j), row in zip(tj, out):
+            contrib[t, j] = float(gate_rows[t, j]) * row
+    for j in range(idx_rows.shape[1]):            # fixed slot order
+        y += contrib[:, j]
+    if shared is not None:
+        y += swiglu_ffn(x_rows, *shared)
+    return y
+
+
+def rel_err(y, y_ref) -> float:
+    """max |y - y_ref| / rms(y_ref): the output tolerance measure."""
+    y = np.asarray(y, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    rms = math.sqrt(float(np.mean(y_ref * y_ref))) if y_ref.size else 0.0
+    if y_ref.size == 0:
+        return 0.0
+    if rms == 0.0:
+        return float(np.max(np.abs(y - y_ref)))
+    return float(np.max(np.abs(y - y_ref)) / rms)

@@ -1,0 +1,63 @@
+"""Parameter and FLOP arithmetic of MoE decoders.
+
+TEST INFRASTRUCTURE (see the package docstring).
+
+Zero to Frontier §13.1, "Total and active parameters": one MoE layer with E
+SwiGLU experts of width d_e, a bias-free d x E router and k experts per token
+stores 3 d d_e E + d E parameters and uses 3 d d_e k + d E per token.  The
+whole-model count follows the page's exercise "Total and active parameters of an
+MoE model": every FFN and expert is a bias-free SwiGLU, each layer has two
+RMSNorm gains of size d, one final norm, shared experts are always active, the
+first n_dense layers keep a dense FFN of width d_ff, and embedding matrices are
+counted in full in both numbers (one matrix if tied, two otherwise).
+
+FLOPs: "FLOPs per token, and the 6N rule for MoE" and the dense-vs-MoE table of
+the "In PyTorch" section give 2 FLOPs per active matrix parameter per token
+forward, i.e. 6 d d_e k + 2 d E for one MoE layer's experts and router.
+"""
+from __future__ import annotations
+
+
+def layer_params(d: int, d_e: int, E: int, k: int) -> tuple[int, int]:
+    """(total, active) of one MoE layer's experts plus its router."""
+    return 3 * d * d_e * E + d * E, 3 * d * d_e * k + d * E
+
+
+def moe_param_count(cfg: dict) -> tuple[int, int]:
+    """(total, active) parameters of a whole decoder described by cfg.
+
+    cfg keys: V, d, L, attn (attention parameters per layer), n_dense, d_ff, E,
+    E_shared, k, d_e, tied.
+    """
+    V, d, L = cfg["V"], cfg["d"], cfg["L"]
+    attn, n_dense, d_ff = cfg["attn"], cfg.get("n_dense", 0), cfg.get("d_ff", 0)
+    E, Es, k, d_e = cfg["E"], cfg.get("E_shared", 0), cfg["k"], cfg["d_e"]
+    norms = 2 * d
+    dense_layer = attn + 3 * d * d_ff + norms
+    moe_total = attn + 3 * d * d_e * (E + Es) + d * E + norms
+    moe_active = attn + 3 * d * d_e * (k + Es) + d * E + norms
+    emb = V * d * (1 if cfg.get("tied", False) else 2)
+    n_moe = L - n_dense
+    total = n_dense * dense_layer + n_moe * moe_total + emb + d
+    active = n_dense * dense_layer + n_moe * moe_active + emb + d
+    return total, active
+
+
+def forward_flops_per_token(d: int, d_e: int, E: int, k: int, d_e_shared: int = 0) -> int:
+    """Forward FLOPs of one MoE layer per token: 6 d d_e k + 2 d E (+ 6 d d_e_shared)."""
+    return 6 * d * d_e * k + 2 * d * E + 6 * d * d_e_shared
+
+
+def router_flops_per_token(d: int, E: int) -> int:
+    """2 d E: the router's share, paid in full by every token."""
+    return 2 * d * E
+
+
+def train_flops(n_active: float, tokens: float) -> float:
+    """6 N_active D: training compute of an MoE model on D tokens."""
+    return 6.0 * n_active * tokens
+
+
+def flops_ratio(n_total: float, n_active: float) -> float:
+    """How many times more compute a dense model of n_total parameters needs."""
+    return n_total / n_active

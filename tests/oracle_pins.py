@@ -1,0 +1,363 @@
+"""Pins of the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+something outside itself: a number printed on a page (tests/golden), a closed
+form, an invariant the pages state, a library routine in a special case that
+reduces to it, or the pure-Python brute force.  ``test_oracle.py`` runs them;
+``test_oracle_mutations.py`` plants mistakes in the oracle and checks that at
+least one pin fails for each.
+
+Functions reach the oracle through module attributes (``mo.softmax`` ...) so that
+a planted mistake is seen by every pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from math import comb
+
+import numpy as np
+
+from oracle import bruteforce as bf
+from oracle import moe_oracle as mo
+from oracle import param_count as pc
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _logit_inputs(logits):
+    """x = e_0 and W_r[:, 0] = logits, so x W_r^T reproduces the logits exactly."""
+    logits = np.asarray(logits, np.float64)
+    E = logits.size
+    d = 4
+    x = np.zeros((1, d))
+    x[0, 0] = 1.0
+    w_r = np.zeros((E, d))
+    w_r[:, 0] = logits
+    # fill the other columns with values that x does not see
+    w_r[:, 1:] = np.arange(E * (d - 1)).reshape(E, d - 1) * 0.37
+    return x, w_r
+
+
+def _tiny_layer(seed, T=5, d=6, d_e=4, E=5, bias=False, shared=False, scale=1.0):
+    g = _rng(seed)
+    x = g.standard_normal((T, d)) * scale
+    w_r = g.standard_normal((E, d))
+    experts = [(g.standard_normal((d_e, d)) * 0.7, g.standard_normal((d_e, d)) * 0.7,
+                g.standard_normal((d, d_e)) * 0.7) for _ in range(E)]
+    b_r = g.standard_normal(E) if bias else None
+    sh = None
+    if shared:
+        sh = (g.standard_normal((3, d)), g.standard_normal((3, d)), g.standard_normal((d, 3)))
+    return x, w_r, experts, b_r, sh
+
+
+# --------------------------------------------------------------------------- printed examples
+
+def pin_router_worked_examples():
+    for ex in GOLDEN["router_examples"]:
+        if "logits" in ex:
+            logits = ex["logits"]
+        else:
+            logits = [0.0] * ex["E"]
+            for e, v in ex["top_logits"].items():
+                logits[int(e)] = v
+        x, w_r = _logit_inputs(logits)
+        r, p, idx, g = mo.route(x, w_r, ex["k"])
+        assert list(idx[0]) == ex["experts"], (ex["source"], idx[0])
+        tol = 0.5 * 10 ** (-ex["decimals"])
+        assert np.allclose(g[0], ex["gates"], atol=tol + 1e-12), (ex["source"], g[0])
+        if "probs" in ex:
+            assert np.allclose(p[0], ex["probs"], atol=tol + 1e-12), (ex["source"], p[0])
+        # closed form for k = 2: g_0 = 1 / (1 + e^{-(r_a - r_b)})
+        ra, rb = logits[ex["experts"][0]], logits[ex["experts"][1]]
+        assert abs(g[0, 0] - 1.0 / (1.0 + math.exp(-(ra - rb)))) < 1e-14
+
+
+def pin_capacity_worked_example():
+    c = GOLDEN["capacity_example"]
+    cap = mo.capacity(c["T"], c["k"], c["E"], c["C"])
+    assert cap == c["slots"], cap
+    # Build the routing the page describes: 3000 of the 4096 tokens choose expert 0
+    # (as one of their two experts); the rest spread over the others.
+    T, E, k = c["T"], c["E"], c["k"]
+    idx = np.zeros((T, k), np.int32)
+    for t in range(T):
+        if t < c["chosen_by"]:
+            idx[t] = (0, 1 + t % 3)
+        else:
+            idx[t] = (1 + t % 3, 1 + (t + 1) % 3)
+    disp = mo.dispatch(idx, E, cap)
+    assert disp.counts[0] == c["chosen_by"]
+    assert disp.counts[0] - disp.kept[0] == c["overflow"]
+    # arrival order: the first `cap` of expert 0's assignments survive
+    assert np.all(disp.row_of[:cap, 0] >= 0) and np.all(disp.row_of[cap:c["chosen_by"], 0] == -1)
+    # the capacity rule at the Switch-style workload: 1.25 * 8192 / 64 = 160
+    assert mo.capacity(8192, 1, 64, 1.25) == 160
+    assert mo.capacity(10, 1, 4, 1.0) == 2        # 2.5 rounds down
+
+
+def pin_param_counts():
+    for name, pcnt in GOLDEN["param_counts"].items():
+        total, active = pc.moe_param_count(pcnt["cfg"])
+        assert total == pcnt["total"], (name, total)
+        assert active == pcnt["active"], (name, active)
+    m = GOLDEN["param_counts"]["mixtral"]
+    cfg = m["cfg"]
+    assert 2 * 4096 ** 2 + 2 * 4096 * 1024 == cfg["attn"]
+    lt, la = pc.layer_params(cfg["d"], cfg["d_e"], cfg["E"], cfg["k"])
+    assert lt == m["eight_experts"] + m["router"]
+    assert lt + cfg["attn"] + m["norms_per_layer"] == m["per_layer"]
+    assert la + cfg["attn"] + m["norms_per_layer"] == m["active_per_layer"]
+    assert pc.layer_params(cfg["d"], cfg["d_e"], 1, 1)[0] - cfg["d"] == m["one_expert"]
+    ds = GOLDEN["param_counts"]["deepseek_v3"]
+    assert pc.layer_params(7168, 2048, 1, 1)[0] - 7168 == ds["one_expert"]
+
+
+def pin_flop_arithmetic():
+    f = GOLDEN["flops"]["router_vs_experts"]
+    router = pc.router_flops_per_token(f["d"], f["E"])
+    experts = pc.forward_flops_per_token(f["d"], f["d_e"], f["E"], f["experts_run"]) - router
+    assert abs(router - f["router_approx"]) / f["router_approx"] < 0.01, router
+    assert abs(experts - f["experts_approx"]) / f["experts_approx"] < 0.001, experts
+    assert 0.004 < router / experts < 0.006                       # "half a percent"
+    fw = GOLDEN["flops"]["forward_per_token"]
+    # 2 FLOPs per active matrix parameter: one layer's count equals 2 * its active params
+    d, de, E, k = 4096, 14336, 8, 2
+    assert pc.forward_flops_per_token(d, de, E, k) == 2 * pc.layer_params(d, de, E, k)[1]
+    assert abs(2 * fw["n_active"] / 1e9 - fw["gflops"]) < 1e-9
+    tr = GOLDEN["flops"]["train"]
+    moe = pc.train_flops(tr["n_active"], tr["tokens"])
+    dense = pc.train_flops(tr["n_total"], tr["tokens"])
+    assert abs(moe - tr["moe_flops"]) / tr["moe_flops"] < 0.02
+    assert abs(dense - tr["dense_flops"]) / tr["dense_flops"] < 0.01
+    assert round(pc.flops_ratio(tr["n_total"], tr["n_active"])) == tr["ratio"]
+
+
+def pin_combinatorics():
+    c = GOLDEN["combinatorics"]
+    assert comb(8, 2) == c["c_8_2"]
+    assert abs(comb(8, 2) ** 32 / c["paths_mixtral_approx"] - 1) < 0.1
+    assert comb(256, 8) == c["c_256_8"]
+
+
+# --------------------------------------------------------------------------- library routines / closed forms
+
+def pin_softmax_library():
+    import scipy.special
+    g = _rng(1)
+    r = g.standard_normal((7, 9)) * 5
+    assert np.allclose(mo.softmax(r), scipy.special.softmax(r, axis=1), rtol=1e-13, atol=0)
+    # large logits stay finite (max subtraction)
+    big = np.array([[1000.0, 999.0, -1000.0]])
+    p = mo.softmax(big)
+    assert np.all(np.isfinite(p)) and abs(p[0, 0] - 1 / (1 + math.exp(-1))) < 1e-14
+
+
+def pin_silu():
+    import torch
+    z = np.linspace(-30, 30, 241)
+    ref = torch.nn.functional.silu(torch.tensor(z, dtype=torch.float64)).numpy()
+    assert np.allclose(mo.silu(z), ref, rtol=1e-14, atol=1e-300)
+    assert mo.silu(np.array([0.0]))[0] == 0.0
+    assert abs(mo.silu(np.array([1.0]))[0] - 1 / (1 + math.exp(-1))) < 1e-15
+
+
+def pin_dense_swiglu_special_case():
+    """E = 1, k = 1: the layer is one dense SwiGLU FFN (gate 1)."""
+    import torch
+    g = _rng(2)
+    T, d, de = 6, 5, 7           # non-square everywhere, so a transposed operand fails
+    x = g.standard_normal((T, d))
+    w_r = g.standard_normal((1, d))
+    wg, wu, wd = g.standard_normal((de, d)), g.standard_normal((de, d)), g.standard_normal((d, de))
+    res = mo.moe_forward(x, w_r, [(wg, wu, wd)], k=1)
+    tx = torch.tensor(x)
+    lin = torch.nn.functional.linear
+    ref = lin(torch.nn.functional.silu(lin(tx, torch.tensor(wg))) * lin(tx, torch.tensor(wu)),
+              torch.tensor(wd)).numpy()
+    assert np.allclose(res.y, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(res.gate == 1.0) and np.all(res.idx == 0)
+    assert np.allclose(mo.swiglu_ffn(x, wg, wu, wd), ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- invariants
+
+def pin_gates_sum_to_one():
+    x, w_r, experts, b_r, _ = _tiny_layer(3, T=40, E=7, bias=True)
+    for k in (1, 2, 3, 7):
+        _, p, idx, g = mo.route(x, w_r, k, b_r)
+        assert np.allclose(g.sum(axis=1), 1.0, atol=1e-14)
+        assert np.all(np.diff(g, axis=1) <= 1e-15)       # slots in descending gate order
+        # chosen experts are the k most probable
+        thr = np.take_along_axis(p, idx.astype(np.int64), axis=1).min(axis=1)
+        for t in range(p.shape[0]):
+            others = np.delete(p[t], idx[t])
+            assert np.all(others <= thr[t] + 0.0)
+
+
+def pin_tie_break():
+    """W_r = 0: every logit is 0, so experts 0..k-1 win with gates 1/k and P = 1/E."""
+    g = _rng(4)
+    T, d, E = 9, 6, 6
+    x = g.standard_normal((T, d))
+    w_r = np.zeros((E, d))
+    for k in (1, 2, 4):
+        _, p, idx, gt = mo.route(x, w_r, k)
+        assert np.all(idx == np.arange(k)[None, :])
+        assert np.allclose(gt, 1.0 / k, atol=1e-15)
+        counts, f, P, aux = mo.load_balance_stats(p, idx, E)
+        assert np.allclose(P, 1.0 / E, atol=1e-15)
+    # a tie between two non-top experts also goes to the lower index
+    x1, w1 = _logit_inputs([0.5, 1.0, 0.5, 0.5, 2.0])
+    _, _, idx, _ = mo.route(x1, w1, 3)
+    assert list(idx[0]) == [4, 1, 0]
+
+
+def pin_aux_balanced():
+    """T = m E, W_r = c [I | 0], x_t = e_{t mod E}: f = P = 1/E and aux = 1 exactly."""
+    E, m, d, c = 8, 5, 11, 3.0
+    T = m * E
+    x = np.zeros((T, d))
+    for t in range(T):
+        x[t, t % E] = 1.0
+    w_r = np.zeros((E, d))
+    w_r[:, :E] = c * np.eye(E)
+    _, p, idx, _ = mo.route(x, w_r, 1)
+    counts, f, P, aux = mo.load_balance_stats(p, idx, E)
+    assert np.all(counts == m)
+    assert np.allclose(f, 1.0 / E, atol=1e-15) and np.allclose(P, 1.0 / E, atol=1e-15)
+    assert abs(aux - 1.0) < 1e-14
+    # unbalanced routing has aux > 1: everything to expert 0
+    x0 = np.zeros((T, d))
+    x0[:, 0] = 1.0
+    _, p0, idx0, _ = mo.route(x0, w_r, 1)
+    assert mo.load_balance_stats(p0, idx0, E)[3] > 1.5
+    # f counts all k choices: sums to 1 at any k, and is 1/E when k = E
+    x2, w2, _, _, _ = _tiny_layer(5, T=30, E=6)
+    _, pE, iE, _ = mo.route(x2, w2, 6)
+    assert np.allclose(mo.load_balance_stats(pE, iE, 6)[1], 1.0 / 6, atol=1e-15)
+    for k in (1, 2, 3):
+        _, p2, i2, _ = mo.route(x2, w2, k)
+        assert abs(mo.load_balance_stats(p2, i2, 6)[1].sum() - 1.0) < 1e-14
+        assert np.allclose(mo.load_balance_stats(p2, i2, 6)[2], p2.mean(axis=0))
+
+
+def pin_near_ties():
+    x, w_r = _logit_inputs([1.0, 1.0 + 5e-7, 0.0, 1.0 + 1e-5])
+    _, p, _, _ = mo.route(x, w_r, 2)
+    # p is about 0.3 for the three near-equal logits: the 2nd/3rd gap (experts 1
+    # and 0) is about 1.5e-7 < 1e-6, the 1st/2nd gap about 2.8e-6 > 1e-6
+    assert list(mo.near_ties(p, 2)) == [0]
+    assert list(mo.near_ties(p, 1)) == []
+    x2, w2 = _logit_inputs([3.0, 1.0, 0.0])
+    _, p2, _, _ = mo.route(x2, w2, 1)
+    assert list(mo.near_ties(p2, 1)) == [] and list(mo.near_ties(p2, 3)) == []
+
+
+def pin_dispatch_invariants():
+    g = _rng(6)
+    for (T, E, k, cap) in [(50, 5, 2, -1), (50, 5, 2, 7), (33, 4, 3, 0), (64, 8, 1, 5), (0, 3, 2, 4)]:
+        idx = np.stack([g.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), np.int32)
+        d = mo.dispatch(idx, E, cap)
+        assert d.counts.sum() == T * k
+        assert np.all(d.kept <= (d.counts if cap < 0 else np.minimum(d.counts, cap)))
+        assert int(d.kept.sum()) + d.dropped.size == T * k
+        assert d.offsets[0] == 0 and np.all(np.diff(d.offsets) == d.kept)
+        # each kept row holds its token, rows of an expert are in arrival order
+        for e in range(E):
+            rows = []
+            for a in range(T * k):
+                t, j = divmod(a, k)
+                if idx[t, j] == e and d.row_of[t, j] >= 0:
+                    rows.append((a, d.row_of[t, j]))
+            rr = [r for _, r in rows]
+            assert rr == list(range(d.offsets[e], d.offsets[e + 1]))
+            for a, r in rows:
+                assert d.row_token[r] == a // k
+        # dropped = beyond the first cap arrivals of each expert
+        seen = np.zeros(E, int)
+        for a in range(T * k):
+            t, j = divmod(a, k)
+            e = idx[t, j]
+            assert (d.row_of[t, j] < 0) == (cap >= 0 and seen[e] >= cap)
+            seen[e] += 1
+
+
+def pin_bruteforce_agreement():
+    """Sparse oracle == pure-Python dense evaluation with zero gates (tiny inputs)."""
+    cases = [
+        dict(seed=7, T=5, d=6, d_e=4, E=5, k=2, cap=-1),
+        dict(seed=8, T=6, d=5, d_e=3, E=4, k=1, cap=-1, bias=True),
+        dict(seed=9, T=8, d=4, d_e=5, E=3, k=2, cap=3),
+        dict(seed=10, T=7, d=3, d_e=2, E=6, k=3, cap=2, shared=True),
+        dict(seed=11, T=4, d=4, d_e=4, E=4, k=4, cap=-1, renorm=False),
+        dict(seed=12, T=6, d=5, d_e=3, E=5, k=2, cap=0),
+    ]
+    for c in cases:
+        x, w_r, experts, b_r, sh = _tiny_layer(c["seed"], T=c["T"], d=c["d"], d_e=c["d_e"], E=c["E"],
+                                               bias=c.get("bias", False), shared=c.get("shared", False))
+        renorm = c.get("renorm", True)
+        res = mo.moe_forward(x, w_r, experts, c["k"], c["cap"], b_r, renorm, sh)
+        yb, ib, gb = bf.moe_dense_bruteforce(x.tolist(), w_r.tolist(),
+                                             [tuple(m.tolist() for m in ex) for ex in experts],
+                                             c["k"], c["cap"], None if b_r is None else b_r.tolist(),
+                                             renorm, None if sh is None else tuple(m.tolist() for m in sh))
+        assert np.array_equal(res.idx, np.array(ib)), c
+        assert np.allclose(res.gate, np.array(gb), rtol=0, atol=1e-14), c
+        assert np.allclose(res.y, np.array(yb), rtol=1e-12, atol=1e-12), c
+        if c["cap"] == 0:
+            # every assignment dropped: only the shared expert (absent here) remains
+            assert np.all(res.y == 0.0)
+
+
+def pin_upcycling():
+    """E identical experts: y = FFN(x) for any router, since gates sum to one."""
+    g = _rng(13)
+    T, d, de, E = 12, 6, 5, 4
+    x = g.standard_normal((T, d))
+    w_r = g.standard_normal((E, d))
+    ex = (g.standard_normal((de, d)), g.standard_normal((de, d)), g.standard_normal((d, de)))
+    ref = mo.swiglu_ffn(x, *ex)
+    for k in (1, 2, 4):
+        res = mo.moe_forward(x, w_r, [ex] * E, k)
+        assert np.allclose(res.y, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_wide_ffn_identity():
+    """A wide SwiGLU cut into E consecutive hidden blocks sums back to the wide FFN
+    (Zero to Frontier, 'An MoE layer is a wide FFN with blocks switched off');
+    with W_r = 0 and k = E every gate is 1/E, so y = FFN_wide(x) / E."""
+    g = _rng(14)
+    T, d, E, de = 5, 6, 4, 3
+    dff = E * de
+    x = g.standard_normal((T, d))
+    Wg, Wu, Wd = g.standard_normal((dff, d)), g.standard_normal((dff, d)), g.standard_normal((d, dff))
+    wide = mo.swiglu_ffn(x, Wg, Wu, Wd)
+    experts = [(Wg[i * de:(i + 1) * de], Wu[i * de:(i + 1) * de], Wd[:, i * de:(i + 1) * de]) for i in range(E)]
+    assert np.allclose(sum(mo.swiglu_ffn(x, *e) for e in experts), wide, rtol=1e-12, atol=1e-12)
+    res = mo.moe_forward(x, np.zeros((E, d)), experts, k=E)
+    assert np.allclose(res.y, wide / E, rtol=1e-12, atol=1e-12)
+
+
+def pin_per_token_path():
+    """outputs_for_tokens (per-token form) agrees with the expert-loop form."""
+    x, w_r, experts, b_r, sh = _tiny_layer(15, T=9, E=5, bias=True, shared=True)
+    res = mo.moe_forward(x, w_r, experts, 2, 3, b_r, True, sh)
+    sel = [0, 3, 8]
+    y = mo.outputs_for_tokens(x[sel], res.idx[sel], res.gate[sel], res.disp.row_of[sel] >= 0,
+                              lambda e: experts[e], sh)
+    assert np.allclose(y, res.y[sel], rtol=1e-12, atol=1e-12)
+
+
+def pin_rel_err():
+    a = np.array([[3.0, -4.0]])
+    assert abs(mo.rel_err(a + np.array([[0.0, 0.1]]), a) - 0.1 / math.sqrt(12.5)) < 1e-15
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,136 @@
+"""Planted mistakes in the CPU oracle must each make at least one pin fail.
+
+The mistakes are planted on the CPU only, by replacing one oracle function at a
+time (pytest's monkeypatch restores it afterwards).  Each models a plausible slip:
+a dropped term, a wrong sign, a wrong axis or index, a transposed operand, a
+wrong tie-break, a wrong capacity rule.
+"""
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import moe_oracle as mo
+
+_orig = {name: getattr(mo, name) for name in
+         ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
+          "capacity", "dispatch", "near_ties"]}
+
+
+def _softmax_no_shift(r):
+    e = np.exp(r)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _softmax_wrong_axis(r):
+    m = r.max(axis=0, keepdims=True)
+    e = np.exp(r - m)
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def _topk_high_index_wins(p, k):
+    E = p.shape[1]
+    order = np.argsort(-p[:, ::-1], axis=1, kind="stable")
+    return (E - 1 - order[:, :k]).astype(np.int32)
+
+
+def _topk_smallest(p, k):
+    return np.argsort(p, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def _topk_unsorted_slots(p, k):
+    return np.sort(_orig["top_k"](p, k), axis=1).astype(np.int32)
+
+
+def _gates_never_renorm(p, idx, renormalize=True):
+    return _orig["gates"](p, idx, False)
+
+
+def _silu_is_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _silu_sign(z):
+    return z / (1.0 + np.exp(z))
+
+
+def _ffn_no_up(X, w_g, w_u, w_d):
+    return mo.silu(np.asarray(X) @ np.asarray(w_g).T) @ np.asarray(w_d).T
+
+
+def _ffn_swapped(X, w_g, w_u, w_d):
+    return _orig["swiglu_ffn"](X, w_u, w_g, w_d)
+
+
+def _ffn_transposed_down(X, w_g, w_u, w_d):
+    X = np.asarray(X, np.float64)
+    h = mo.silu(X @ np.asarray(w_g).T) * (X @ np.asarray(w_u).T)
+    wd = np.asarray(w_d)
+    return h @ (wd if wd.shape[0] == h.shape[1] else wd.reshape(wd.shape[1], wd.shape[0]))
+
+
+def _router_bias_minus(x, w_r, b_r=None):
+    r = np.asarray(x, np.float64) @ np.asarray(w_r, np.float64).T
+    return r - (0 if b_r is None else np.asarray(b_r)[None, :])
+
+
+def _stats_top1_f(p, idx, E):
+    counts, f, P, aux = _orig["load_balance_stats"](p, idx, E)
+    f = np.bincount(idx[:, 0], minlength=E) / idx.shape[0]
+    return counts, f, P, float(E * np.sum(f * P))
+
+
+def _stats_P_of_chosen(p, idx, E):
+    counts, f, P, aux = _orig["load_balance_stats"](p, idx, E)
+    P = (np.take_along_axis(p, idx.astype(np.int64), axis=1).sum(axis=0).sum() / p.shape[0]) * np.ones(E) / E
+    return counts, f, P, float(E * np.sum(f * P))
+
+
+def _capacity_no_k(T, k, E, C):
+    return int(np.floor(C * T / E))
+
+
+def _capacity_ceil(T, k, E, C):
+    return int(np.ceil(C * T * k / E + 0.5))
+
+
+def _dispatch_keep_last(idx, E, cap=-1):
+    if cap < 0:
+        return _orig["dispatch"](idx, E, cap)
+    rev = _orig["dispatch"](idx[::-1, ::-1].copy(), E, cap)
+    T, k = idx.shape
+    row_of = rev.row_of[::-1, ::-1].copy()
+    return mo.Dispatch(rev.counts, rev.kept, rev.offsets, rev.row_token, row_of)
+
+
+def _dispatch_no_cap(idx, E, cap=-1):
+    return _orig["dispatch"](idx, E, -1)
+
+
+def _near_ties_off_by_one(p, k, threshold=mo.NEAR_TIE):
+    return _orig["near_ties"](p, k + 1 if k + 1 < p.shape[1] else k, threshold)
+
+
+MUTANTS = [
+    ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
+    ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
+    ("gates", _gates_never_renorm),
+    ("silu", _silu_is_sigmoid), ("silu", _silu_sign),
+    ("swiglu_ffn", _ffn_no_up), ("swiglu_ffn", _ffn_swapped), ("swiglu_ffn", _ffn_transposed_down),
+    ("router_logits", _router_bias_minus),
+    ("load_balance_stats", _stats_top1_f), ("load_balance_stats", _stats_P_of_chosen),
+    ("capacity", _capacity_no_k), ("capacity", _capacity_ceil),
+    ("dispatch", _dispatch_keep_last), ("dispatch", _dispatch_no_cap),
+    ("near_ties", _near_ties_off_by_one),
+]
+
+
+@pytest.mark.parametrize("target,mutant", MUTANTS, ids=[m.__name__ for _, m in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, target, mutant):
+    monkeypatch.setattr(mo, target, mutant)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except Exception:            # an assertion or a shape error: either way the pin caught it
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {mutant.__name__} in {target}"
