@@ -1,0 +1,162 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts FFN layer, forward pass.
+ *
+ * The layer (Zero to Frontier §13.1 "Why MoE", section "The MoE layer"; the routing
+ * paragraph of the kevinluzbetak.com "Mixture-Of-Experts" page): for each token row x,
+ *   r = x W_r (+ b)                       one fp32 logit per expert
+ *   p = softmax(r)                        over all E experts, fp32
+ *   K = the k experts with largest r      lower expert index wins a tie
+ *   g_j = p_{K_j} / sum_{i in K} p_i      (renormalize = 1)   or   g_j = p_{K_j} (renormalize = 0)
+ *   y = sum_{j : kept} g_j (SiLU(x W_g^{K_j}) * x W_u^{K_j}) W_d^{K_j}   (+ shared SwiGLU(x))
+ * with an optional per-expert capacity (AI Engineering Illustrated, "The safety valve is a
+ * capacity limit"): each expert keeps its first `capacity` assignments in arrival order
+ * t*k + j; dropped assignments contribute nothing, so a token whose every assignment is
+ * dropped gets y = 0 and the caller's residual carries it through.
+ *
+ * Conventions for every call below
+ *   - Row-major arrays.  Weights are stored [out, in] (nn.Linear), so every product
+ *     reads both operands along the contraction dimension.
+ *   - Element type of x and of every weight: shape->dtype (MOE_F32 or MOE_BF16; bf16 is
+ *     stored as raw 16-bit patterns).  Router bias, gates, f, P, aux, o and y are fp32.
+ *     Indices and counts are int32.
+ *   - Every pointer argument is DEVICE memory owned by the caller, except `shape`
+ *     (host).  The library allocates nothing and keeps no state between calls; scratch
+ *     comes from the caller's workspace `ws` of at least moe_workspace_bytes() bytes.
+ *     Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream); no call
+ *     synchronises the host.
+ *   - Arguments are checked on the host before any HIP call; the first failure is
+ *     returned and nothing is launched.  A failed launch returns MOE_ERR_HIP.  Kernels do
+ *     not report data errors: NaN or Inf inputs, or indices outside [0, E) passed to
+ *     moe_permute, are outside the contract.
+ *   - Results are deterministic: the same inputs give bit-identical outputs (no float
+ *     atomics; integer work is order-free or ordered).
+ *
+ * Supported shapes (else MOE_ERR_UNSUPPORTED or MOE_ERR_SHAPE):
+ *   T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 16); d, d_e, d_e_shared multiples of 128;
+ *   d_e_shared >= 0 (0 = no shared expert); T*k < 2^31; dtype in {MOE_F32, MOE_BF16}.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is negative or inconsistent (k > E, k < 1, ...) */
+  MOE_ERR_UNSUPPORTED = 3, /* valid but outside the supported set above */
+  MOE_ERR_WORKSPACE = 4,   /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef struct {
+  int32_t T;           /* tokens (rows of x) */
+  int32_t d;           /* model width */
+  int32_t d_e;         /* routed expert hidden width */
+  int32_t E;           /* routed experts */
+  int32_t k;           /* experts per token */
+  int32_t capacity;    /* per-expert kept-assignment limit; < 0 = unlimited */
+  int32_t renormalize; /* 1: gates renormalised over the k chosen; 0: raw softmax p */
+  int32_t d_e_shared;  /* hidden width of the always-on shared expert; 0 = none */
+  int32_t dtype;       /* moe_dtype of x and all weights */
+} moe_shape;
+
+/* ---------------------------------------------------------------- host-only helpers
+ * No device access; usable on a machine without a GPU. */
+
+/* Per-expert capacity floor(C * T * k / E) (the kevinluzbetak.com capacity worked
+ * example counts top-k slots; at k = 1 it is AI Engineering Illustrated's
+ * tokens / experts * factor).  Errors: cap NULL -> MOE_ERR_NULL; T < 0, k < 1, E < 1,
+ * C < 0 or not finite, or a result >= 2^31 -> MOE_ERR_SHAPE. */
+moe_status moe_capacity(int32_t T, int32_t k, int32_t E, double C, int32_t *cap);
+
+/* Workspace bytes needed by moe_forward for this shape; the same figure covers each of
+ * the split calls (moe_route, moe_permute, moe_expert_ffn).  Validates the shape. */
+moe_status moe_workspace_bytes(const moe_shape *shape, size_t *bytes);
+
+/* Static string naming a status code. */
+const char *moe_status_str(moe_status status);
+
+/* ---------------------------------------------------------------- device calls */
+
+/* Router: logits, softmax, top-k, gates and the Switch load-balance statistics
+ * (kevinluzbetak.com page, load-balancing fixes and the layer's auxiliary-loss code).
+ *   x      [T, d]        dtype     token rows
+ *   w_r    [E, d]        dtype     router weight
+ *   b_r    [E]           fp32      per-expert logit bias, or NULL
+ *   idx    [T, k]        int32     out: chosen experts, descending gate; idx[:,0] = top-1
+ *   gate   [T, k]        fp32      out: gates
+ *   counts [E]           int32     out: assignments per expert over all k choices, before capacity
+ *   f      [E]           fp32      out: counts / (T*k)      (0 when T = 0)
+ *   P      [E]           fp32      out: mean over tokens of p (0 when T = 0)
+ *   aux    [1]           fp32      out: E * sum_e f_e P_e (no loss weight applied)
+ * Logits, softmax and selection are fp32; bf16 inputs are multiplied exactly and summed
+ * in fp32. */
+moe_status moe_route(const moe_shape *shape, const void *x, const void *w_r, const float *b_r,
+                     int32_t *idx, float *gate, int32_t *counts, float *f, float *P, float *aux,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch: counting sort of the T*k assignments by expert, stable in arrival order
+ * t*k + j, truncated at shape->capacity, then a gather of token rows into
+ * expert-contiguous order (the per-expert token lists of the PyTorch layer on the
+ * kevinluzbetak.com page, laid out as one list; "sort tokens by expert").
+ *   x         [T, d]      dtype     token rows
+ *   idx       [T, k]      int32     expert of each assignment (each in [0, E))
+ *   kept      [E]         int32     out: min(count_e, capacity)
+ *   offsets   [E+1]       int32     out: exclusive scan of kept; offsets[E] = kept rows R
+ *   row_token [T*k]       int32     out: token of expert-ordered row r < R (rest untouched)
+ *   row_of    [T, k]      int32     out: row of assignment (t, j), or -1 if dropped
+ *   x_perm    [T*k, d]    dtype     out: x_perm[r] = x[row_token[r]] for r < R */
+moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *idx, int32_t *kept,
+                       int32_t *offsets, int32_t *row_token, int32_t *row_of, void *x_perm,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped SwiGLU experts over expert-contiguous rows (Zero to Frontier §13.1, "The MoE
+ * layer": FFN_i(x) = (SiLU(x W_g) * x W_u) W_d).  Rows offsets[e] .. offsets[e+1]-1 of
+ * x_perm go through expert e; offsets[E] <= T*k.
+ *   x_perm  [T*k, d]          dtype
+ *   offsets [E+1]             int32
+ *   w_gate  [E, d_e, d]       dtype
+ *   w_up    [E, d_e, d]       dtype
+ *   w_down  [E, d, d_e]       dtype
+ *   o       [T*k, d]          fp32      out: rows < offsets[E]; the rest untouched
+ * The hidden activation is rounded to dtype between the two products (bf16 RNE for
+ * MOE_BF16).  The shared expert is this call with E = 1, k = 1, d_e = d_e_shared and
+ * offsets = {0, T}. */
+moe_status moe_expert_ffn(const moe_shape *shape, const void *x_perm, const int32_t *offsets,
+                          const void *w_gate, const void *w_up, const void *w_down, float *o,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Gate-weighted combine back to token order (the layer's weighted sum,
+ * Zero to Frontier "The MoE layer" equation):
+ *   y[t] = shared_out[t] (or 0) + sum_{j = 0..k-1, row_of[t,j] >= 0} gate[t,j] * o[row_of[t,j]]
+ * summed in that fixed order.
+ *   o [T*k, d] fp32; row_of [T, k] int32; gate [T, k] fp32; shared_out [T, d] fp32 or NULL;
+ *   y [T, d] fp32 out. */
+moe_status moe_combine(const moe_shape *shape, const float *o, const int32_t *row_of,
+                       const float *gate, const float *shared_out, float *y, void *stream);
+
+/* The whole layer: route -> dispatch -> grouped experts (+ shared expert) -> combine.
+ * Arguments as in the split calls; ws_gate/ws_up ([d_e_shared, d]) and ws_down
+ * ([d, d_e_shared]) are the shared expert's weights, required iff d_e_shared > 0.
+ * offsets [E+1], row_token [T*k] and row_of [T, k] are optional outputs (NULL: kept in the
+ * workspace). */
+moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_r, const float *b_r,
+                       const void *w_gate, const void *w_up, const void *w_down,
+                       const void *ws_gate, const void *ws_up, const void *ws_down,
+                       float *y, int32_t *idx, float *gate, int32_t *counts, int32_t *kept,
+                       float *f, float *P, float *aux,
+                       int32_t *offsets, int32_t *row_token, int32_t *row_of,
+                       void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,61 @@
+// Host-side launchers of the gfx950 MoE kernels (internal to the library).
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per router block; also the chunk size of the dispatch counting sort.
+constexpr int kRouteTokens = 16;
+
+inline int route_blocks(int T) { return (T + kRouteTokens - 1) / kRouteTokens; }
+
+// Router: fp32 logits via MFMA, softmax, top-k (lowest index on ties), gates,
+// per-block partial sums of p and per-block expert histograms.
+hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d,
+                         int E, int k, int renorm, int32_t* idx, float* gate, float* p_part,
+                         int32_t* hist, hipStream_t stream);
+
+// Per-chunk expert histograms of an index array (dispatch without the router).
+hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t stream);
+
+// One block: counts, capacity, offsets, per-chunk bases, grouped-GEMM tile starts,
+// and (when p_part != NULL) f, P, aux.
+hipError_t launch_scan(const int32_t* hist, const float* p_part, int nb, int T, int k, int E, int cap,
+                       int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* chunk_base,
+                       float* f, float* P, float* aux, int bm1, int32_t* tstart1, int bm2,
+                       int32_t* tstart2, hipStream_t stream);
+
+// Grouped-GEMM tile starts from row offsets alone.
+hipError_t launch_tile_sched(const int32_t* offsets, int E, int bm1, int32_t* tstart1, int bm2,
+                             int32_t* tstart2, hipStream_t stream);
+
+// Stable ranks within each expert, capacity, row_of / row_token, and the gather
+// x_perm[row] = x[token].
+hipError_t launch_rank_gather(int dtype, const void* x, const int32_t* idx, int T, int d, int k, int E,
+                              int cap, const int32_t* chunk_base, const int32_t* offsets,
+                              int32_t* row_token, int32_t* row_of, void* x_perm, hipStream_t stream);
+
+// y[t] = shared[t] (or 0) + sum_j gate[t,j] * o[row_of[t,j]] over kept slots.
+hipError_t launch_combine(const float* o, const int32_t* row_of, const float* gate, const float* shared,
+                          float* y, int T, int d, int k, hipStream_t stream);
+
+// Grouped GEMM tile configurations (one kernel template; see grouped_gemm.hip).
+enum GemmKind { kGemmLarge = 0, kGemmStream = 1, kGemmDecode = 2 };
+int gemm_block_m(GemmKind kind);
+
+// Gate/up product with the SiLU(a) * b epilogue:  h[r, n] = SiLU(A_e W_g[e]^T) * (A_e W_u[e]^T).
+// offsets == NULL means one group of `dense_rows` rows.  tstart = per-group tile starts.
+hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const void* Wg, const void* Wu,
+                              const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
+                              int max_tiles_m, int N, int K, void* H, hipStream_t stream);
+
+// Down projection:  o[r, n] = H_e W_d[e]^T, fp32 out.
+hipError_t launch_gemm_down(GemmKind kind, int dtype, const void* H, const void* Wd, const int32_t* offsets,
+                            const int32_t* tstart, int G, int dense_rows, int max_tiles_m, int N, int K,
+                            float* O, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,258 @@
+// C ABI of the MoE layer (declared in include/moe.h): argument checks, workspace layout,
+// and the launch sequence of the gfx950 kernels.  No device allocation, no host sync.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t p_part, hist, chunk_base, counts, kept, offsets, row_token, row_of, tstart1, tstart2;
+  size_t x_perm, h, o, sh_h, sh_o, total;
+};
+
+size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+Layout layout(const moe_shape& s) {
+  Layout L{};
+  const size_t es = elem_size(s.dtype);
+  const size_t nb = (size_t)route_blocks(s.T);
+  const size_t E = (size_t)s.E, R = (size_t)s.T * (size_t)s.k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  L.p_part = take(nb * E * sizeof(float));
+  L.hist = take(nb * E * sizeof(int32_t));
+  L.chunk_base = take(nb * E * sizeof(int32_t));
+  L.counts = take(E * sizeof(int32_t));
+  L.kept = take(E * sizeof(int32_t));
+  L.offsets = take((E + 1) * sizeof(int32_t));
+  L.row_token = take(R * sizeof(int32_t));
+  L.row_of = take(R * sizeof(int32_t));
+  L.tstart1 = take((E + 1) * sizeof(int32_t));
+  L.tstart2 = take((E + 1) * sizeof(int32_t));
+  L.x_perm = take(R * (size_t)s.d * es);
+  L.h = take(R * (size_t)s.d_e * es);
+  L.o = take(R * (size_t)s.d * sizeof(float));
+  L.sh_h = take((size_t)s.T * (size_t)s.d_e_shared * es);
+  L.sh_o = take(s.d_e_shared > 0 ? (size_t)s.T * (size_t)s.d * sizeof(float) : 0);
+  L.total = off;
+  return L;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_NULL;
+  if (s->T < 0 || s->d < 1 || s->d_e < 1 || s->E < 1 || s->k < 1 || s->k > s->E || s->d_e_shared < 0)
+    return MOE_ERR_SHAPE;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->E > 1024 || s->k > 16) return MOE_ERR_UNSUPPORTED;
+  if (s->d % 128 || s->d_e % 128 || s->d_e_shared % 128) return MOE_ERR_UNSUPPORTED;
+  if ((long long)s->T * s->k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  // the gather addresses x_perm in 16-byte units with int32: T*k*d*elem_size / 16 < 2^31
+  if ((long long)s->T * s->k * (long long)s->d * (s->dtype == MOE_BF16 ? 2 : 4) >= (1LL << 35))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Tile configuration from the expected rows per expert (host-known bounds only).
+GemmKind choose_kind(long long rows_total, int groups, int cap) {
+  const double mean = (double)rows_total / (double)groups;
+  double mx = mean + 4.0 * sqrt(mean) + 2.0;
+  if (cap >= 0) mx = std::min(mx, (double)cap);
+  if (mx <= 16.0) return kGemmDecode;
+  if (mean >= 384.0) return kGemmLarge;
+  return kGemmStream;
+}
+
+// Upper bound on the number of m-tiles over all groups.
+int max_m_tiles(long long rows_bound, int groups, int cap, int bm) {
+  long long a = (rows_bound + bm - 1) / bm + groups;
+  if (cap >= 0) {
+    long long per = (std::min<long long>(cap, rows_bound) + bm - 1) / bm;
+    a = std::min(a, per * groups);
+  }
+  return (int)std::min<long long>(a, 1LL << 30);
+}
+
+#define MOE_HIP(call)                               \
+  do {                                              \
+    if ((call) != hipSuccess) return MOE_ERR_HIP;   \
+  } while (0)
+
+template <typename P>
+P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
+
+moe_status run_router(const moe_shape& s, const void* x, const void* w_r, const float* b_r, int32_t* idx,
+                      float* gate, int32_t* counts, float* f, float* P, float* aux, int32_t* kept,
+                      int32_t* offsets, int bm1, int bm2, void* ws, hipStream_t st) {
+  const Layout L = layout(s);
+  const int nb = route_blocks(s.T);
+  if (s.T > 0)
+    MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, idx, gate,
+                          at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
+  MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts,
+                      kept, offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm1, at<int32_t>(ws, L.tstart1),
+                      bm2, at<int32_t>(ws, L.tstart2), st));
+  return MOE_OK;
+}
+
+moe_status run_ffn(const moe_shape& s, int G, const void* A, const int32_t* offsets, const int32_t* tstart1,
+                   const int32_t* tstart2, GemmKind kind, int tiles1, int tiles2, int dense_rows, int d_e,
+                   const void* wg, const void* wu, const void* wd, void* h, float* o, hipStream_t st) {
+  MOE_HIP(launch_gemm_gateup(kind, s.dtype, A, wg, wu, offsets, tstart1, G, dense_rows, tiles1, d_e, s.d, h, st));
+  MOE_HIP(launch_gemm_down(kind, s.dtype, h, wd, offsets, tstart2, G, dense_rows, tiles2, s.d, d_e, o, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: inconsistent or negative size";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype outside the supported set";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP call failed";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_capacity(int32_t T, int32_t k, int32_t E, double C, int32_t* cap) {
+  if (!cap) return MOE_ERR_NULL;
+  if (T < 0 || k < 1 || E < 1 || !(C >= 0.0) || !isfinite(C)) return MOE_ERR_SHAPE;
+  const double v = floor(C * (double)T * (double)k / (double)E);
+  if (v >= 2147483648.0) return MOE_ERR_SHAPE;
+  *cap = (int32_t)v;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  *bytes = layout(*shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const void* w_r, const float* b_r, int32_t* idx,
+                     float* gate, int32_t* counts, float* f, float* P, float* aux, void* ws, size_t ws_bytes,
+                     void* stream) {
+  moe_status v = check_shape(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if ((s.T > 0 && (!x || !w_r || !idx || !gate)) || !counts || !f || !P || !aux || !ws) return MOE_ERR_NULL;
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return run_router(s, x, w_r, b_r, idx, gate, counts, f, P, aux, at<int32_t>(ws, L.kept),
+                    at<int32_t>(ws, L.offsets), 1, 1, ws, (hipStream_t)stream);
+}
+
+moe_status moe_permute(const moe_shape* shape, const void* x, const int32_t* idx, int32_t* kept, int32_t* offsets,
+                       int32_t* row_token, int32_t* row_of, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  moe_status v = check_shape(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if ((s.T > 0 && (!x || !idx || !row_token || !row_of || !x_perm)) || !kept || !offsets || !ws) return MOE_ERR_NULL;
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int nb = route_blocks(s.T);
+  if (s.T > 0) MOE_HIP(launch_hist(idx, s.T, s.k, s.E, at<int32_t>(ws, L.hist), st));
+  MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), nullptr, nb, s.T, s.k, s.E, s.capacity, nullptr, kept, offsets,
+                      at<int32_t>(ws, L.chunk_base), nullptr, nullptr, nullptr, 1, at<int32_t>(ws, L.tstart1), 1,
+                      at<int32_t>(ws, L.tstart2), st));
+  if (s.T > 0)
+    MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
+                               offsets, row_token, row_of, x_perm, st));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                          const void* w_up, const void* w_down, float* o, void* ws, size_t ws_bytes, void* stream) {
+  moe_status v = check_shape(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (!x_perm || !offsets || !w_gate || !w_up || !w_down || !o || !ws) return MOE_ERR_NULL;
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const long long R = (long long)s.T * s.k;
+  if (R == 0) return MOE_OK;
+  const GemmKind kind = choose_kind(R, s.E, s.capacity);
+  const int bm = gemm_block_m(kind);
+  int32_t* ts1 = at<int32_t>(ws, L.tstart1);
+  int32_t* ts2 = at<int32_t>(ws, L.tstart2);
+  MOE_HIP(launch_tile_sched(offsets, s.E, bm, ts1, bm, ts2, st));
+  const int tiles = max_m_tiles(R, s.E, -1, bm);
+  return run_ffn(s, s.E, x_perm, offsets, ts1, ts2, kind, tiles, tiles, 0, s.d_e, w_gate, w_up, w_down,
+                 at<void>(ws, L.h), o, st);
+}
+
+moe_status moe_combine(const moe_shape* shape, const float* o, const int32_t* row_of, const float* gate,
+                       const float* shared_out, float* y, void* stream) {
+  moe_status v = check_shape(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!o || !row_of || !gate || !y) return MOE_ERR_NULL;
+  MOE_HIP(launch_combine(o, row_of, gate, shared_out, y, s.T, s.d, s.k, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, const float* b_r, const void* w_gate,
+                       const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                       const void* ws_down, float* y, int32_t* idx, float* gate, int32_t* counts, int32_t* kept,
+                       float* f, float* P, float* aux, int32_t* offsets, int32_t* row_token, int32_t* row_of,
+                       void* ws, size_t ws_bytes, void* stream) {
+  moe_status v = check_shape(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if ((s.T > 0 && (!x || !w_r || !w_gate || !w_up || !w_down || !y || !idx || !gate)) || !counts || !kept || !f ||
+      !P || !aux || !ws)
+    return MOE_ERR_NULL;
+  if (s.d_e_shared > 0 && s.T > 0 && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_NULL;
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (!offsets) offsets = at<int32_t>(ws, L.offsets);
+  if (!row_token) row_token = at<int32_t>(ws, L.row_token);
+  if (!row_of) row_of = at<int32_t>(ws, L.row_of);
+
+  const long long R = (long long)s.T * s.k;
+  const GemmKind kind = choose_kind(std::max<long long>(R, 1), s.E, s.capacity);
+  const int bm = gemm_block_m(kind);
+  moe_status r = run_router(s, x, w_r, b_r, idx, gate, counts, f, P, aux, kept, offsets, bm, bm, ws, st);
+  if (r != MOE_OK || s.T == 0) return r;
+  MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
+                             offsets, row_token, row_of, at<void>(ws, L.x_perm), st));
+  const int tiles = max_m_tiles(R, s.E, s.capacity, bm);
+  r = run_ffn(s, s.E, at<void>(ws, L.x_perm), offsets, at<int32_t>(ws, L.tstart1), at<int32_t>(ws, L.tstart2), kind,
+              tiles, tiles, 0, s.d_e, w_gate, w_up, w_down, at<void>(ws, L.h), at<float>(ws, L.o), st);
+  if (r != MOE_OK) return r;
+  const float* shared_out = nullptr;
+  if (s.d_e_shared > 0) {
+    const GemmKind sk = choose_kind(s.T, 1, -1);
+    const int sbm = gemm_block_m(sk);
+    const int stiles = (s.T + sbm - 1) / sbm;
+    r = run_ffn(s, 1, x, nullptr, nullptr, nullptr, sk, stiles, stiles, s.T, s.d_e_shared, ws_gate, ws_up, ws_down,
+                at<void>(ws, L.sh_h), at<float>(ws, L.sh_o), st);
+    if (r != MOE_OK) return r;
+    shared_out = at<float>(ws, L.sh_o);
+  }
+  MOE_HIP(launch_combine(at<float>(ws, L.o), row_of, gate, shared_out, y, s.T, s.d, s.k, st));
+  return MOE_OK;
+}
+
+}  // extern "C"

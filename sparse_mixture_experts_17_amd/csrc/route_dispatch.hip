@@ -1,0 +1,415 @@
+// Router, dispatch (counting sort + capacity + gather) and combine kernels for gfx950.
+//
+// Router: the linear router, softmax and top-k of the layer (Zero to Frontier §13.1
+// "Why MoE", section "The MoE layer"; the routing paragraph of the kevinluzbetak.com
+// "Mixture-Of-Experts" page), with logits, softmax and selection in fp32 (the Switch
+// router precision remark of AI Engineering Illustrated, "The router is small but it
+// decides everything").
+//
+// Dispatch: the per-expert token lists of the layer as one expert-contiguous list, built
+// by a stable counting sort (histogram per chunk of tokens, scan, rank in arrival order),
+// with the capacity limit of AI Engineering Illustrated, "The safety valve is a capacity
+// limit": an expert keeps its first `cap` assignments in arrival order t*k + j.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------ router
+//
+// One block = 16 tokens x all E experts, 4 waves.
+// Phase 1: logits[16][E] via 16x16 MFMA tiles (A = 16 token rows, B = 16 router rows),
+//          operands read straight from global memory (16 B per lane), bias added, to LDS.
+// Phase 2: each wave takes 4 tokens: softmax over E (lane l holds experts l + 64 q),
+//          k rounds of wave arg-max (ties -> lower index), gates, LDS histogram.
+// Phase 3: per-block partial sums of p (fixed order over waves) and histogram to global.
+template <typename T>
+__global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
+                                                     const float* __restrict__ b_r, int T_, int d, int E,
+                                                     int k, int renorm, int32_t* __restrict__ idx,
+                                                     float* __restrict__ gate, float* __restrict__ p_part,
+                                                     int32_t* __restrict__ hist) {
+  constexpr int TB = kRouteTokens;
+  extern __shared__ float smem[];
+  float* logits = smem;                // [TB][E]
+  float* psum = smem + TB * E;         // [4][E]
+  int* lhist = (int*)(psum + 4 * E);   // [E]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * TB;
+  for (int i = tid; i < E; i += 256) lhist[i] = 0;
+
+  // ---- phase 1: logits
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int tok = min(t0 + r16, T_ - 1);            // rows past T repeat row T-1; never used
+  const size_t row_bytes = (size_t)d * sizeof(T);
+  const char* xrow = (const char*)x + (size_t)tok * row_bytes + grp * 16;
+  const int nchunks = (int)(row_bytes / 64);
+  const int n_et = (E + 15) / 16;
+  for (int tb = wave * 4; tb < n_et; tb += 16) {     // up to 4 expert tiles per wave per pass
+    const int ntl = min(4, n_et - tb);
+    const char* wrow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int e = min((tb + j) * 16 + r16, E - 1);
+      wrow[j] = (const char*)w_r + (size_t)e * row_bytes + grp * 16;
+    }
+    f32x4_t acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (ntl == 4) {
+#pragma unroll 4
+      for (int c = 0; c < nchunks; ++c) {
+        u32x4_t a = *(const u32x4_t*)(xrow + (size_t)c * 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x4_t b = *(const u32x4_t*)(wrow[j] + (size_t)c * 64);
+          Mfma<T>::step(acc[j], a, b);
+        }
+      }
+    } else {
+#pragma unroll 2
+      for (int c = 0; c < nchunks; ++c) {
+        u32x4_t a = *(const u32x4_t*)(xrow + (size_t)c * 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < ntl) {
+            u32x4_t b = *(const u32x4_t*)(wrow[j] + (size_t)c * 64);
+            Mfma<T>::step(acc[j], a, b);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int e = (tb + j) * 16 + r16;
+      if (j < ntl && e < E) {
+        float bias = b_r ? b_r[e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) logits[(grp * 4 + i) * E + e] = acc[j][i] + bias;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: softmax and top-k, one token per wave at a time
+  const int nq = (E + 63) / 64;   // <= 16
+  float pacc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) pacc[q] = 0.f;
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tl = wave * 4 + tt;
+    const int t = t0 + tl;
+    if (t >= T_) break;
+    float v[16];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      int e = q * 64 + lane;
+      v[q] = (q < nq && e < E) ? logits[tl * E + e] : -INFINITY;
+      m = fmaxf(m, v[q]);
+    }
+    m = wave_max(m);
+    float ex[16];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      ex[q] = (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
+      s += ex[q];
+    }
+    s = wave_sum(s);
+    const float inv = 1.f / s;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) pacc[q] += ex[q] * inv;
+
+    uint32_t taken = 0;
+    int my_e = 0;
+    float my_ex = 0.f, selsum = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {     // ascending expert index within the lane: '>' keeps the lowest
+        int e = q * 64 + lane;
+        if (q < nq && e < E && !((taken >> q) & 1u) && v[q] > bv) { bv = v[q]; be = e; }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o, kWave);
+        int oe = __shfl_xor(be, o, kWave);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      }
+      if ((be & 63) == lane) taken |= 1u << (be >> 6);
+      float exj = expf(bv - m);
+      selsum += exj;
+      if (lane == j) { my_e = be; my_ex = exj; }
+    }
+    if (lane < k) {
+      idx[(size_t)t * k + lane] = my_e;
+      gate[(size_t)t * k + lane] = renorm ? my_ex / selsum : my_ex * inv;
+      atomicAdd(&lhist[my_e], 1);
+    }
+  }
+
+  // ---- phase 3: block partials
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    int e = q * 64 + lane;
+    if (q < nq && e < E) psum[wave * E + e] = pacc[q];
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    p_part[(size_t)blockIdx.x * E + e] = ((psum[e] + psum[E + e]) + psum[2 * E + e]) + psum[3 * E + e];
+    hist[(size_t)blockIdx.x * E + e] = lhist[e];
+  }
+}
+
+hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E,
+                         int k, int renorm, int32_t* idx, float* gate, float* p_part, int32_t* hist,
+                         hipStream_t stream) {
+  const int nb = route_blocks(T);
+  const size_t lds = (size_t)(kRouteTokens * E + 4 * E) * sizeof(float) + (size_t)E * sizeof(int);
+  if (dtype == 1) {
+    auto kern = router_kernel<uint16_t>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const uint16_t*)x, (const uint16_t*)w_r, b_r,
+                       T, d, E, k, renorm, idx, gate, p_part, hist);
+  } else {
+    auto kern = router_kernel<float>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const float*)x, (const float*)w_r, b_r, T, d,
+                       E, k, renorm, idx, gate, p_part, hist);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ histogram
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                   int32_t* __restrict__ hist) {
+  extern __shared__ int lh[];
+  for (int i = threadIdx.x; i < E; i += 256) lh[i] = 0;
+  __syncthreads();
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int n = min(kRouteTokens, T - t0) * k;
+  for (int i = threadIdx.x; i < n; i += 256) atomicAdd(&lh[idx[(size_t)t0 * k + i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = lh[e];
+}
+
+hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t stream) {
+  hipLaunchKernelGGL(hist_kernel, dim3(route_blocks(T)), dim3(256), (size_t)E * sizeof(int), stream, idx, T,
+                     k, E, hist);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ scan (1 block)
+//
+// Thread e walks the chunks in order: chunk_base[b][e] = assignments to e in chunks < b;
+// counts[e] = all of them.  kept = min(counts, cap); offsets and tile starts are
+// exclusive scans over experts.  f, P, aux use fixed-order sums.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist,
+                                                    const float* __restrict__ p_part, int nb, int T, int k,
+                                                    int E, int cap, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ chunk_base, float* __restrict__ f,
+                                                    float* __restrict__ P, float* __restrict__ aux, int bm1,
+                                                    int32_t* __restrict__ tstart1, int bm2,
+                                                    int32_t* __restrict__ tstart2) {
+  __shared__ int s_scan[1024];
+  __shared__ float s_red[1024];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  float ps = 0.f;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      chunk_base[(size_t)b * E + e] = cnt;
+      cnt += hist[(size_t)b * E + e];
+    }
+    if (p_part)
+      for (int b = 0; b < nb; ++b) ps += p_part[(size_t)b * E + e];
+  }
+  const int kp = e < E ? (cap < 0 ? cnt : min(cnt, cap)) : 0;
+  int tot;
+  const int off = block1024_exclusive_scan(kp, s_scan, &tot);
+  const int nt1 = (kp + bm1 - 1) / bm1, nt2 = (kp + bm2 - 1) / bm2;
+  int tot1, tot2;
+  const int ts1 = block1024_exclusive_scan(nt1, s_scan, &tot1);
+  const int ts2 = block1024_exclusive_scan(nt2, s_scan, &tot2);
+  if (e < E) {
+    if (counts) counts[e] = cnt;
+    kept[e] = kp;
+    offsets[e] = off;
+    tstart1[e] = ts1;
+    tstart2[e] = ts2;
+  }
+  if (e == 0) {
+    offsets[E] = tot;
+    tstart1[E] = tot1;
+    tstart2[E] = tot2;
+  }
+  if (p_part) {
+    const long long R = (long long)T * k;
+    float fe = (e < E && R > 0) ? (float)((double)cnt / (double)R) : 0.f;
+    float Pe = (e < E && T > 0) ? ps / (float)T : 0.f;
+    if (e < E) {
+      f[e] = fe;
+      P[e] = Pe;
+    }
+    s_red[e] = fe * Pe;
+    __syncthreads();
+    for (int h = 512; h > 0; h >>= 1) {
+      if (e < h) s_red[e] += s_red[e + h];
+      __syncthreads();
+    }
+    if (e == 0) aux[0] = (float)E * s_red[0];
+  }
+}
+
+hipError_t launch_scan(const int32_t* hist, const float* p_part, int nb, int T, int k, int E, int cap,
+                       int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* chunk_base, float* f,
+                       float* P, float* aux, int bm1, int32_t* tstart1, int bm2, int32_t* tstart2,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, hist, p_part, nb, T, k, E, cap, counts, kept,
+                     offsets, chunk_base, f, P, aux, bm1, tstart1, bm2, tstart2);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(1024) void tile_sched_kernel(const int32_t* __restrict__ offsets, int E, int bm1,
+                                                          int32_t* __restrict__ tstart1, int bm2,
+                                                          int32_t* __restrict__ tstart2) {
+  __shared__ int s_scan[1024];
+  const int e = threadIdx.x;
+  const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int tot1, tot2;
+  const int ts1 = block1024_exclusive_scan((rows + bm1 - 1) / bm1, s_scan, &tot1);
+  const int ts2 = block1024_exclusive_scan((rows + bm2 - 1) / bm2, s_scan, &tot2);
+  if (e < E) {
+    tstart1[e] = ts1;
+    tstart2[e] = ts2;
+  }
+  if (e == 0) {
+    tstart1[E] = tot1;
+    tstart2[E] = tot2;
+  }
+}
+
+hipError_t launch_tile_sched(const int32_t* offsets, int E, int bm1, int32_t* tstart1, int bm2, int32_t* tstart2,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(tile_sched_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, bm1, tstart1, bm2, tstart2);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ rank + gather
+//
+// One block per chunk of 16 tokens (<= 256 assignments).  The rank of assignment i
+// within its expert is the chunk's base for that expert plus the number of earlier
+// assignments in the chunk with the same expert (stable, arrival order).  Kept
+// assignments then copy their token row into x_perm with 16-byte loads and stores.
+template <typename T>
+__global__ __launch_bounds__(256) void rank_gather_kernel(const T* __restrict__ x, const int32_t* __restrict__ idx,
+                                                          int T_, int d, int k, int E, int cap,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ row_token,
+                                                          int32_t* __restrict__ row_of, T* __restrict__ x_perm) {
+  __shared__ int s_e[256];
+  __shared__ int s_row[256];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int n = min(kRouteTokens, T_ - t0) * k;
+  if (tid < n) s_e[tid] = idx[(size_t)t0 * k + tid];
+  __syncthreads();
+  if (tid < n) {
+    const int e = s_e[tid];
+    int r = 0;
+    for (int j = 0; j < tid; ++j) r += (s_e[j] == e);
+    const int g = chunk_base[(size_t)blockIdx.x * E + e] + r;
+    const int row = (cap < 0 || g < cap) ? offsets[e] + g : -1;
+    row_of[(size_t)t0 * k + tid] = row;
+    s_row[tid] = row;
+    if (row >= 0) row_token[row] = t0 + tid / k;
+  }
+  __syncthreads();
+  const int P = (int)((size_t)d * sizeof(T) / 16);   // 16-byte pieces per row
+  const int total = n * P;
+  constexpr int U = 4;
+  for (int base = tid; base < total; base += 256 * U) {
+    u32x4_t v[U];
+    int dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = base + u * 256;
+      dst[u] = -1;
+      if (it < total) {
+        const int item = it / P, piece = it - item * P;
+        const int row = s_row[item];
+        if (row >= 0) {
+          const int t = t0 + item / k;
+          v[u] = *((const u32x4_t*)((const char*)x + (size_t)t * d * sizeof(T)) + piece);
+          dst[u] = row * P + piece;   // in 16-byte units
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (dst[u] >= 0) ((u32x4_t*)x_perm)[(size_t)dst[u]] = v[u];
+  }
+}
+
+hipError_t launch_rank_gather(int dtype, const void* x, const int32_t* idx, int T, int d, int k, int E, int cap,
+                              const int32_t* chunk_base, const int32_t* offsets, int32_t* row_token,
+                              int32_t* row_of, void* x_perm, hipStream_t stream) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(rank_gather_kernel<uint16_t>, dim3(route_blocks(T)), dim3(256), 0, stream,
+                       (const uint16_t*)x, idx, T, d, k, E, cap, chunk_base, offsets, row_token, row_of,
+                       (uint16_t*)x_perm);
+  else
+    hipLaunchKernelGGL(rank_gather_kernel<float>, dim3(route_blocks(T)), dim3(256), 0, stream, (const float*)x,
+                       idx, T, d, k, E, cap, chunk_base, offsets, row_token, row_of, (float*)x_perm);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ combine
+//
+// The layer's gate-weighted sum back in token order (Zero to Frontier §13.1, "The MoE
+// layer" equation), accumulated as: shared (or 0), then slot 0, 1, ..., k-1 with one
+// fused multiply-add each.  A dropped slot (row -1) adds nothing.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ gate,
+                                                      const float* __restrict__ shared, float* __restrict__ y,
+                                                      int T, int d, int k) {
+  __shared__ int s_row[16];
+  __shared__ float s_g[16];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_row[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
+    s_g[threadIdx.x] = gate[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int d4 = d / 4;
+  for (int c = threadIdx.x; c < d4; c += 256) {
+    f32x4_t acc = shared ? ((const f32x4_t*)shared)[(size_t)t * d4 + c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int row = s_row[j];
+      if (row >= 0) {
+        const f32x4_t v = ((const f32x4_t*)o)[(size_t)row * d4 + c];
+        const float g = s_g[j];
+        acc[0] = fmaf(g, v[0], acc[0]);
+        acc[1] = fmaf(g, v[1], acc[1]);
+        acc[2] = fmaf(g, v[2], acc[2]);
+        acc[3] = fmaf(g, v[3], acc[3]);
+      }
+    }
+    ((f32x4_t*)y)[(size_t)t * d4 + c] = acc;
+  }
+}
+
+hipError_t launch_combine(const float* o, const int32_t* row_of, const float* gate, const float* shared, float* y,
+                          int T, int d, int k, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, o, row_of, gate, shared, y, T, d, k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,133 @@
+"""Shared checks of the HIP path against the CPU oracle (used by the GPU tests).
+
+Protocol
+  1. Routing: idx from the GPU equals the oracle's top-k for every token outside the
+     near-tie set N (k-th and (k+1)-th oracle probabilities within 1e-6); tokens in N
+     are reported and must still hold a valid choice.
+  2. Gates within 1e-5 absolute of the oracle's gates for the GPU's idx; counts exact;
+     f equal to float32(counts / (T k)); P and aux within 1e-5 relative.
+  3. Dispatch (kept, offsets, row_token, row_of, dropped set) bit-exact against the
+     oracle's dispatch of the GPU's idx; x_perm rows bit-identical to x rows.
+  4. Output: max|y - y_oracle| / rms(y_oracle) <= 1e-4 (fp32) or 2e-2 (bf16), the
+     oracle run with the GPU's routing; at full size on sampled tokens.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import sys
+import time
+
+import numpy as np
+import torch
+
+import sparse_mixture_experts_17_amd as moe
+import workloads as wl
+from oracle import moe_oracle as mo
+from workloads.device import upload
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def shape_of(w: wl.Workload, T=None):
+    cap = -1 if w.capacity_factor is None else moe.moe_capacity(w.T, w.k, w.E, w.capacity_factor)
+    return moe.make_shape(w.T if T is None else T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
+                          d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32), cap
+
+
+def oracle_cap(w: wl.Workload) -> int:
+    return -1 if w.capacity_factor is None else mo.capacity(w.T, w.k, w.E, w.capacity_factor)
+
+
+def f64(a, w):
+    return wl.as_f64(a, w.dtype)
+
+
+def experts_f64(inp, es, threads=16):
+    """{e: float64 weights} for the experts in es, drawn in parallel on the host."""
+    def one(e):
+        return e, tuple(f64(m, inp.wl) for m in inp.expert(e))
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        return dict(ex.map(one, sorted(set(int(e) for e in es))))
+
+
+def check_routing(w, inp, idx, gate, counts, f, P, aux):
+    """Steps 1-2; returns (p, near-tie tokens, flipped tokens)."""
+    x = f64(inp.x, w)
+    r, p, own_idx, _ = mo.route(x, f64(inp.w_r, w), w.k, inp.b_r, w.renormalize)
+    nt = mo.near_ties(p, w.k)
+    mask = np.ones(w.T, bool)
+    mask[nt] = False
+    assert np.array_equal(idx[mask], own_idx[mask]), \
+        f"routing differs on {np.nonzero((idx != own_idx).any(1) & mask)[0][:10]}"
+    flipped = [int(t) for t in nt if not np.array_equal(idx[t], own_idx[t])]
+    for t in flipped:          # a near tie may go either way, but the choice must be a valid top-k
+        kth = np.sort(p[t])[::-1][w.k - 1]
+        assert len(set(idx[t])) == w.k and np.all(p[t, idx[t]] >= kth - 1e-6)
+    g_ref = mo.gates(p, idx, w.renormalize)
+    assert np.max(np.abs(gate - g_ref)) <= 1e-5, np.max(np.abs(gate - g_ref))
+    c_ref, f_ref, P_ref, aux_ref = mo.load_balance_stats(p, idx, w.E)
+    assert np.array_equal(counts, c_ref)
+    assert np.array_equal(f, f_ref.astype(np.float32))
+    assert np.max(np.abs(P - P_ref) / np.maximum(P_ref, 1e-30)) <= 1e-5, np.max(np.abs(P - P_ref) / P_ref)
+    assert abs(aux - aux_ref) <= 1e-5 * abs(aux_ref)
+    return p, nt, flipped
+
+
+def check_dispatch(w, idx, cap, kept, offsets, row_token, row_of):
+    d = mo.dispatch(idx, w.E, cap)
+    assert np.array_equal(kept, d.kept)
+    assert np.array_equal(offsets, d.offsets)
+    R = int(d.offsets[-1])
+    assert np.array_equal(row_token[:R], d.row_token)
+    assert np.array_equal(row_of, d.row_of)
+    return d
+
+
+def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
+    """Forward on the GPU + every protocol check.  sample=None: all tokens' y checked."""
+    t0 = time.time()
+    inp = wl.make_inputs(w, seed)
+    dev = upload(inp)
+    shape, cap = shape_of(w)
+    assert cap == oracle_cap(w)
+    out = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+    torch.cuda.synchronize()
+    h = {k: getattr(out, k).cpu().numpy() for k in
+         ["y", "idx", "gate", "counts", "kept", "f", "P", "aux", "offsets", "row_token", "row_of"]}
+    if repeat_check:
+        out2 = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+        torch.cuda.synchronize()
+        for k in h:
+            assert np.array_equal(getattr(out2, k).cpu().numpy().view(np.uint8), h[k].view(np.uint8)), \
+                f"second run differs in {k}"
+    del dev, out
+    torch.cuda.empty_cache()
+    p, nt, flipped = check_routing(w, inp, h["idx"], h["gate"], h["counts"], h["f"], h["P"], h["aux"][0])
+    disp = check_dispatch(w, h["idx"], cap, h["kept"], h["offsets"], h["row_token"], h["row_of"])
+    x = f64(inp.x, w)
+    sh = inp.shared()
+    sh = None if sh is None else tuple(f64(m, w) for m in sh)
+    if sample is None:
+        ex = experts_f64(inp, range(w.E))
+        ref = mo.moe_forward(x, f64(inp.w_r, w), [ex[e] for e in range(w.E)], w.k, cap, inp.b_r, w.renormalize,
+                             sh, idx=h["idx"])
+        y_ref, y = ref.y, h["y"]
+    else:
+        toks = np.asarray(sample)
+        kept_mask = disp.row_of[toks] >= 0
+        need = h["idx"][toks][kept_mask]
+        ex = experts_f64(inp, need)
+        g_ref = mo.gates(p[toks], h["idx"][toks], w.renormalize)
+        y_ref = mo.outputs_for_tokens(x[toks], h["idx"][toks], g_ref, kept_mask, lambda e: ex[e], sh)
+        y = h["y"][toks]
+    err = mo.rel_err(y, y_ref)
+    dropped = int(disp.dropped.size)
+    log(f"[{w.name}] T={w.T} d={w.d} d_e={w.d_e} E={w.E} k={w.k} cap={cap}: max|dy|/rms={err:.3e} "
+        f"near_ties={len(nt)} flipped={len(flipped)} dropped={dropped} ({time.time() - t0:.1f}s)")
+    assert err <= TOL[w.dtype], err
+    return dict(err=err, near_ties=len(nt), flipped=len(flipped), dropped=dropped, host=h)

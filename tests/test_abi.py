@@ -1,0 +1,132 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every symbol the
+header declares, and its host-side checks reject bad arguments before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_17_amd as moe
+from sparse_mixture_experts_17_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert names == sorted(["moe_capacity", "moe_workspace_bytes", "moe_status_str", "moe_route", "moe_permute",
+                            "moe_expert_ffn", "moe_combine", "moe_forward"])
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_capacity_helper():
+    assert moe.moe_capacity(4096, 2, 4, 1.25) == 2560      # kevinluzbetak.com capacity worked example
+    assert moe.moe_capacity(8192, 1, 64, 1.25) == 160      # Switch-style workload
+    assert moe.moe_capacity(10, 1, 4, 1.0) == 2            # rounds down
+    assert moe.moe_capacity(0, 1, 4, 1.0) == 0
+    lib = _lib.lib()
+    out = C.c_int32()
+    assert lib.moe_capacity(10, 1, 4, 1.0, None) == 1
+    for args in [(-1, 1, 4, 1.0), (10, 0, 4, 1.0), (10, 1, 0, 1.0), (10, 1, 4, -0.5), (10, 1, 4, float("nan")),
+                 (10, 1, 4, float("inf")), (2 ** 30, 16, 1, 1.0)]:
+        assert lib.moe_capacity(*args, C.byref(out)) == 2, args
+
+
+def _shape(**kw):
+    base = dict(T=64, d=512, d_e=1024, E=8, k=2, capacity=-1, renormalize=True, d_e_shared=0, dtype=moe.MOE_F32)
+    base.update(kw)
+    return moe.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9), 2), (dict(k=0), 2), (dict(T=-1), 2), (dict(E=0), 2), (dict(d_e_shared=-128), 2),
+    (dict(E=1025, k=2), 3), (dict(k=17, E=32), 3), (dict(d=500), 3), (dict(d_e=1000), 3),
+    (dict(d_e_shared=100), 3), (dict(dtype=7), 3),
+])
+def test_shape_validation(kw, status):
+    n = C.c_size_t()
+    assert _lib.lib().moe_workspace_bytes(C.byref(_shape(**kw)), C.byref(n)) == status
+
+
+def test_workspace_bytes_grows_with_shape():
+    a = moe.moe_workspace_bytes(_shape())
+    b = moe.moe_workspace_bytes(_shape(T=128))
+    c = moe.moe_workspace_bytes(_shape(d_e_shared=256))
+    assert 0 < a < b and a < c
+    assert moe.moe_workspace_bytes(_shape(T=0)) > 0
+    assert _lib.lib().moe_workspace_bytes(None, C.byref(C.c_size_t())) == 1
+    assert _lib.lib().moe_workspace_bytes(C.byref(_shape()), None) == 1
+
+
+def test_status_strings():
+    for s in range(6):
+        assert moe.moe_status_str(s).startswith(_lib.STATUS[s])
+
+
+# Error paths of the device calls.  The fake addresses below are never dereferenced:
+# each call fails its host-side check first and returns before any HIP call.
+FAKE = C.c_void_p(0x1000)
+
+
+def _args(n):
+    return [FAKE] * n
+
+
+def test_device_calls_reject_null_and_small_workspace():
+    lib = _lib.lib()
+    s = _shape()
+    ws_need = moe.moe_workspace_bytes(s)
+    # moe_route: x, w_r, b_r, idx, gate, counts, f, P, aux, ws
+    a = _args(10)
+    a[2] = None                                         # b_r may be NULL
+    assert lib.moe_route(C.byref(s), *a[:9], a[9], 1, None) == 4
+    for i in (0, 1, 3, 4, 5, 6, 7, 8, 9):
+        b = list(a)
+        b[i] = None
+        assert lib.moe_route(C.byref(s), *b[:9], b[9], ws_need, None) == 1, i
+    # moe_permute: x, idx, kept, offsets, row_token, row_of, x_perm, ws
+    a = _args(8)
+    assert lib.moe_permute(C.byref(s), *a[:7], a[7], ws_need - 1, None) == 4
+    for i in range(8):
+        b = list(a)
+        b[i] = None
+        assert lib.moe_permute(C.byref(s), *b[:7], b[7], ws_need, None) == 1, i
+    # moe_expert_ffn: x_perm, offsets, wg, wu, wd, o, ws
+    a = _args(7)
+    assert lib.moe_expert_ffn(C.byref(s), *a[:6], a[6], 0, None) == 4
+    for i in range(7):
+        b = list(a)
+        b[i] = None
+        assert lib.moe_expert_ffn(C.byref(s), *b[:6], b[6], ws_need, None) == 1, i
+    # moe_combine: o, row_of, gate, shared (optional), y
+    for i in (0, 1, 2, 4):
+        b = _args(5)
+        b[i] = None
+        assert lib.moe_combine(C.byref(s), *b, None) == 1, i
+    # moe_forward: 20 pointers + ws
+    a = _args(21)
+    # order: x w_r b_r w_gate w_up w_down ws_gate ws_up ws_down y idx gate counts kept f P aux offsets
+    #        row_token row_of ws; b_r, the shared weights and offsets/row_token/row_of are optional
+    for i in (2, 6, 7, 8, 17, 18, 19):
+        a[i] = None
+    assert lib.moe_forward(C.byref(s), *a[:20], a[20], 10, None) == 4
+    for i in (0, 1, 3, 4, 5, 9, 10, 11, 12, 13, 14, 15, 16, 20):
+        b = list(a)
+        b[i] = None
+        assert lib.moe_forward(C.byref(s), *b[:20], b[20], ws_need, None) == 1, i
+    # shared expert weights are required when d_e_shared > 0
+    s2 = _shape(d_e_shared=256)
+    assert lib.moe_forward(C.byref(s2), *a[:20], a[20], moe.moe_workspace_bytes(s2), None) == 1
+    # shape errors come first
+    bad = _shape(k=9)
+    assert lib.moe_forward(C.byref(bad), *_args(20), FAKE, 1 << 40, None) == 2
+    assert lib.moe_route(None, *_args(9), FAKE, 1 << 40, None) == 1

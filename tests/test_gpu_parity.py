@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases span several tiles and a ragged tail; the full-size workloads are
+checked on every routing and dispatch output and on sampled output rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_mixture_experts_17_amd as moe
+import workloads as wl
+from oracle import moe_oracle as mo
+from workloads.device import upload
+
+import gpu_parity as gp
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+BASE = {w: wl.get(w) for w in wl.WORKLOADS}
+
+# small cases shaped like each workload (seconds for the oracle)
+SMALL = [
+    BASE["tiny_fp32"],
+    wl.scaled(BASE["tiny_fp32"], name="fp32_ragged", T=77, d=256, d_e=384, E=6, k=3),
+    wl.scaled(BASE["switch_capacity"], name="switch_small", T=1000, d=256, d_e=512, E=64, k=1),
+    wl.scaled(BASE["switch_capacity"], name="switch_raw_p", T=333, d=256, d_e=256, E=16, k=1, renormalize=False),
+    wl.scaled(BASE["switch_capacity"], name="capacity_top2", T=500, d=128, d_e=256, E=8, k=2, capacity_factor=1.0),
+    wl.scaled(BASE["mixtral_prefill"], name="mixtral_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill"], name="mixtral_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_decode"], name="mixtral_decode_small", T=16, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["deepseek_v3"], name="deepseek_small", T=300, d=512, d_e=256, E=256, k=8, d_e_shared=256),
+    wl.scaled(BASE["deepseek_v3"], name="deepseek_shared_large", T=1100, d=256, d_e=128, E=32, k=4, d_e_shared=384),
+    wl.scaled(BASE["mixtral_prefill"], name="max_E_k", T=40, d=128, d_e=128, E=1024, k=16),
+    wl.scaled(BASE["mixtral_prefill"], name="dense_E1", T=130, d=256, d_e=256, E=1, k=1),
+    wl.scaled(BASE["mixtral_prefill"], name="k_equals_E", T=50, d=128, d_e=128, E=4, k=4),
+    wl.scaled(BASE["mixtral_prefill"], name="one_token", T=1, d=128, d_e=256, E=8, k=2),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_forward_small(w):
+    gp.run_forward(w, repeat_check=True)
+
+
+FULL = ["tiny_fp32", "switch_capacity", "mixtral_decode", "mixtral_prefill", "deepseek_v3"]
+
+
+@needs_gpu
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size(name):
+    w = BASE[name]
+    rng = np.random.default_rng(1234)
+    if w.T <= 64:
+        sample = None
+    else:
+        n = 24 if name == "deepseek_v3" else 48
+        sample = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, n, replace=False)]))
+    res = gp.run_forward(w, sample=sample)
+    if name == "switch_capacity":
+        assert res["dropped"] > 0            # the skewed bias makes experts overflow
+
+
+def _upload_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+@needs_gpu
+def test_split_calls_compose():
+    """moe_route -> moe_permute -> moe_expert_ffn (+ shared) -> moe_combine equals moe_forward."""
+    w = wl.scaled(BASE["deepseek_v3"], name="split", T=211, d=256, d_e=128, E=16, k=3, d_e_shared=256,
+                  capacity_factor=1.1)
+    inp = wl.make_inputs(w)
+    dev = upload(inp)
+    shape, cap = gp.shape_of(w)
+    ref = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+    T, d, E, k = w.T, w.d, w.E, w.k
+    ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    i32, f32 = torch.int32, torch.float32
+    idx = torch.empty((T, k), dtype=i32, device="cuda")
+    gate = torch.empty((T, k), dtype=f32, device="cuda")
+    counts = torch.empty(E, dtype=i32, device="cuda")
+    f = torch.empty(E, dtype=f32, device="cuda")
+    P = torch.empty(E, dtype=f32, device="cuda")
+    aux = torch.empty(1, dtype=f32, device="cuda")
+    moe.moe_route(shape, dev.x, dev.w_r, dev.b_r, idx, gate, counts, f, P, aux, ws)
+    kept = torch.empty(E, dtype=i32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=i32, device="cuda")
+    row_token = torch.full((T * k,), -7, dtype=i32, device="cuda")
+    row_of = torch.empty((T, k), dtype=i32, device="cuda")
+    x_perm = torch.zeros((T * k, d), dtype=dev.x.dtype, device="cuda")
+    moe.moe_permute(shape, dev.x, idx, kept, offsets, row_token, row_of, x_perm, ws)
+    o = torch.zeros((T * k, d), dtype=f32, device="cuda")
+    moe.moe_expert_ffn(shape, x_perm, offsets, dev.w_gate, dev.w_up, dev.w_down, o, ws)
+    sshape = moe.make_shape(T, d, w.d_e_shared, 1, 1, dtype=shape.dtype)
+    sws = torch.empty(moe.moe_workspace_bytes(sshape), dtype=torch.uint8, device="cuda")
+    s_out = torch.zeros((T, d), dtype=f32, device="cuda")
+    soff = _upload_i32([0, T])
+    moe.moe_expert_ffn(sshape, dev.x, soff, dev.shared[0].unsqueeze(0).contiguous(),
+                       dev.shared[1].unsqueeze(0).contiguous(), dev.shared[2].unsqueeze(0).contiguous(), s_out, sws)
+    y = torch.empty((T, d), dtype=f32, device="cuda")
+    moe.moe_combine(shape, o, row_of, gate, s_out, y)
+    torch.cuda.synchronize()
+    for a, b in [(idx, ref.idx), (gate, ref.gate), (counts, ref.counts), (f, ref.f), (P, ref.P), (aux, ref.aux),
+                 (kept, ref.kept), (offsets, ref.offsets), (row_of, ref.row_of), (y, ref.y)]:
+        assert torch.equal(a, b)
+    R = int(offsets[-1])
+    assert torch.equal(row_token[:R], ref.row_token[:R])
+    assert torch.all(row_token[R:] == -7)           # rows past R untouched
+    # x_perm rows are the token rows, bit for bit
+    rt = row_token[:R].long()
+    assert torch.equal(x_perm[:R].view(torch.int16), dev.x[rt].view(torch.int16))
+
+
+@needs_gpu
+def test_permute_given_indices():
+    """moe_permute on host-made indices: all tokens to one expert (maximum overflow)."""
+    w = wl.scaled(BASE["mixtral_prefill"], name="perm", T=500, d=128, d_e=128, E=8, k=2)
+    inp = wl.make_inputs(w)
+    dev = upload(inp)
+    rng = np.random.default_rng(5)
+    idx = np.stack([np.concatenate([[3], rng.choice([e for e in range(8) if e != 3], 1)]) for _ in range(w.T)])
+    for cap in (-1, 0, 37, 499):
+        shape = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=cap, dtype=moe.MOE_BF16)
+        ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        kept = torch.empty(8, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(9, dtype=torch.int32, device="cuda")
+        row_token = torch.empty(w.T * 2, dtype=torch.int32, device="cuda")
+        row_of = torch.empty((w.T, 2), dtype=torch.int32, device="cuda")
+        x_perm = torch.empty((w.T * 2, w.d), dtype=torch.bfloat16, device="cuda")
+        moe.moe_permute(shape, dev.x, _upload_i32(idx), kept, offsets, row_token, row_of, x_perm, ws)
+        torch.cuda.synchronize()
+        gp.check_dispatch(w, idx, cap, kept.cpu().numpy(), offsets.cpu().numpy(), row_token.cpu().numpy(),
+                          row_of.cpu().numpy())
+
+
+@needs_gpu
+def test_expert_ffn_given_rows():
+    """moe_expert_ffn on host-built expert-ordered rows, ragged groups incl. empty ones."""
+    for w, rows in [(wl.scaled(BASE["tiny_fp32"], name="ffn32", T=200, d=256, d_e=256, E=5, k=1), [0, 57, 1, 0, 142]),
+                    (wl.scaled(BASE["mixtral_prefill"], name="ffnbf", T=1300, d=256, d_e=512, E=3, k=1),
+                     [600, 0, 700])]:
+        inp = wl.make_inputs(w)
+        dev = upload(inp)
+        shape, _ = gp.shape_of(w)
+        offs = np.concatenate([[0], np.cumsum(rows)])
+        o = torch.zeros((w.T, w.d), dtype=torch.float32, device="cuda")
+        ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        moe.moe_expert_ffn(shape, dev.x, _upload_i32(offs), dev.w_gate, dev.w_up, dev.w_down, o, ws)
+        torch.cuda.synchronize()
+        x = gp.f64(inp.x, w)
+        ref = np.zeros((w.T, w.d))
+        for e in range(w.E):
+            if rows[e]:
+                ref[offs[e]:offs[e + 1]] = mo.swiglu_ffn(x[offs[e]:offs[e + 1]], *(gp.f64(m, w) for m in inp.expert(e)))
+        err = mo.rel_err(o.cpu().numpy(), ref)
+        assert err <= gp.TOL[w.dtype], err
+
+
+@needs_gpu
+def test_combine_given_rows():
+    rng = np.random.default_rng(9)
+    T, d, k = 123, 384, 3
+    o = rng.standard_normal((T * k, d)).astype(np.float32)
+    row_of = rng.permutation(T * k).reshape(T, k).astype(np.int32)
+    row_of[rng.random((T, k)) < 0.2] = -1
+    gate = rng.random((T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, d)).astype(np.float32)
+    shape = moe.make_shape(T, d, 128, 8, k, dtype=moe.MOE_F32)
+    for shared in (None, sh):
+        y = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        moe.moe_combine(shape, torch.from_numpy(o).cuda(), _upload_i32(row_of), torch.from_numpy(gate).cuda(),
+                        None if shared is None else torch.from_numpy(shared).cuda(), y)
+        torch.cuda.synchronize()
+        ref = np.zeros((T, d)) if shared is None else shared.astype(np.float64)
+        for j in range(k):
+            m = row_of[:, j] >= 0
+            ref[m] += gate[m, j:j + 1].astype(np.float64) * o[row_of[m, j]].astype(np.float64)
+        assert mo.rel_err(y.cpu().numpy(), ref) <= 1e-6
+
+
+@needs_gpu
+def test_degenerate_inputs():
+    # T = 0: statistics are zero, nothing else is touched
+    shape = moe.make_shape(0, 128, 128, 8, 2, dtype=moe.MOE_BF16)
+    out = moe.alloc_forward(shape)
+    out.f.fill_(7)
+    out.P.fill_(7)
+    out.aux.fill_(7)
+    out.counts.fill_(7)
+    e = torch.empty(0, device="cuda", dtype=torch.bfloat16)
+    moe.moe_forward(shape, e, e, None, e, e, e, None, None, None, out.y, out.idx, out.gate, out.counts, out.kept,
+                    out.f, out.P, out.aux, out.offsets, None, out.row_of, out.ws)
+    torch.cuda.synchronize()
+    assert torch.all(out.f == 0) and torch.all(out.P == 0) and float(out.aux) == 0 and torch.all(out.counts == 0)
+    assert torch.all(out.offsets == 0)
+    # router weight zero: every logit ties, experts 0..k-1 win with gates 1/k
+    w = wl.scaled(BASE["mixtral_prefill"], name="ties", T=70, d=128, d_e=128, E=8, k=3)
+    inp = wl.make_inputs(w)
+    dev = upload(inp)
+    shape, _ = gp.shape_of(w)
+    out = moe.forward(shape, dev.x, torch.zeros_like(dev.w_r), None, dev.w_gate, dev.w_up, dev.w_down)
+    torch.cuda.synchronize()
+    assert torch.all(out.idx.cpu() == torch.arange(3, dtype=torch.int32))
+    assert torch.allclose(out.gate.cpu(), torch.full((70, 3), 1 / 3), atol=1e-7)
+    assert torch.allclose(out.P.cpu(), torch.full((8,), 1 / 8), atol=1e-7)
+    # capacity 0: every assignment dropped, y = 0 (no shared expert) -- the residual carries the token
+    shape0 = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=0, dtype=moe.MOE_BF16)
+    out = moe.forward(shape0, dev.x, dev.w_r, None, dev.w_gate, dev.w_up, dev.w_down)
+    torch.cuda.synchronize()
+    assert torch.all(out.y == 0) and torch.all(out.row_of == -1) and torch.all(out.kept == 0)
+    assert int(out.counts.sum()) == w.T * w.k
+    # a dominant bias sends every token's top choice to expert 5; capacity 9 keeps the first 9
+    b = torch.zeros(8, dtype=torch.float32, device="cuda")
+    b[5] = 50.0
+    shape9 = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=9, dtype=moe.MOE_BF16)
+    out = moe.forward(shape9, dev.x, dev.w_r, b, dev.w_gate, dev.w_up, dev.w_down)
+    torch.cuda.synchronize()
+    assert torch.all(out.idx[:, 0] == 5)
+    ro = out.row_of.cpu().numpy()
+    assert np.all(ro[:9, 0] >= 0) and np.all(ro[9:, 0] == -1) and int(out.kept[5]) == 9

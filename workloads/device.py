@@ -1,0 +1,55 @@
+"""Upload a workload's host inputs into torch device tensors (marshalling only).
+
+bf16 inputs travel as their raw 16-bit patterns and are reinterpreted as
+torch.bfloat16 on the device, so the device sees exactly the host bits.  Expert
+weights are drawn and copied one expert at a time (threads draw ahead), which
+keeps host memory small at the largest workload.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import Inputs, _threads
+
+
+def _to_dev(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+        return t.to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+@dataclass
+class DeviceInputs:
+    x: torch.Tensor
+    w_r: torch.Tensor
+    b_r: torch.Tensor | None
+    w_gate: torch.Tensor     # [E, d_e, d]
+    w_up: torch.Tensor       # [E, d_e, d]
+    w_down: torch.Tensor     # [E, d, d_e]
+    shared: tuple | None     # (W_g, W_u, W_d) or None
+
+
+def upload(inp: Inputs, device="cuda", threads: int | None = None) -> DeviceInputs:
+    wl = inp.wl
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    wg = torch.empty((wl.E, wl.d_e, wl.d), dtype=tdt, device=device)
+    wu = torch.empty((wl.E, wl.d_e, wl.d), dtype=tdt, device=device)
+    wd = torch.empty((wl.E, wl.d, wl.d_e), dtype=tdt, device=device)
+    with cf.ThreadPoolExecutor(max_workers=threads or _threads()) as ex:
+        futs = [ex.submit(inp.expert, e) for e in range(wl.E)]
+        for e, fu in enumerate(futs):
+            a, b, c = fu.result()
+            wg[e].copy_(_to_dev(a, wl.dtype, device))
+            wu[e].copy_(_to_dev(b, wl.dtype, device))
+            wd[e].copy_(_to_dev(c, wl.dtype, device))
+            futs[e] = None
+    sh = inp.shared()
+    shared = None if sh is None else tuple(_to_dev(m, wl.dtype, device) for m in sh)
+    b_r = None if inp.b_r is None else torch.from_numpy(inp.b_r).to(device)
+    return DeviceInputs(_to_dev(inp.x, wl.dtype, device), _to_dev(inp.w_r, wl.dtype, device), b_r,
+                        wg, wu, wd, shared)
