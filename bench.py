@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X, with roofline and CPU-oracle baseline.
+
+One step = one moe_forward call (router, dispatch, grouped SwiGLU experts, combine)
+over one batch of synthetic tokens already resident in device memory.  Default
+workload: the Mixtral 8x7B layer shape at a prefill batch of 4096 tokens (bf16
+weights and activations, fp32 accumulate).  A decode-batch line (16 tokens, same
+weights) rides along as "secondary".
+
+Prints ONE JSON line.  Timing: W untimed warm-up steps, then K steps bracketed by
+torch.cuda.synchronize(); per-stage durations come from HIP events that the library
+records on its stream at the stage boundaries (moe_forward's stage_events).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at Mixtral shape; % bf16 MFMA peak / % HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = C.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        arr = (C.c_void_p * n)()
+        for i in range(n):
+            h = C.c_void_p()
+            if self.hip.hipEventCreate(C.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = h
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = C.c_float()
+        if self.hip.hipEventElapsedTime(C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, arr):
+        for h in arr:
+            self.hip.hipEventDestroy(h)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "sparse_mixture_experts_17_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if the kernels
+    are unchanged since it was taken; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("per_launch_bytes", {}).get(workload, {}).get(stage)
+
+
+def run_gpu(wl_name, steps, warmup, dev_weights=None):
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_17_amd as moe
+    import workloads as wl
+    from workloads.device import upload
+
+    w = wl.get(wl_name)
+    inp = wl.make_inputs(w, seed=0)
+    t0 = time.time()
+    if dev_weights is None:
+        dev = upload(inp)
+    else:                                    # same experts and router (same streams), new tokens
+        import workloads.device as wd
+        dev = wd.DeviceInputs(wd._to_dev(inp.x, w.dtype, "cuda"), dev_weights.w_r, dev_weights.b_r,
+                              dev_weights.w_gate, dev_weights.w_up, dev_weights.w_down, dev_weights.shared)
+    t_up = time.time() - t0
+    cap = -1 if w.capacity_factor is None else moe.moe_capacity(w.T, w.k, w.E, w.capacity_factor)
+    shape = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
+                           d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32)
+    out = moe.alloc_forward(shape)
+    ev = HipEvents()
+    nst = moe._lib.MOE_NUM_STAGES
+    warm_ev = ev.create(nst + 1)
+    step_ev = [ev.create(nst + 1) for _ in range(steps)]
+    for _ in range(warmup):
+        moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared, out=out,
+                    stage_events=warm_ev)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared, out=out,
+                    stage_events=step_ev[s])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    stage_ms = np.array([[ev.elapsed_ms(e[i], e[i + 1]) for i in range(nst)] for e in step_ev])
+    ev.destroy(warm_ev)
+    for e in step_ev:
+        ev.destroy(e)
+    stages = {n: float(v) for n, v in zip(moe._lib.STAGE_NAMES, stage_ms.mean(axis=0))}
+    kept = out.kept.cpu().numpy()
+    R_kept = int(kept.sum())
+    touched = int((kept > 0).sum())
+    info = dict(w=w, shape=shape, cap=cap, total_ms=total_ms, wall_s=t_wall, stages=stages, R_kept=R_kept,
+                touched=touched, upload_s=t_up, dev=dev, inp=inp, idx=out.idx.cpu().numpy())
+    return info
+
+
+def layer_work(w, R_kept, touched):
+    """Algorithmic FLOPs and bytes of one layer call (per unit figures x units)."""
+    s = 2 if w.dtype == "bf16" else 4
+    flops_gate_up = 4 * w.d * w.d_e * R_kept
+    flops_down = 2 * w.d * w.d_e * R_kept
+    flops_router = 2 * w.d * w.E * w.T
+    flops_shared = 6 * w.d * w.d_e_shared * w.T
+    bytes_gate_up = touched * 2 * w.d * w.d_e * s + R_kept * w.d * s + R_kept * w.d_e * s
+    bytes_down = touched * w.d * w.d_e * s + R_kept * w.d_e * s + R_kept * w.d * 4
+    bytes_layer = (touched * 3 * w.d * w.d_e * s + w.E * w.d * s + w.T * w.d * s + w.T * w.d * 4 + w.T * w.k * 8
+                   + 3 * w.d * w.d_e_shared * s)
+    return dict(flops_gate_up=flops_gate_up, flops_down=flops_down, flops_layer=flops_gate_up + flops_down +
+                flops_router + flops_shared, bytes_gate_up=bytes_gate_up, bytes_down=bytes_down,
+                bytes_layer=bytes_layer)
+
+
+def cpu_baseline(info, target_s):
+    """The CPU oracle, unchanged, on the first n tokens of the same workload."""
+    import numpy as np
+    import workloads as wl
+    from oracle import moe_oracle as mo
+    try:
+        import threadpoolctl
+        pools = threadpoolctl.threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in pools if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    w, inp = info["w"], info["inp"]
+    x = wl.as_f64(inp.x, w.dtype)
+    w_r = wl.as_f64(inp.w_r, w.dtype)
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        experts = list(ex.map(lambda e: tuple(wl.as_f64(m, w.dtype) for m in inp.expert(e)), range(w.E)))
+    sh = inp.shared()
+    sh = None if sh is None else tuple(wl.as_f64(m, w.dtype) for m in sh)
+    cap = -1 if w.capacity_factor is None else mo.capacity(w.T, w.k, w.E, w.capacity_factor)
+    n = min(w.T, 64)
+    while True:
+        t0 = time.perf_counter()
+        mo.moe_forward(x[:n], w_r, experts, w.k, cap, inp.b_r, w.renormalize, sh)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or n >= w.T:
+            break
+        n = min(w.T, max(n * 2, int(n * target_s / 3 / max(dt, 1e-3))))
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of {w.name}, fp64 NumPy oracle, {dt:.2f} s "
+                      f"(weights widened to fp64 beforehand, untimed)"}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the layer is measured at its per-GPU shape; "
+                          "multi-GPU expert parallelism is design-only (see DESIGN.md)", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    print(f"[bench] workload {a.workload}: generating and uploading inputs", file=sys.stderr, flush=True)
+    info = run_gpu(a.workload, a.steps, a.warmup)
+    w = info["w"]
+    work = layer_work(w, info["R_kept"], info["touched"])
+    ms = info["total_ms"] / a.steps
+    value = w.T / (ms / 1e3)
+    st = info["stages"]
+    gu_ms = st["gate_up"]
+    mfma_bound = w.dtype == "bf16" and info["R_kept"] / max(info["touched"], 1) >= 315
+    if mfma_bound:
+        achieved = work["flops_gate_up"] / (gu_ms / 1e3) / 1e12
+        roof = {"kernel": "grouped_gemm gate_up (SiLU*up fused)", "bound": "mfma", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(w.name, "gate_up"), "avg_ms": gu_ms,
+                "algorithmic": f"4*d*d_e FLOPs per kept row x {info['R_kept']} rows"}
+    else:
+        achieved = work["bytes_gate_up"] / (gu_ms / 1e3) / 1e9
+        roof = {"kernel": "grouped_gemm gate_up (SiLU*up fused)", "bound": "hbm", "achieved": achieved,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": measured_traffic(w.name, "gate_up"), "avg_ms": gu_ms,
+                "algorithmic": "gate+up weights of touched experts + x_perm rows + h rows"}
+    layer = {"tflops": work["flops_layer"] / (ms / 1e3) / 1e12, "gbs": work["bytes_layer"] / (ms / 1e3) / 1e9}
+    layer["frac_mfma"] = layer["tflops"] / PEAK_BF16_TFLOPS
+    layer["frac_hbm"] = layer["gbs"] / PEAK_HBM_GBS
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "d_e": w.d_e, "E": w.E, "k": w.k,
+                   "capacity": info["cap"], "d_e_shared": w.d_e_shared, "parallelism": "none (1 GPU)",
+                   "weights": "random, seeded (N(0,1/fan_in)), bf16"},
+        "roofline": roof,
+        "layer": layer,
+        "stages_ms": st,
+    }
+    if not a.no_secondary and w.name == "mixtral_prefill":
+        print("[bench] secondary: mixtral_decode on the same weights", file=sys.stderr, flush=True)
+        dec = run_gpu("mixtral_decode", max(a.steps, 20), a.warmup, dev_weights=info["dev"])
+        wd = dec["w"]
+        dwork = layer_work(wd, dec["R_kept"], dec["touched"])
+        dms = dec["total_ms"] / max(a.steps, 20)
+        gb = dwork["bytes_gate_up"] / (dec["stages"]["gate_up"] / 1e3) / 1e9
+        line["secondary"] = {
+            "workload": wd.name, "value": wd.T / (dms / 1e3), "unit": "tokens/s", "ms_per_step": dms,
+            "stages_ms": dec["stages"], "experts_touched": dec["touched"],
+            "roofline": {"kernel": "grouped_gemm gate_up (decode tiles)", "bound": "hbm", "achieved": gb,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["stages"]["gate_up"]},
+            "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        }
+    if not a.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(info, a.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

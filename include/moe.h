@@ -147,14 +147,31 @@ moe_status moe_combine(const moe_shape *shape, const float *o, const int32_t *ro
  * Arguments as in the split calls; ws_gate/ws_up ([d_e_shared, d]) and ws_down
  * ([d, d_e_shared]) are the shared expert's weights, required iff d_e_shared > 0.
  * offsets [E+1], row_token [T*k] and row_of [T, k] are optional outputs (NULL: kept in the
- * workspace). */
+ * workspace).
+ * stage_events: NULL, or a host array of MOE_NUM_STAGES + 1 hipEvent_t (created by the
+ * caller) that the call records on `stream` at the stage boundaries, in the order of
+ * moe_stage, then once after the last stage; elapsed time between events i and i+1 is
+ * stage i.  Stages that do not run for this shape (the shared expert when d_e_shared = 0)
+ * are recorded as empty.  For timing only; results do not depend on it. */
+typedef enum {
+  MOE_STAGE_ROUTER = 0,      /* logits, softmax, top-k, gates, partial statistics */
+  MOE_STAGE_SCAN = 1,        /* counts, capacity, offsets, f, P, aux */
+  MOE_STAGE_PERMUTE = 2,     /* stable ranks, row_of / row_token, gather into x_perm */
+  MOE_STAGE_GATE_UP = 3,     /* grouped SiLU(x W_g) * (x W_u) */
+  MOE_STAGE_DOWN = 4,        /* grouped h W_d */
+  MOE_STAGE_SHARED_GATE_UP = 5,
+  MOE_STAGE_SHARED_DOWN = 6,
+  MOE_STAGE_COMBINE = 7,     /* gate-weighted sum back to token order */
+  MOE_NUM_STAGES = 8
+} moe_stage;
+
 moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_r, const float *b_r,
                        const void *w_gate, const void *w_up, const void *w_down,
                        const void *ws_gate, const void *ws_up, const void *ws_down,
                        float *y, int32_t *idx, float *gate, int32_t *counts, int32_t *kept,
                        float *f, float *P, float *aux,
                        int32_t *offsets, int32_t *row_token, int32_t *row_of,
-                       void *ws, size_t ws_bytes, void *stream);
+                       void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_NUM_STAGES = 8
+STAGE_NAMES = ["router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
 
@@ -32,7 +34,7 @@ SIGNATURES = {
     "moe_permute": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_expert_ffn": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_combine": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P]),
-    "moe_forward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 20 + [_P, C.c_size_t, _P]),
+    "moe_forward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 20 + [_P, C.c_size_t, _P, _P]),
 }
 
 _lib = None
@@ -46,6 +48,9 @@ def lib() -> C.CDLL:
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -c 'import __graft_entry__ as g; g.build()'` "
                               "(or python sparse_mixture_experts_17_amd/build.py)")
+        # torch's ROCm wheel carries its own HIP runtime (same soname): load torch first so
+        # the library binds to that one runtime and torch's streams and pointers are valid.
+        import torch  # noqa: F401
         l = C.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(l, name)

@@ -215,7 +215,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
                        const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
                        const void* ws_down, float* y, int32_t* idx, float* gate, int32_t* counts, int32_t* kept,
                        float* f, float* P, float* aux, int32_t* offsets, int32_t* row_token, int32_t* row_of,
-                       void* ws, size_t ws_bytes, void* stream) {
+                       void* ws, size_t ws_bytes, void* stream, void* const* stage_events) {
   moe_status v = check_shape(shape);
   if (v != MOE_OK) return v;
   const moe_shape& s = *shape;
@@ -229,29 +229,60 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   if (!offsets) offsets = at<int32_t>(ws, L.offsets);
   if (!row_token) row_token = at<int32_t>(ws, L.row_token);
   if (!row_of) row_of = at<int32_t>(ws, L.row_of);
+  // stage boundary marks (timing only)
+  int next_stage = 0;
+  auto mark = [&](int upto) -> bool {
+    if (!stage_events) return true;
+    for (; next_stage <= upto; ++next_stage)
+      if (hipEventRecord((hipEvent_t)stage_events[next_stage], st) != hipSuccess) return false;
+    return true;
+  };
+#define MOE_MARK(i) \
+  if (!mark(i)) return MOE_ERR_HIP
 
   const long long R = (long long)s.T * s.k;
   const GemmKind kind = choose_kind(std::max<long long>(R, 1), s.E, s.capacity);
   const int bm = gemm_block_m(kind);
-  moe_status r = run_router(s, x, w_r, b_r, idx, gate, counts, f, P, aux, kept, offsets, bm, bm, ws, st);
-  if (r != MOE_OK || s.T == 0) return r;
-  MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
-                             offsets, row_token, row_of, at<void>(ws, L.x_perm), st));
+  const int nb = route_blocks(s.T);
+  int32_t* ts1 = at<int32_t>(ws, L.tstart1);
+  int32_t* ts2 = at<int32_t>(ws, L.tstart2);
+  MOE_MARK(MOE_STAGE_ROUTER);
+  if (s.T > 0)
+    MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, idx, gate,
+                          at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
+  MOE_MARK(MOE_STAGE_SCAN);
+  MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts, kept,
+                      offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm, ts1, bm, ts2, st));
+  MOE_MARK(MOE_STAGE_PERMUTE);
+  if (s.T > 0)
+    MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
+                               offsets, row_token, row_of, at<void>(ws, L.x_perm), st));
+  MOE_MARK(MOE_STAGE_GATE_UP);
   const int tiles = max_m_tiles(R, s.E, s.capacity, bm);
-  r = run_ffn(s, s.E, at<void>(ws, L.x_perm), offsets, at<int32_t>(ws, L.tstart1), at<int32_t>(ws, L.tstart2), kind,
-              tiles, tiles, 0, s.d_e, w_gate, w_up, w_down, at<void>(ws, L.h), at<float>(ws, L.o), st);
-  if (r != MOE_OK) return r;
+  if (s.T > 0) {
+    MOE_HIP(launch_gemm_gateup(kind, s.dtype, at<void>(ws, L.x_perm), w_gate, w_up, offsets, ts1, s.E, 0, tiles,
+                               s.d_e, s.d, at<void>(ws, L.h), st));
+    MOE_MARK(MOE_STAGE_DOWN);
+    MOE_HIP(launch_gemm_down(kind, s.dtype, at<void>(ws, L.h), w_down, offsets, ts2, s.E, 0, tiles, s.d, s.d_e,
+                             at<float>(ws, L.o), st));
+  }
+  MOE_MARK(MOE_STAGE_SHARED_GATE_UP);
   const float* shared_out = nullptr;
-  if (s.d_e_shared > 0) {
+  if (s.d_e_shared > 0 && s.T > 0) {
     const GemmKind sk = choose_kind(s.T, 1, -1);
     const int sbm = gemm_block_m(sk);
     const int stiles = (s.T + sbm - 1) / sbm;
-    r = run_ffn(s, 1, x, nullptr, nullptr, nullptr, sk, stiles, stiles, s.T, s.d_e_shared, ws_gate, ws_up, ws_down,
-                at<void>(ws, L.sh_h), at<float>(ws, L.sh_o), st);
-    if (r != MOE_OK) return r;
+    MOE_HIP(launch_gemm_gateup(sk, s.dtype, x, ws_gate, ws_up, nullptr, nullptr, 1, s.T, stiles, s.d_e_shared, s.d,
+                               at<void>(ws, L.sh_h), st));
+    MOE_MARK(MOE_STAGE_SHARED_DOWN);
+    MOE_HIP(launch_gemm_down(sk, s.dtype, at<void>(ws, L.sh_h), ws_down, nullptr, nullptr, 1, s.T, stiles, s.d,
+                             s.d_e_shared, at<float>(ws, L.sh_o), st));
     shared_out = at<float>(ws, L.sh_o);
   }
-  MOE_HIP(launch_combine(at<float>(ws, L.o), row_of, gate, shared_out, y, s.T, s.d, s.k, st));
+  MOE_MARK(MOE_STAGE_COMBINE);
+  if (s.T > 0) MOE_HIP(launch_combine(at<float>(ws, L.o), row_of, gate, shared_out, y, s.T, s.d, s.k, st));
+  MOE_MARK(MOE_NUM_STAGES);
+#undef MOE_MARK
   return MOE_OK;
 }
 

@@ -90,11 +90,13 @@ def moe_combine(shape, o, row_of, gate, shared_out, y, stream=None) -> None:
 
 
 def moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, idx, gate, counts, kept,
-                f, P, aux, offsets, row_token, row_of, ws, stream=None) -> None:
+                f, P, aux, offsets, row_token, row_of, ws, stream=None, stage_events=None) -> None:
+    """stage_events: None, or a ctypes array of MOE_NUM_STAGES + 1 hipEvent_t handles."""
     check("moe_forward", lib().moe_forward(
         C.byref(shape), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
         _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(idx), _ptr(gate), _ptr(counts), _ptr(kept), _ptr(f), _ptr(P),
-        _ptr(aux), _ptr(offsets), _ptr(row_token), _ptr(row_of), _ptr(ws), _nbytes(ws), _stream(stream)))
+        _ptr(aux), _ptr(offsets), _ptr(row_token), _ptr(row_of), _ptr(ws), _nbytes(ws), _stream(stream),
+        stage_events))
 
 
 # ------------------------------------------------------------------ convenience
@@ -136,10 +138,10 @@ def alloc_forward(shape: MoeShape, device="cuda") -> ForwardOutputs:
 
 
 def forward(shape: MoeShape, x, w_r, b_r, w_gate, w_up, w_down, shared=None, out: ForwardOutputs | None = None,
-            stream=None) -> ForwardOutputs:
+            stream=None, stage_events=None) -> ForwardOutputs:
     """Run the whole layer; returns the outputs (allocating them unless `out` is given)."""
     out = out or alloc_forward(shape, x.device)
     sg, su, sd = shared if shared is not None else (None, None, None)
     moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, sg, su, sd, out.y, out.idx, out.gate, out.counts,
-                out.kept, out.f, out.P, out.aux, out.offsets, out.row_token, out.row_of, out.ws, stream)
+                out.kept, out.f, out.P, out.aux, out.offsets, out.row_token, out.row_of, out.ws, stream, stage_events)
     return out

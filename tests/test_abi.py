@@ -118,15 +118,15 @@ def test_device_calls_reject_null_and_small_workspace():
     #        row_token row_of ws; b_r, the shared weights and offsets/row_token/row_of are optional
     for i in (2, 6, 7, 8, 17, 18, 19):
         a[i] = None
-    assert lib.moe_forward(C.byref(s), *a[:20], a[20], 10, None) == 4
+    assert lib.moe_forward(C.byref(s), *a[:20], a[20], 10, None, None) == 4
     for i in (0, 1, 3, 4, 5, 9, 10, 11, 12, 13, 14, 15, 16, 20):
         b = list(a)
         b[i] = None
-        assert lib.moe_forward(C.byref(s), *b[:20], b[20], ws_need, None) == 1, i
+        assert lib.moe_forward(C.byref(s), *b[:20], b[20], ws_need, None, None) == 1, i
     # shared expert weights are required when d_e_shared > 0
     s2 = _shape(d_e_shared=256)
-    assert lib.moe_forward(C.byref(s2), *a[:20], a[20], moe.moe_workspace_bytes(s2), None) == 1
+    assert lib.moe_forward(C.byref(s2), *a[:20], a[20], moe.moe_workspace_bytes(s2), None, None) == 1
     # shape errors come first
     bad = _shape(k=9)
-    assert lib.moe_forward(C.byref(bad), *_args(20), FAKE, 1 << 40, None) == 2
+    assert lib.moe_forward(C.byref(bad), *_args(20), FAKE, 1 << 40, None, None) == 2
     assert lib.moe_route(None, *_args(9), FAKE, 1 << 40, None) == 1

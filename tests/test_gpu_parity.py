@@ -25,7 +25,8 @@ SMALL = [
     BASE["tiny_fp32"],
     wl.scaled(BASE["tiny_fp32"], name="fp32_ragged", T=77, d=256, d_e=384, E=6, k=3),
     wl.scaled(BASE["switch_capacity"], name="switch_small", T=1000, d=256, d_e=512, E=64, k=1),
-    wl.scaled(BASE["switch_capacity"], name="switch_raw_p", T=333, d=256, d_e=256, E=16, k=1, renormalize=False),
+    wl.scaled(BASE["switch_capacity"], name="switch_raw_p", T=700, d=256, d_e=256, E=16, k=1, renormalize=False,
+              capacity_factor=2.0),
     wl.scaled(BASE["switch_capacity"], name="capacity_top2", T=500, d=128, d_e=256, E=8, k=2, capacity_factor=1.0),
     wl.scaled(BASE["mixtral_prefill"], name="mixtral_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill"], name="mixtral_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
