@@ -52,6 +52,11 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # a kernel whose host stub the compiler dropped shows up as an undefined symbol
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "3moe" in l]
+    if missing:
+        raise RuntimeError("library has undefined kernel symbols: " + ", ".join(missing[:5]))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -7,7 +7,8 @@
 // stored [out, in], so both operands are read along the contraction dimension.
 //
 // One kernel template, three tile configurations:
-//   large   BM=128 BN=128, 2x2 waves  -- many rows per expert (MFMA-bound)
+//   large   BM=256 BN=128 (gate/up) or 256 (down), 2x2 waves, 128x128 accumulators per
+//           wave -- many rows per expert (MFMA-bound)
 //   stream  BM=192 BN=64,  1x4 waves  -- ~100-190 rows per expert: one block holds all
 //                                         of an expert's rows, so each weight tile is read once
 //   decode  BM=16  BN=64,  1x4 waves  -- a few rows per expert (weight streaming)
@@ -15,10 +16,10 @@
 // same n-tile share the A fragments) and applies SiLU(a) * b in registers; the down
 // variant writes fp32.
 //
-// Memory path per K step (128 bytes of each row): global -> registers (16 B per thread
-// per piece, coalesced along K) -> LDS (XOR-swizzled 16-byte pieces) -> MFMA operands,
-// with the next step's global loads in flight during the current step's MFMAs
-// (two LDS stages, one barrier per step).
+// Memory path per K step (128 bytes of each row): global -> LDS directly (16-byte
+// pieces, XOR-swizzled so MFMA operand reads are bank-conflict free) -> MFMA operands,
+// with the next step's loads in flight during the current step's MFMAs (two LDS
+// stages, one barrier per step).
 //
 // Scheduling: a persistent grid of (#CUs x occupancy) blocks; tiles are numbered
 // L = 0 .. live-1 and each XCD (blocks b with b % 8 == x) walks its own contiguous
@@ -44,6 +45,7 @@ struct GemmArgs {
 template <typename T, int BM, int BN, int WM, int WN, bool GATED>
 struct GemmTile {
   static constexpr int NT = WM * WN * kWave;
+  static constexpr int BM_ = BM, BN_ = BN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 16, TN = WTN / 16;
   static constexpr int NB = GATED ? 2 : 1;
@@ -55,10 +57,44 @@ struct GemmTile {
   static constexpr int B_IT = (BROWS * 8 + NT - 1) / NT;
   static constexpr int STAGE = (BM + BROWS) * ROWB;
   static constexpr int LDS = 2 * STAGE;
+  // Skip MFMAs of 16-row subtiles that hold no rows.  Worth a branch only where most
+  // subtiles can be empty (the stream and decode tiles); the large tile keeps a
+  // branch-free inner loop.
+  static constexpr bool SKIP_ROWS = BM != 256;
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
 };
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
+constexpr int kBufFlags = 0x00020000;
+
+// Enqueue one K step of A and B tiles into an LDS stage (asynchronous; completion is
+// tracked by vmcnt).  Wave-uniform branches only.
+template <typename Cfg>
+__device__ __forceinline__ void issue_stage(char* As, uint32_t kb, __amdgpu_buffer_rsrc_t rsA,
+                                            __amdgpu_buffer_rsrc_t rsB0, __amdgpu_buffer_rsrc_t rsB1,
+                                            const uint32_t* voffA, const uint32_t* voffB, int wave) {
+  char* Bs = As + Cfg::BM_ * 128;
+#pragma unroll
+  for (int it = 0; it < Cfg::A_IT; ++it) {
+    const int q0 = it * Cfg::NT + wave * kWave;
+    if (q0 < Cfg::BM_ * 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (__attribute__((address_space(3))) void*)(As + q0 * 16), 16,
+                                               voffA[it], kb, 0, 0);
+  }
+#pragma unroll
+  for (int it = 0; it < Cfg::B_IT; ++it) {
+    const int q0 = it * Cfg::NT + wave * kWave;
+    if (q0 < Cfg::BROWS * 8) {
+      auto* dst = (__attribute__((address_space(3))) void*)(Bs + q0 * 16);
+      if (Cfg::NB == 2 && (q0 >> 3) >= Cfg::BN_)                 // up rows of the gated product
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, voffB[it], kb, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, voffB[it], kb, 0, 0);
+    }
+  }
+}
 
 template <typename T, int BM, int BN, int WM, int WN, bool GATED>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
@@ -67,7 +103,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   constexpr int A_IT = Cfg::A_IT, B_IT = Cfg::B_IT, EPP = Cfg::EPP, BKE = Cfg::BKE, STAGE = Cfg::STAGE;
   extern __shared__ __align__(16) char lds[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
   const int wm = wave / WN, wn = wave % WN;
   const int N = args.N, K = args.K, G = args.G;
   const int ntn = N / BN;
@@ -99,9 +136,35 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       row0 = mt * BM;
       rows = min(BM, args.dense_rows - row0);
     }
+    // Buffer resources over this tile's A rows and B rows; per-lane 32-bit offsets are fixed
+    // for the tile and the K step rides in the scalar offset.
     const char* Ab = (const char*)args.A + (size_t)row0 * row_stride;
     const char* B0b = (const char*)args.B0 + ((size_t)g * N + (size_t)nt * BN) * row_stride;
-    const char* B1b = GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride : nullptr;
+    const char* B1b = GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride : B0b;
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, 0x7fffffff, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, 0x7fffffff, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, 0x7fffffff, kBufFlags);
+
+    // Global -> LDS without a register round trip (buffer_load_dwordx4 ... lds): lane L of a
+    // wave instruction writes LDS bytes [base + 16 L, base + 16 L + 16), so each lane loads
+    // the global piece that belongs at that swizzled LDS position.  Rows past `rows` repeat
+    // the last valid row: their results are never stored.
+    uint32_t voffA[A_IT], voffB[B_IT];
+#pragma unroll
+    for (int it = 0; it < A_IT; ++it) {
+      const int q = it * NT + wave * kWave + lane, r = q >> 3;
+      const int cl = (q & 7) ^ ((r >> 1) & 7);
+      voffA[it] = (uint32_t)(min(r, rows - 1) * row_stride + cl * 16);
+    }
+#pragma unroll
+    for (int it = 0; it < B_IT; ++it) {
+      const int q = it * NT + wave * kWave + lane, r = q >> 3;
+      const int cl = (q & 7) ^ ((r >> 1) & 7);
+      voffB[it] = (uint32_t)((GATED && r >= BN ? r - BN : r) * row_stride + cl * 16);
+    }
+    auto issue = [&](int ks, int s) {
+      issue_stage<Cfg>(lds + s * STAGE, (uint32_t)ks * 128, rsA, rsB0, rsB1, voffA, voffB, wave);
+    };
 
     f32x4_t acc0[TM][TN], acc1[TM][TN];
 #pragma unroll
@@ -112,77 +175,57 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         acc1[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
 
-    u32x4_t ra[A_IT], rb[B_IT];
-    auto load_global = [&](int ks) {
-      const size_t kb = (size_t)ks * 128;
-#pragma unroll
-      for (int it = 0; it < A_IT; ++it) {
-        const int p = tid + it * NT;
-        const int r = p >> 3, c = p & 7;
-        if (p < BM * 8 && r < rows)
-          ra[it] = *(const u32x4_t*)(Ab + (size_t)r * row_stride + kb + c * 16);
-        else
-          ra[it] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int it = 0; it < B_IT; ++it) {
-        const int p = tid + it * NT;
-        const int r = p >> 3, c = p & 7;
-        if (p < BROWS * 8) {
-          const char* src = (!GATED || r < BN) ? B0b + (size_t)r * row_stride : B1b + (size_t)(r - BN) * row_stride;
-          rb[it] = *(const u32x4_t*)(src + kb + c * 16);
-        }
-      }
-    };
-    auto store_lds = [&](int s) {
-      char* As = lds + s * STAGE;
-      char* Bs = As + BM * 128;
-#pragma unroll
-      for (int it = 0; it < A_IT; ++it) {
-        const int p = tid + it * NT;
-        if (p < BM * 8) *(u32x4_t*)(As + swz(p >> 3, p & 7)) = ra[it];
-      }
-#pragma unroll
-      for (int it = 0; it < B_IT; ++it) {
-        const int p = tid + it * NT;
-        if (p < BROWS * 8) *(u32x4_t*)(Bs + swz(p >> 3, p & 7)) = rb[it];
-      }
-    };
+    // One K step from LDS stage s: 2 chunks of 64 bytes.  The A fragment of the next
+    // subtile (and at the chunk boundary the next chunk's B fragments) is read before
+    // the current subtile's MFMAs are issued, so LDS latency hides behind MFMA work.
     auto compute = [&](int s) {
       const char* As = lds + s * STAGE;
       const char* Bs = As + BM * 128;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int c = kc * 4 + (lane >> 4);
-        u32x4_t bfr[TN * NB];
+      const int ra = wm * Cfg::WTM + (lane & 15);
+      const int rb = wn * Cfg::WTN + (lane & 15);
+      auto rdA = [&](int i, int kc) {
+        const int r = ra + i * 16;
+        return *(const u32x4_t*)(As + swz(r, kc * 4 + (lane >> 4)));
+      };
+      auto rdB = [&](u32x4_t* b, int kc) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int r = wn * Cfg::WTN + j * 16 + (lane & 15);
-          bfr[j] = *(const u32x4_t*)(Bs + swz(r, c));
-          if constexpr (GATED) bfr[TN + j] = *(const u32x4_t*)(Bs + swz(BN + r, c));
+          const int r = rb + j * 16;
+          b[j] = *(const u32x4_t*)(Bs + swz(r, kc * 4 + (lane >> 4)));
+          if constexpr (GATED) b[TN + j] = *(const u32x4_t*)(Bs + swz(BN + r, kc * 4 + (lane >> 4)));
         }
+      };
+      u32x4_t b0[TN * NB], b1[TN * NB];
+      rdB(b0, 0);
+      u32x4_t a_cur = rdA(0, 0), a_nxt;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          if (wm * Cfg::WTM + i * 16 < rows) {          // wave-uniform: skip all-padding subtiles
-            const int r = wm * Cfg::WTM + i * 16 + (lane & 15);
-            const u32x4_t af = *(const u32x4_t*)(As + swz(r, c));
+          if (i + 1 < TM) a_nxt = rdA(i + 1, kc);
+          else if (kc == 0) { rdB(b1, 1); a_nxt = rdA(0, 1); }
+          // keep the scheduler from sinking those reads below this subtile's MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+          const u32x4_t* b = kc == 0 ? b0 : b1;
+          if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {   // wave-uniform: skip padding subtiles
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-              Mfma<T>::step(acc0[i][j], af, bfr[j]);
-              if constexpr (GATED) Mfma<T>::step(acc1[i][j], af, bfr[TN + j]);
+              Mfma<T>::step(acc0[i][j], a_cur, b[j]);
+              if constexpr (GATED) Mfma<T>::step(acc1[i][j], a_cur, b[TN + j]);
             }
           }
+          a_cur = a_nxt;
         }
       }
     };
 
-    load_global(0);
-    store_lds(0);
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int ks = 0; ks < nks; ++ks) {
-      if (ks + 1 < nks) load_global(ks + 1);
+      if (ks + 1 < nks) issue(ks + 1, (ks + 1) & 1);   // lands while this step's MFMAs run
       compute(ks & 1);
-      if (ks + 1 < nks) store_lds((ks + 1) & 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
 
@@ -233,12 +276,19 @@ static hipError_t launch_cfg(const GemmArgs& a, int max_tiles_m, hipStream_t str
   return hipGetLastError();
 }
 
-int gemm_block_m(GemmKind kind) { return kind == kGemmLarge ? 128 : (kind == kGemmStream ? 192 : 16); }
+int gemm_block_m(GemmKind kind) { return kind == kGemmLarge ? 256 : (kind == kGemmStream ? 192 : 16); }
 
 template <typename T, bool GATED>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
-    case kGemmLarge: a.m_fast = 1; return launch_cfg<T, 128, 128, 2, 2, GATED>(a, max_tiles_m, s);
+    case kGemmLarge:
+      a.m_fast = 1;
+      if constexpr (GATED) {
+        return launch_cfg<T, 256, 128, 2, 2, GATED>(a, max_tiles_m, s);   // 128x(64+64) per wave
+      } else {
+        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 2, 2, GATED>(a, max_tiles_m, s);
+        return launch_cfg<T, 256, 128, 2, 2, GATED>(a, max_tiles_m, s);
+      }
     case kGemmStream: a.m_fast = 0; return launch_cfg<T, 192, 64, 1, 4, GATED>(a, max_tiles_m, s);
     default: a.m_fast = 0; return launch_cfg<T, 16, 64, 1, 4, GATED>(a, max_tiles_m, s);
   }
