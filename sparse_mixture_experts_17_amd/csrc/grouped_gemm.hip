@@ -23,7 +23,8 @@
 //
 // Scheduling: a persistent grid of (#CUs x occupancy) blocks; tiles are numbered
 // L = 0 .. live-1 and each XCD (blocks b with b % 8 == x) walks its own contiguous
-// eighth of L, so tiles that share operands run on the same L2.
+// eighth of L, so tiles that share operands run on the same L2 (see the tile order
+// in the kernel).
 #include <algorithm>
 
 #include "common.h"
@@ -39,7 +40,6 @@ struct GemmArgs {
   const int32_t* tstart;    // [G+1] first m-tile of each group (unused when dense)
   int G, dense_rows, N, K;
   void* C;                  // [rows, N]  (dtype for gated, fp32 for down)
-  int m_fast;               // tile order: 1 = m-tiles fastest, 0 = n-tiles fastest
 };
 
 template <typename T, int BM, int BN, int WM, int WN, bool GATED>
@@ -119,21 +119,43 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const size_t row_stride = (size_t)K * sizeof(T);   // bytes per row of A and of every weight
 
   for (int L = lo + j0; L < hi; L += bpx) {
-    int mt, nt;
-    if (args.m_fast) { mt = L % mt_live; nt = L / mt_live; }
-    else { nt = L % ntn; mt = L / ntn; }
-    int g = 0, row0, rows;
+    // Tile order: group by group (expert), and inside a group in super-tiles of all its
+    // m-tiles x GN n-tiles, GN chosen so one super-tile is about one XCD's worth of
+    // concurrent blocks.  Blocks that run together then share their weight tile (same
+    // n-tile, all m-tiles of the group: weights leave HBM once) and their activation
+    // rows (same m-tile, neighbouring n-tiles) in the XCD's L2.
+    const int mq = L / ntn;                            // any m-tile index in L's group range
+    int g = 0, t0g = 0, t1g = mt_live;
     if (offsets) {
-      int a = 0, b = G - 1;                            // largest g with tstart[g] <= mt
+      int a = 0, b = G - 1;                            // largest g with tstart[g] <= mq
       while (a < b) {
         int mid = (a + b + 1) >> 1;
-        if (tstart[mid] <= mt) a = mid; else b = mid - 1;
+        if (tstart[mid] <= mq) a = mid; else b = mid - 1;
       }
       g = a;
-      row0 = offsets[g] + (mt - tstart[g]) * BM;
+      t0g = tstart[g];
+      t1g = tstart[g + 1];
+    }
+    const int Me = t1g - t0g;                          // m-tiles of this group
+    const int l = L - t0g * ntn;
+    const int GN = max(1, bpx / Me);
+    const int full = ntn / GN;
+    int m, nt;
+    if (l < full * Me * GN) {
+      const int sb = l / (Me * GN), w = l - sb * (Me * GN);
+      m = w % Me;
+      nt = sb * GN + w / Me;
+    } else {
+      const int w = l - full * Me * GN;
+      m = w % Me;
+      nt = full * GN + w / Me;
+    }
+    int row0, rows;
+    if (offsets) {
+      row0 = offsets[g] + m * BM;
       rows = min(BM, offsets[g + 1] - row0);
     } else {
-      row0 = mt * BM;
+      row0 = m * BM;
       rows = min(BM, args.dense_rows - row0);
     }
     // Buffer resources over this tile's A rows and B rows; per-lane 32-bit offsets are fixed
@@ -282,22 +304,21 @@ template <typename T, bool GATED>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
     case kGemmLarge:
-      a.m_fast = 1;
       if constexpr (GATED) {
-        return launch_cfg<T, 256, 128, 2, 2, GATED>(a, max_tiles_m, s);   // 128x(64+64) per wave
+        return launch_cfg<T, 256, 128, 4, 2, GATED>(a, max_tiles_m, s);   // 64x(64+64) per wave
       } else {
-        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 2, 2, GATED>(a, max_tiles_m, s);
-        return launch_cfg<T, 256, 128, 2, 2, GATED>(a, max_tiles_m, s);
+        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED>(a, max_tiles_m, s);
+        return launch_cfg<T, 256, 128, 4, 2, GATED>(a, max_tiles_m, s);
       }
-    case kGemmStream: a.m_fast = 0; return launch_cfg<T, 192, 64, 1, 4, GATED>(a, max_tiles_m, s);
-    default: a.m_fast = 0; return launch_cfg<T, 16, 64, 1, 4, GATED>(a, max_tiles_m, s);
+    case kGemmStream: return launch_cfg<T, 192, 64, 1, 4, GATED>(a, max_tiles_m, s);
+    default: return launch_cfg<T, 16, 64, 1, 4, GATED>(a, max_tiles_m, s);
   }
 }
 
 hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const void* Wg, const void* Wu,
                               const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
                               int N, int K, void* H, hipStream_t stream) {
-  GemmArgs a{A, Wg, Wu, offsets, tstart, G, dense_rows, N, K, H, 0};
+  GemmArgs a{A, Wg, Wu, offsets, tstart, G, dense_rows, N, K, H};
   return dtype == 1 ? dispatch_kind<uint16_t, true>(kind, a, max_tiles_m, stream)
                     : dispatch_kind<float, true>(kind, a, max_tiles_m, stream);
 }
@@ -305,7 +326,7 @@ hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const voi
 hipError_t launch_gemm_down(GemmKind kind, int dtype, const void* H, const void* Wd, const int32_t* offsets,
                             const int32_t* tstart, int G, int dense_rows, int max_tiles_m, int N, int K, float* O,
                             hipStream_t stream) {
-  GemmArgs a{H, Wd, nullptr, offsets, tstart, G, dense_rows, N, K, O, 0};
+  GemmArgs a{H, Wd, nullptr, offsets, tstart, G, dense_rows, N, K, O};
   return dtype == 1 ? dispatch_kind<uint16_t, false>(kind, a, max_tiles_m, stream)
                     : dispatch_kind<float, false>(kind, a, max_tiles_m, stream);
 }
