@@ -7,19 +7,21 @@
 // stored [out, in], so both operands are read along the contraction dimension.
 //
 // One kernel template, three tile configurations:
-//   large   BM=256 BN=128 (gate/up) or 256 (down), 2x2 waves, 128x128 accumulators per
-//           wave -- many rows per expert (MFMA-bound)
-//   stream  BM=192 BN=64,  1x4 waves  -- ~100-190 rows per expert: one block holds all
-//                                         of an expert's rows, so each weight tile is read once
-//   decode  BM=16  BN=64,  1x4 waves  -- a few rows per expert (weight streaming)
+//   large   BM=256, BN=128 (gate/up) or 256 (down), 4x2 waves, 2 LDS stages -- many rows
+//           per expert (MFMA-bound)
+//   stream  BM=160, BN=128 (gate/up) or 256 (down), 2x4 waves, 3 LDS stages -- ~100-250
+//           rows per expert (weight streaming; an expert's m-tiles run side by side so
+//           its weight tile leaves HBM once)
+//   decode  BM=16, BN=64 (gate/up, 1x4 waves) or 32 (down, 1x2 waves), 4 LDS stages --
+//           a few rows per expert (weight streaming)
 // The gate/up variant holds two accumulators per output tile (gate and up rows of the
 // same n-tile share the A fragments) and applies SiLU(a) * b in registers; the down
 // variant writes fp32.
 //
 // Memory path per K step (128 bytes of each row): global -> LDS directly (16-byte
 // pieces, XOR-swizzled so MFMA operand reads are bank-conflict free) -> MFMA operands,
-// with the next step's loads in flight during the current step's MFMAs (two LDS
-// stages, one barrier per step).
+// with the next steps' loads in flight during the current step's MFMAs (a ring of
+// 2-4 LDS stages, one barrier per step).
 //
 // Scheduling: a persistent grid of (#CUs x occupancy) blocks; tiles are numbered
 // L = 0 .. live-1 and each XCD (blocks b with b % 8 == x) walks its own contiguous
@@ -33,7 +35,8 @@
 namespace moe {
 
 struct GemmArgs {
-  const void* A;            // [rows, K] activations in expert order
+  const void* A;            // [rows, K] activations in expert order, or token rows (a_rows)
+  const int32_t* a_rows;    // NULL, or row of A for each expert-ordered row (gather in the load)
   const void* B0;           // [G, N, K] gate (gated) or down weights
   const void* B1;           // [G, N, K] up weights (gated only)
   const int32_t* offsets;   // [G+1] or NULL (dense: one group of dense_rows)
@@ -42,7 +45,7 @@ struct GemmArgs {
   void* C;                  // [rows, N]  (dtype for gated, fp32 for down)
 };
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES>
 struct GemmTile {
   static constexpr int NT = WM * WN * kWave;
   static constexpr int BM_ = BM, BN_ = BN;
@@ -56,7 +59,18 @@ struct GemmTile {
   static constexpr int A_IT = (BM * 8 + NT - 1) / NT;
   static constexpr int B_IT = (BROWS * 8 + NT - 1) / NT;
   static constexpr int STAGE = (BM + BROWS) * ROWB;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int NSTAGE = STAGES;                            // LDS ring depth
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int NW = WM * WN;
+  // buffer loads per stage issued by the wave with the fewest (the last one); waiting
+  // until at most LPS * n are outstanding leaves n newer stages in flight
+  static constexpr int LPS = [] {
+    int n = 0;
+    for (int it = 0; it < A_IT; ++it) n += (it * NT + (NW - 1) * kWave < BM * 8);
+    for (int it = 0; it < B_IT; ++it) n += (it * NT + (NW - 1) * kWave < BROWS * 8);
+    return n;
+  }();
+  static_assert(LPS * (STAGES - 2) <= 63, "vmcnt range");
   // Skip MFMAs of 16-row subtiles that hold no rows.  Worth a branch only where most
   // subtiles can be empty (the stream and decode tiles); the large tile keeps a
   // branch-free inner loop.
@@ -68,6 +82,36 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >>
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufFlags = 0x00020000;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the LDS ring.  __syncthreads() would also wait for every
+// outstanding global load (its release fence), which would drain the ring; here each
+// wave has already waited for the loads it needs (vmcnt) and for its own LDS reads
+// (lgkmcnt), so a bare s_barrier is enough.  The empty asm statements keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until the oldest in-flight K step has landed, leaving `ahead` newer ones in flight.
+template <int LPS, int STAGES>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (STAGES <= 2) {
+    wait_vmcnt<0>();
+  } else {
+    switch (ahead) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<LPS>(); break;
+      default: wait_vmcnt<2 * LPS>(); break;
+    }
+  }
+}
 
 // Enqueue one K step of A and B tiles into an LDS stage (asynchronous; completion is
 // tracked by vmcnt).  Wave-uniform branches only.
@@ -96,9 +140,9 @@ __device__ __forceinline__ void issue_stage(char* As, uint32_t kb, __amdgpu_buff
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED>;
+  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES>;
   constexpr int NT = Cfg::NT, TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB, BROWS = Cfg::BROWS;
   constexpr int A_IT = Cfg::A_IT, B_IT = Cfg::B_IT, EPP = Cfg::EPP, BKE = Cfg::BKE, STAGE = Cfg::STAGE;
   extern __shared__ __align__(16) char lds[];
@@ -160,7 +204,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     }
     // Buffer resources over this tile's A rows and B rows; per-lane 32-bit offsets are fixed
     // for the tile and the K step rides in the scalar offset.
-    const char* Ab = (const char*)args.A + (size_t)row0 * row_stride;
+    const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride);
     const char* B0b = (const char*)args.B0 + ((size_t)g * N + (size_t)nt * BN) * row_stride;
     const char* B1b = GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride : B0b;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, 0x7fffffff, kBufFlags);
@@ -176,7 +220,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     for (int it = 0; it < A_IT; ++it) {
       const int q = it * NT + wave * kWave + lane, r = q >> 3;
       const int cl = (q & 7) ^ ((r >> 1) & 7);
-      voffA[it] = (uint32_t)(min(r, rows - 1) * row_stride + cl * 16);
+      const int rr = min(r, rows - 1);
+      const size_t arow = args.a_rows ? (size_t)args.a_rows[row0 + rr] : (size_t)rr;
+      voffA[it] = (uint32_t)(arow * row_stride + cl * 16);
     }
 #pragma unroll
     for (int it = 0; it < B_IT; ++it) {
@@ -241,15 +287,20 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       }
     };
 
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // STAGES-deep ring: up to STAGES-1 K steps in flight while one is consumed.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // previous tile's stores drained
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < nks) issue(p, p);
+    int slot = 0;
     for (int ks = 0; ks < nks; ++ks) {
-      if (ks + 1 < nks) issue(ks + 1, (ks + 1) & 1);   // lands while this step's MFMAs run
-      compute(ks & 1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      wait_stage<Cfg::LPS, STAGES>(min(STAGES - 2, nks - 1 - ks));   // step ks has landed
+      block_barrier();                                  // ... for every wave; slot ks-1 is free
+      if (ks + STAGES - 1 < nks) issue(ks + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
+      compute(slot);
+      slot = slot + 1 == STAGES ? 0 : slot + 1;
     }
+    __syncthreads();                                    // LDS free for the next tile
 
     // epilogue: lane holds rows 4*(lane/16)+q of each 16x16 tile, column lane%16
 #pragma unroll
@@ -276,10 +327,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 
 // ------------------------------------------------------------------------------ launch
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES>
 static hipError_t launch_cfg(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
-  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED>;
-  auto kern = grouped_gemm_kernel<T, BM, BN, WM, WN, GATED>;
+  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES>;
+  auto kern = grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES>;
   static const int occ = [&] {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
     int n = 0;
@@ -298,27 +349,40 @@ static hipError_t launch_cfg(const GemmArgs& a, int max_tiles_m, hipStream_t str
   return hipGetLastError();
 }
 
-int gemm_block_m(GemmKind kind) { return kind == kGemmLarge ? 256 : (kind == kGemmStream ? 192 : 16); }
+int gemm_block_m(GemmKind kind) { return kind == kGemmLarge ? 256 : (kind == kGemmStream ? 160 : 16); }
 
 template <typename T, bool GATED>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
     case kGemmLarge:
+      // 8 waves, 2 LDS stages: LDS bandwidth, not latency, is the limit here
       if constexpr (GATED) {
-        return launch_cfg<T, 256, 128, 4, 2, GATED>(a, max_tiles_m, s);   // 64x(64+64) per wave
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2>(a, max_tiles_m, s);   // 64x(64+64) per wave
       } else {
-        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED>(a, max_tiles_m, s);
-        return launch_cfg<T, 256, 128, 4, 2, GATED>(a, max_tiles_m, s);
+        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2>(a, max_tiles_m, s);
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2>(a, max_tiles_m, s);
       }
-    case kGemmStream: return launch_cfg<T, 192, 64, 1, 4, GATED>(a, max_tiles_m, s);
-    default: return launch_cfg<T, 16, 64, 1, 4, GATED>(a, max_tiles_m, s);
+    case kGemmStream:
+      // weight streaming with ~100-250 rows per expert: wide weight tiles, 3-deep ring so
+      // two K steps of weights are in flight per CU
+      if constexpr (GATED) {
+        return launch_cfg<T, 160, 128, 2, 4, GATED, 3>(a, max_tiles_m, s);   // 80x(32+32) per wave
+      } else {
+        if (a.N % 256 == 0) return launch_cfg<T, 160, 256, 2, 4, GATED, 3>(a, max_tiles_m, s);
+        return launch_cfg<T, 160, 128, 2, 4, GATED, 3>(a, max_tiles_m, s);
+      }
+    default:
+      // decode: a few rows per expert, 4-deep ring; the down product has half the weight
+      // rows of gate/up, so narrower tiles give it as many blocks streaming in parallel
+      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, 4>(a, max_tiles_m, s);
+      else return launch_cfg<T, 16, 32, 1, 2, GATED, 4>(a, max_tiles_m, s);
   }
 }
 
-hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const void* Wg, const void* Wu,
-                              const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
-                              int N, int K, void* H, hipStream_t stream) {
-  GemmArgs a{A, Wg, Wu, offsets, tstart, G, dense_rows, N, K, H};
+hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const int32_t* a_rows, const void* Wg,
+                              const void* Wu, const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
+                              int max_tiles_m, int N, int K, void* H, hipStream_t stream) {
+  GemmArgs a{A, a_rows, Wg, Wu, offsets, tstart, G, dense_rows, N, K, H};
   return dtype == 1 ? dispatch_kind<uint16_t, true>(kind, a, max_tiles_m, stream)
                     : dispatch_kind<float, true>(kind, a, max_tiles_m, stream);
 }
@@ -326,7 +390,7 @@ hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const voi
 hipError_t launch_gemm_down(GemmKind kind, int dtype, const void* H, const void* Wd, const int32_t* offsets,
                             const int32_t* tstart, int G, int dense_rows, int max_tiles_m, int N, int K, float* O,
                             hipStream_t stream) {
-  GemmArgs a{H, Wd, nullptr, offsets, tstart, G, dense_rows, N, K, O};
+  GemmArgs a{H, nullptr, Wd, nullptr, offsets, tstart, G, dense_rows, N, K, O};
   return dtype == 1 ? dispatch_kind<uint16_t, false>(kind, a, max_tiles_m, stream)
                     : dispatch_kind<float, false>(kind, a, max_tiles_m, stream);
 }

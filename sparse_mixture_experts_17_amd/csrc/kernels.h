@@ -34,7 +34,7 @@ hipError_t launch_tile_sched(const int32_t* offsets, int E, int bm1, int32_t* ts
                              int32_t* tstart2, hipStream_t stream);
 
 // Stable ranks within each expert, capacity, row_of / row_token, and the gather
-// x_perm[row] = x[token].
+// x_perm[row] = x[token] (skipped when x_perm is NULL).
 hipError_t launch_rank_gather(int dtype, const void* x, const int32_t* idx, int T, int d, int k, int E,
                               int cap, const int32_t* chunk_base, const int32_t* offsets,
                               int32_t* row_token, int32_t* row_of, void* x_perm, hipStream_t stream);
@@ -47,10 +47,12 @@ hipError_t launch_combine(const float* o, const int32_t* row_of, const float* ga
 enum GemmKind { kGemmLarge = 0, kGemmStream = 1, kGemmDecode = 2 };
 int gemm_block_m(GemmKind kind);
 
-// Gate/up product with the SiLU(a) * b epilogue:  h[r, n] = SiLU(A_e W_g[e]^T) * (A_e W_u[e]^T).
+// Gate/up product with the SiLU(a) * b epilogue:  h[r, n] = SiLU(A_r W_g[e]^T) * (A_r W_u[e]^T).
+// A_r is row r of A, or row a_rows[r] of A when a_rows != NULL (the dispatch gather done by
+// the loads; the byte offset a_rows[r] * K * elem must stay below 2^32).
 // offsets == NULL means one group of `dense_rows` rows.  tstart = per-group tile starts.
-hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const void* Wg, const void* Wu,
-                              const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
+hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const int32_t* a_rows, const void* Wg,
+                              const void* Wu, const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
                               int max_tiles_m, int N, int K, void* H, hipStream_t stream);
 
 // Down projection:  o[r, n] = H_e W_d[e]^T, fp32 out.

@@ -57,6 +57,8 @@ moe_status check_shape(const moe_shape* s) {
   if (s->E > 1024 || s->k > 16) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 || s->d_e % 128 || s->d_e_shared % 128) return MOE_ERR_UNSUPPORTED;
   if ((long long)s->T * s->k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  // the forward gathers rows of x with 32-bit byte offsets: T*d*elem_size < 2^32
+  if ((long long)s->T * s->d * (s->dtype == MOE_BF16 ? 2 : 4) >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
   // the gather addresses x_perm in 16-byte units with int32: T*k*d*elem_size / 16 < 2^31
   if ((long long)s->T * s->k * (long long)s->d * (s->dtype == MOE_BF16 ? 2 : 4) >= (1LL << 35))
     return MOE_ERR_UNSUPPORTED;
@@ -108,7 +110,8 @@ moe_status run_router(const moe_shape& s, const void* x, const void* w_r, const 
 moe_status run_ffn(const moe_shape& s, int G, const void* A, const int32_t* offsets, const int32_t* tstart1,
                    const int32_t* tstart2, GemmKind kind, int tiles1, int tiles2, int dense_rows, int d_e,
                    const void* wg, const void* wu, const void* wd, void* h, float* o, hipStream_t st) {
-  MOE_HIP(launch_gemm_gateup(kind, s.dtype, A, wg, wu, offsets, tstart1, G, dense_rows, tiles1, d_e, s.d, h, st));
+  MOE_HIP(launch_gemm_gateup(kind, s.dtype, A, nullptr, wg, wu, offsets, tstart1, G, dense_rows, tiles1, d_e, s.d, h,
+                             st));
   MOE_HIP(launch_gemm_down(kind, s.dtype, h, wd, offsets, tstart2, G, dense_rows, tiles2, s.d, d_e, o, st));
   return MOE_OK;
 }
@@ -253,15 +256,17 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   MOE_MARK(MOE_STAGE_SCAN);
   MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts, kept,
                       offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm, ts1, bm, ts2, st));
+  // The forward pass does not materialise x_perm: the permute stage produces the row
+  // indices and the gate/up GEMM gathers token rows of x through them as it loads.
   MOE_MARK(MOE_STAGE_PERMUTE);
   if (s.T > 0)
     MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
-                               offsets, row_token, row_of, at<void>(ws, L.x_perm), st));
+                               offsets, row_token, row_of, nullptr, st));
   MOE_MARK(MOE_STAGE_GATE_UP);
   const int tiles = max_m_tiles(R, s.E, s.capacity, bm);
   if (s.T > 0) {
-    MOE_HIP(launch_gemm_gateup(kind, s.dtype, at<void>(ws, L.x_perm), w_gate, w_up, offsets, ts1, s.E, 0, tiles,
-                               s.d_e, s.d, at<void>(ws, L.h), st));
+    MOE_HIP(launch_gemm_gateup(kind, s.dtype, x, row_token, w_gate, w_up, offsets, ts1, s.E, 0, tiles, s.d_e, s.d,
+                               at<void>(ws, L.h), st));
     MOE_MARK(MOE_STAGE_DOWN);
     MOE_HIP(launch_gemm_down(kind, s.dtype, at<void>(ws, L.h), w_down, offsets, ts2, s.E, 0, tiles, s.d, s.d_e,
                              at<float>(ws, L.o), st));
@@ -272,8 +277,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
     const GemmKind sk = choose_kind(s.T, 1, -1);
     const int sbm = gemm_block_m(sk);
     const int stiles = (s.T + sbm - 1) / sbm;
-    MOE_HIP(launch_gemm_gateup(sk, s.dtype, x, ws_gate, ws_up, nullptr, nullptr, 1, s.T, stiles, s.d_e_shared, s.d,
-                               at<void>(ws, L.sh_h), st));
+    MOE_HIP(launch_gemm_gateup(sk, s.dtype, x, nullptr, ws_gate, ws_up, nullptr, nullptr, 1, s.T, stiles,
+                               s.d_e_shared, s.d, at<void>(ws, L.sh_h), st));
     MOE_MARK(MOE_STAGE_SHARED_DOWN);
     MOE_HIP(launch_gemm_down(sk, s.dtype, at<void>(ws, L.sh_h), ws_down, nullptr, nullptr, 1, s.T, stiles, s.d,
                              s.d_e_shared, at<float>(ws, L.sh_o), st));

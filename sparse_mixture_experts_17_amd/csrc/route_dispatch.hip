@@ -10,6 +10,8 @@
 // by a stable counting sort (histogram per chunk of tokens, scan, rank in arrival order),
 // with the capacity limit of AI Engineering Illustrated, "The safety valve is a capacity
 // limit": an expert keeps its first `cap` assignments in arrival order t*k + j.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -19,10 +21,35 @@ namespace moe {
 //
 // One block = 16 tokens x all E experts, 4 waves.
 // Phase 1: logits[16][E] via 16x16 MFMA tiles (A = 16 token rows, B = 16 router rows),
-//          operands read straight from global memory (16 B per lane), bias added, to LDS.
+//          operands read straight from global memory (16 B per lane).  Expert tiles are
+//          dealt to waves in groups of up to 4; when there are fewer than 4 groups the
+//          contraction is split across waves instead, and the partial logits are summed
+//          in LDS in a fixed order (bias added last).
 // Phase 2: each wave takes 4 tokens: softmax over E (lane l holds experts l + 64 q),
 //          k rounds of wave arg-max (ties -> lower index), gates, LDS histogram.
 // Phase 3: per-block partial sums of p (fixed order over waves) and histogram to global.
+
+// Contraction split of the router for E experts: 4 waves share the work.
+__host__ __device__ inline int router_ksplit(int E) {
+  const int groups = ((E + 15) / 16 + 3) / 4;
+  return groups == 1 ? 4 : (groups == 2 ? 2 : 1);
+}
+
+// Partial logits of NTL consecutive expert tiles over chunks [c0, c1) of 64 bytes.
+template <typename T, int NTL>
+__device__ __forceinline__ void router_tiles(const char* xrow, const char* const* wrow, int c0, int c1,
+                                             f32x4_t* acc) {
+#pragma unroll 8
+  for (int c = c0; c < c1; ++c) {
+    const u32x4_t a = *(const u32x4_t*)(xrow + (size_t)c * 64);
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) {
+      const u32x4_t b = *(const u32x4_t*)(wrow[j] + (size_t)c * 64);
+      Mfma<T>::step(acc[j], a, b);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
                                                      const float* __restrict__ b_r, int T_, int d, int E,
@@ -30,13 +57,14 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
                                                      float* __restrict__ gate, float* __restrict__ p_part,
                                                      int32_t* __restrict__ hist) {
   constexpr int TB = kRouteTokens;
+  const int ksplit = router_ksplit(E);
   extern __shared__ float smem[];
-  float* logits = smem;                // [TB][E]
-  float* psum = smem + TB * E;         // [4][E]
-  int* lhist = (int*)(psum + 4 * E);   // [E]
+  float* logits = smem;                          // [TB][E]  (partials: [ksplit][TB][E])
+  float* psum = smem + ksplit * TB * E;          // [4][E]
+  int* lhist = (int*)(psum + 4 * E);             // [E]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
   for (int i = tid; i < E; i += 256) lhist[i] = 0;
 
@@ -47,7 +75,10 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
   const char* xrow = (const char*)x + (size_t)tok * row_bytes + grp * 16;
   const int nchunks = (int)(row_bytes / 64);
   const int n_et = (E + 15) / 16;
-  for (int tb = wave * 4; tb < n_et; tb += 16) {     // up to 4 expert tiles per wave per pass
+  const int kpart = wave % ksplit;
+  const int c0 = kpart * nchunks / ksplit, c1 = (kpart + 1) * nchunks / ksplit;
+  float* part = logits + kpart * TB * E;
+  for (int tb = (wave / ksplit) * 4; tb < n_et; tb += 4 * (4 / ksplit)) {
     const int ntl = min(4, n_et - tb);
     const char* wrow[4];
 #pragma unroll
@@ -58,38 +89,26 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
     f32x4_t acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (ntl == 4) {
-#pragma unroll 4
-      for (int c = 0; c < nchunks; ++c) {
-        u32x4_t a = *(const u32x4_t*)(xrow + (size_t)c * 64);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4_t b = *(const u32x4_t*)(wrow[j] + (size_t)c * 64);
-          Mfma<T>::step(acc[j], a, b);
-        }
-      }
-    } else {
-#pragma unroll 2
-      for (int c = 0; c < nchunks; ++c) {
-        u32x4_t a = *(const u32x4_t*)(xrow + (size_t)c * 64);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < ntl) {
-            u32x4_t b = *(const u32x4_t*)(wrow[j] + (size_t)c * 64);
-            Mfma<T>::step(acc[j], a, b);
-          }
-        }
-      }
+    switch (ntl) {
+      case 4: router_tiles<T, 4>(xrow, wrow, c0, c1, acc); break;
+      case 3: router_tiles<T, 3>(xrow, wrow, c0, c1, acc); break;
+      case 2: router_tiles<T, 2>(xrow, wrow, c0, c1, acc); break;
+      default: router_tiles<T, 1>(xrow, wrow, c0, c1, acc); break;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int e = (tb + j) * 16 + r16;
       if (j < ntl && e < E) {
-        float bias = b_r ? b_r[e] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) logits[(grp * 4 + i) * E + e] = acc[j][i] + bias;
+        for (int i = 0; i < 4; ++i) part[(grp * 4 + i) * E + e] = acc[j][i];
       }
     }
+  }
+  __syncthreads();
+  for (int i = tid; i < TB * E; i += 256) {          // fixed-order sum of the K parts, then bias
+    float v = logits[i];
+    for (int p = 1; p < ksplit; ++p) v += logits[p * TB * E + i];
+    logits[i] = v + (b_r ? b_r[i % E] : 0.f);
   }
   __syncthreads();
 
@@ -169,7 +188,7 @@ hipError_t launch_router(int dtype, const void* x, const void* w_r, const float*
                          int k, int renorm, int32_t* idx, float* gate, float* p_part, int32_t* hist,
                          hipStream_t stream) {
   const int nb = route_blocks(T);
-  const size_t lds = (size_t)(kRouteTokens * E + 4 * E) * sizeof(float) + (size_t)E * sizeof(int);
+  const size_t lds = (size_t)(router_ksplit(E) * kRouteTokens * E + 4 * E) * sizeof(float) + (size_t)E * sizeof(int);
   if (dtype == 1) {
     auto kern = router_kernel<uint16_t>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -206,8 +225,11 @@ hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, h
 
 // ------------------------------------------------------------------------------ scan (1 block)
 //
-// Thread e walks the chunks in order: chunk_base[b][e] = assignments to e in chunks < b;
-// counts[e] = all of them.  kept = min(counts, cap); offsets and tile starts are
+// Per-chunk bases by expert: chunk_base[b][e] = assignments to e in chunks < b;
+// counts[e] = all of them.  The chunks are cut into G = 1024 / E contiguous groups
+// so all 1024 threads work: thread (g, e) sums its group's chunks, a serial pass over
+// the G group sums per expert turns them into group bases, and each thread then
+// writes its chunks' bases.  kept = min(counts, cap); offsets and tile starts are
 // exclusive scans over experts.  f, P, aux use fixed-order sums.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist,
                                                     const float* __restrict__ p_part, int nb, int T, int k,
@@ -218,18 +240,40 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ tstart1, int bm2,
                                                     int32_t* __restrict__ tstart2) {
   __shared__ int s_scan[1024];
+  __shared__ int s_part[1024];
   __shared__ float s_red[1024];
-  const int e = threadIdx.x;
-  int cnt = 0;
+  const int tid = threadIdx.x;
+  const int G = max(1, 1024 / E);
+  const int ge = tid / E, ee = tid - ge * E;              // group and expert of this thread
+  const bool act = ge < G;
+  const int b0 = act ? (int)((long long)ge * nb / G) : 0, b1 = act ? (int)((long long)(ge + 1) * nb / G) : 0;
+  int c = 0;
   float ps = 0.f;
-  if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      chunk_base[(size_t)b * E + e] = cnt;
-      cnt += hist[(size_t)b * E + e];
+  for (int b = b0; b < b1; ++b) c += hist[(size_t)b * E + ee];
+  if (p_part)
+    for (int b = b0; b < b1; ++b) ps += p_part[(size_t)b * E + ee];
+  s_part[tid] = c;
+  s_red[tid] = ps;
+  __syncthreads();
+  int cnt = 0;
+  float pe = 0.f;
+  if (tid < E) {                                          // group bases and totals per expert
+    for (int g = 0; g < G; ++g) {
+      const int v = s_part[g * E + tid];
+      s_part[g * E + tid] = cnt;
+      cnt += v;
+      pe += s_red[g * E + tid];
     }
-    if (p_part)
-      for (int b = 0; b < nb; ++b) ps += p_part[(size_t)b * E + e];
   }
+  __syncthreads();
+  if (act) {
+    int run = s_part[tid];
+    for (int b = b0; b < b1; ++b) {
+      chunk_base[(size_t)b * E + ee] = run;
+      run += hist[(size_t)b * E + ee];
+    }
+  }
+  const int e = tid;
   const int kp = e < E ? (cap < 0 ? cnt : min(cnt, cap)) : 0;
   int tot;
   const int off = block1024_exclusive_scan(kp, s_scan, &tot);
@@ -252,11 +296,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (p_part) {
     const long long R = (long long)T * k;
     float fe = (e < E && R > 0) ? (float)((double)cnt / (double)R) : 0.f;
-    float Pe = (e < E && T > 0) ? ps / (float)T : 0.f;
+    float Pe = (e < E && T > 0) ? pe / (float)T : 0.f;
     if (e < E) {
       f[e] = fe;
       P[e] = Pe;
     }
+    __syncthreads();
     s_red[e] = fe * Pe;
     __syncthreads();
     for (int h = 512; h > 0; h >>= 1) {
@@ -319,7 +364,7 @@ __global__ __launch_bounds__(256) void rank_gather_kernel(const T* __restrict__ 
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kRouteTokens;
   const int n = min(kRouteTokens, T_ - t0) * k;
-  if (tid < n) s_e[tid] = idx[(size_t)t0 * k + tid];
+  if (tid < n) s_e[tid] = idx[(size_t)t0 * k + tid];   // the other splits redo this small rank
   __syncthreads();
   if (tid < n) {
     const int e = s_e[tid];
@@ -327,15 +372,21 @@ __global__ __launch_bounds__(256) void rank_gather_kernel(const T* __restrict__ 
     for (int j = 0; j < tid; ++j) r += (s_e[j] == e);
     const int g = chunk_base[(size_t)blockIdx.x * E + e] + r;
     const int row = (cap < 0 || g < cap) ? offsets[e] + g : -1;
-    row_of[(size_t)t0 * k + tid] = row;
     s_row[tid] = row;
-    if (row >= 0) row_token[row] = t0 + tid / k;
+    if (blockIdx.y == 0) {                       // one split writes the index outputs
+      row_of[(size_t)t0 * k + tid] = row;
+      if (row >= 0) row_token[row] = t0 + tid / k;
+    }
   }
+  if (!x_perm) return;                         // indices only; the GEMM gathers rows itself
   __syncthreads();
   const int P = (int)((size_t)d * sizeof(T) / 16);   // 16-byte pieces per row
-  const int total = n * P;
+  // the copy of this chunk is shared by gridDim.y blocks (more blocks for small batches)
+  const int total_all = n * P;
+  const int lo = (int)((long long)total_all * blockIdx.y / gridDim.y);
+  const int total = (int)((long long)total_all * (blockIdx.y + 1) / gridDim.y);
   constexpr int U = 4;
-  for (int base = tid; base < total; base += 256 * U) {
+  for (int base = lo + tid; base < total; base += 256 * U) {
     u32x4_t v[U];
     int dst[U];
 #pragma unroll
@@ -361,12 +412,15 @@ __global__ __launch_bounds__(256) void rank_gather_kernel(const T* __restrict__ 
 hipError_t launch_rank_gather(int dtype, const void* x, const int32_t* idx, int T, int d, int k, int E, int cap,
                               const int32_t* chunk_base, const int32_t* offsets, int32_t* row_token,
                               int32_t* row_of, void* x_perm, hipStream_t stream) {
+  const int nb = route_blocks(T);
+  const int splits = x_perm ? std::max(1, std::min(16, 512 / nb)) : 1;
+  const dim3 grid(nb, splits);
   if (dtype == 1)
-    hipLaunchKernelGGL(rank_gather_kernel<uint16_t>, dim3(route_blocks(T)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(rank_gather_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        (const uint16_t*)x, idx, T, d, k, E, cap, chunk_base, offsets, row_token, row_of,
                        (uint16_t*)x_perm);
   else
-    hipLaunchKernelGGL(rank_gather_kernel<float>, dim3(route_blocks(T)), dim3(256), 0, stream, (const float*)x,
+    hipLaunchKernelGGL(rank_gather_kernel<float>, grid, dim3(256), 0, stream, (const float*)x,
                        idx, T, d, k, E, cap, chunk_base, offsets, row_token, row_of, (float*)x_perm);
   return hipGetLastError();
 }
