@@ -151,8 +151,10 @@ moe_status moe_combine(const moe_shape *shape, const float *o, const int32_t *ro
  * stage_events: NULL, or a host array of MOE_NUM_STAGES + 1 hipEvent_t (created by the
  * caller) that the call records on `stream` at the stage boundaries, in the order of
  * moe_stage, then once after the last stage; elapsed time between events i and i+1 is
- * stage i.  Stages that do not run for this shape (the shared expert when d_e_shared = 0)
- * are recorded as empty.  For timing only; results do not depend on it. */
+ * stage i.  NULL entries are skipped (record only the boundaries you need: each record
+ * costs a few microseconds of stream time).  Stages that do not run for this shape (the
+ * shared expert when d_e_shared = 0) are recorded as empty.  For timing only; results do
+ * not depend on it. */
 typedef enum {
   MOE_STAGE_ROUTER = 0,      /* logits, softmax, top-k, gates, partial statistics */
   MOE_STAGE_SCAN = 1,        /* counts, capacity, offsets, f, P, aux */

@@ -237,7 +237,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   auto mark = [&](int upto) -> bool {
     if (!stage_events) return true;
     for (; next_stage <= upto; ++next_stage)
-      if (hipEventRecord((hipEvent_t)stage_events[next_stage], st) != hipSuccess) return false;
+      if (stage_events[next_stage] && hipEventRecord((hipEvent_t)stage_events[next_stage], st) != hipSuccess)
+        return false;
     return true;
   };
 #define MOE_MARK(i) \
