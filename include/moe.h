@@ -106,7 +106,7 @@ moe_status moe_route(const moe_shape *shape, const void *x, const void *w_r, con
 /* Dispatch: counting sort of the T*k assignments by expert, stable in arrival order
  * t*k + j, truncated at shape->capacity, then a gather of token rows into
  * expert-contiguous order (the per-expert token lists of the PyTorch layer on the
- * kevinluzbetak.com page, laid out as one list; "sort tokens by expert").
+ * kevinluzbetak.com page, laid out as one list: tokens sorted by expert).
  *   x         [T, d]      dtype     token rows
  *   idx       [T, k]      int32     expert of each assignment (each in [0, E))
  *   kept      [E]         int32     out: min(count_e, capacity)

@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE (see the package docstring).
 
-It evaluates the "wasteful" form that Zero to Frontier §13.1 uses to check its
+It evaluates the dense form that Zero to Frontier §13.1 uses to check its
 worked example ("A worked example small enough to check by hand"): run every
 expert on every token and multiply the unchosen ones by a zero gate.  It is an
 independent second implementation of the same definition: nested loops over

@@ -22,8 +22,8 @@ in the design notes of the repository):
     kevinluzbetak.com routing paragraph) -- equal in exact arithmetic to the
     softmax over the k chosen logits of the "The MoE layer" gate equation.
   * ``renormalize=False`` keeps the raw softmax probability as the gate (the
-    Switch top-1 variant, and the "skip the renormalisation" remark of the
-    kevinluzbetak.com router worked example).
+    Switch top-1 variant; the kevinluzbetak.com router worked example notes that
+    some implementations use the raw probabilities).
   * capacity: each expert keeps at most ``cap`` assignments; assignments are
     taken in arrival order t*k + j and the rest are dropped.  A dropped
     assignment contributes nothing; a surviving gate is not renormalised; a
