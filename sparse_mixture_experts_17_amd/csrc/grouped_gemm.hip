@@ -272,8 +272,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         for (int i = 0; i < TM; ++i) {
           if (i + 1 < TM) a_nxt = rdA(i + 1, kc);
           else if (kc == 0) { rdB(b1, 1); a_nxt = rdA(0, 1); }
-          // keep the scheduler from sinking those reads below this subtile's MFMAs
-          __builtin_amdgcn_sched_barrier(0);
           const u32x4_t* b = kc == 0 ? b0 : b1;
           if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {   // wave-uniform: skip padding subtiles
 #pragma unroll
