@@ -31,11 +31,29 @@ def _expert(Wg, Wu, Wd, x):
     return _matvec(Wd, h)
 
 
-def moe_dense_bruteforce(x, w_r, experts, k, cap=-1, b_r=None, renormalize=True, shared=None):
+def _select(score, k, allowed):
+    """k rounds of 'best remaining allowed expert', lower index on ties."""
+    chosen = []
+    for _ in range(k):
+        best = -1
+        for e in range(len(score)):
+            if e in chosen or not allowed[e]:
+                continue
+            if best < 0 or score[e] > score[best]:
+                best = e
+        chosen.append(best)
+    return chosen
+
+
+def moe_dense_bruteforce(x, w_r, experts, k, cap=-1, b_r=None, renormalize=True, shared=None,
+                         scoring="softmax", n_group=1, topk_group=1):
     """Returns (y, idx, gates) as nested lists.
 
     x [T][d]; w_r [E][d]; experts[e] = (Wg [d_e][d], Wu [d_e][d], Wd [d][d_e]);
-    b_r [E] or None.  cap < 0: unlimited.
+    b_r [E] or None.  cap < 0: unlimited.  scoring "sigmoid": independent sigmoid
+    affinities, b_r used only to choose, gates from the affinities; n_group > 1: only the
+    topk_group groups (consecutive blocks of E / n_group experts) with the highest best
+    member may be chosen.
     """
     T = len(x)
     E = len(w_r)
@@ -43,21 +61,22 @@ def moe_dense_bruteforce(x, w_r, experts, k, cap=-1, b_r=None, renormalize=True,
     ys, idxs, gs = [], [], []
     seen = [0] * E
     for t in range(T):
-        logits = [sum(w_r[e][i] * x[t][i] for i in range(d)) + (b_r[e] if b_r is not None else 0.0)
-                  for e in range(E)]
-        mx = max(logits)
-        ex = [math.exp(v - mx) for v in logits]
-        s = sum(ex)
-        p = [v / s for v in ex]
-        chosen = []
-        for _ in range(k):                        # selection, lowest index on ties
-            best = -1
-            for e in range(E):
-                if e in chosen:
-                    continue
-                if best < 0 or p[e] > p[best]:
-                    best = e
-            chosen.append(best)
+        raw = [sum(w_r[e][i] * x[t][i] for i in range(d)) for e in range(E)]
+        if scoring == "softmax":
+            logits = [raw[e] + (b_r[e] if b_r is not None else 0.0) for e in range(E)]
+            mx = max(logits)
+            ex = [math.exp(v - mx) for v in logits]
+            s = sum(ex)
+            p = [v / s for v in ex]
+            sel = p
+        else:
+            p = [1.0 / (1.0 + math.exp(-v)) for v in raw]
+            sel = [p[e] + (b_r[e] if b_r is not None else 0.0) for e in range(E)]
+        gsz = E // n_group
+        best_in = [max(sel[g * gsz:(g + 1) * gsz]) for g in range(n_group)]
+        groups = _select(best_in, topk_group, [True] * n_group)
+        allowed = [(e // gsz) in groups for e in range(E)]
+        chosen = _select(sel, k, allowed)
         if renormalize:
             z = sum(p[e] for e in chosen)
             g_sel = [p[e] / z for e in chosen]

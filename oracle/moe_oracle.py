@@ -221,18 +221,84 @@ class Result:
     near_tie: np.ndarray   # token indices
 
 
-def route(x, w_r, k: int, b_r=None, renormalize: bool = True, idx=None):
-    """Router half of the layer: logits, p, idx, gates (idx may be forced)."""
-    r = router_logits(x, w_r, b_r)
-    p = softmax(r)
+# --------------------------------------------------------------------------- DeepSeek-V3 style router
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Per-expert affinity 1 / (1 + e^{-z})."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def group_limited_top_k(score: np.ndarray, k: int, n_group: int, topk_group: int) -> np.ndarray:
+    """Top-k of `score` among the experts of each token's topk_group best groups.
+
+    The E experts are cut into n_group consecutive groups of E / n_group.  A group's
+    score is the highest expert score in it (reading: the pages say only that a token is
+    limited to 4 of its 8 groups -- jacopoparretti.dev, "Smaller experts, more of them").
+    Groups and experts are ranked by score, the lower index winning a tie.
+    """
+    T, E = score.shape
+    gs = E // n_group
+    gscore = score.reshape(T, n_group, gs).max(axis=2)
+    gorder = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, gorder, True, axis=1)
+    masked = np.where(np.repeat(allowed, gs, axis=1), score, -np.inf)
+    return top_k(masked, k)
+
+
+def near_ties_grouped(score: np.ndarray, k: int, n_group: int, topk_group: int,
+                      threshold: float = NEAR_TIE) -> np.ndarray:
+    """Tokens whose group choice or expert choice is decided by a gap < threshold."""
+    T, E = score.shape
+    gs = E // n_group
+    out = np.zeros(T, dtype=bool)
+    if topk_group < n_group:
+        gscore = -np.sort(-score.reshape(T, n_group, gs).max(axis=2), axis=1)
+        out |= gscore[:, topk_group - 1] - gscore[:, topk_group] < threshold
+    gscore = score.reshape(T, n_group, gs).max(axis=2)
+    gorder = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, gorder, True, axis=1)
+    masked = np.where(np.repeat(allowed, gs, axis=1), score, -np.inf)
+    if k < topk_group * gs:
+        srt = -np.sort(-masked, axis=1)
+        out |= srt[:, k - 1] - srt[:, k] < threshold
+    return np.nonzero(out)[0]
+
+
+def route(x, w_r, k: int, b_r=None, renormalize: bool = True, idx=None, scoring: str = "softmax",
+          n_group: int = 1, topk_group: int = 1):
+    """Router half of the layer: (logits, p, idx, gates, near-tie tokens); idx may be forced.
+
+    scoring="softmax": p = softmax(x W_r + b) and the top-k of p (b is part of the logits).
+    scoring="sigmoid": the DeepSeek-V3 rule -- an independent sigmoid affinity s per expert,
+    the bias b added to s only to pick the experts, gates from s of the chosen ones
+    (AI Engineering Illustrated, "The router is small but it decides everything" and "Fix 2
+    nudges a bias instead"; jacopoparretti.dev, "Experts and a router" and "A bias").  Here
+    p is the affinity s, which the statistics average as P.
+    n_group > 1 limits each token to its topk_group best expert groups.
+    """
+    if scoring == "softmax":
+        r = router_logits(x, w_r, b_r)
+        p = softmax(r)
+        sel = p
+    elif scoring == "sigmoid":
+        r = router_logits(x, w_r, None)
+        p = sigmoid(r)
+        sel = p if b_r is None else p + np.asarray(b_r, np.float64)[None, :]
+    else:
+        raise ValueError(scoring)
     if idx is None:
-        idx = top_k(p, k)
+        idx = top_k(sel, k) if n_group == 1 else group_limited_top_k(sel, k, n_group, topk_group)
     g = gates(p, idx, renormalize)
-    return r, p, np.asarray(idx, np.int32), g
+    nt = near_ties(sel, k) if n_group == 1 else near_ties_grouped(sel, k, n_group, topk_group)
+    return r, p, np.asarray(idx, np.int32), g, nt
 
 
 def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: bool = True,
-                shared=None, idx=None) -> Result:
+                shared=None, idx=None, scoring: str = "softmax", n_group: int = 1,
+                topk_group: int = 1) -> Result:
     """The whole layer.
 
     experts: sequence (or any object with ``__getitem__`` and ``__len__``) whose
@@ -241,11 +307,12 @@ def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: b
     of the readable PyTorch layer (Zero to Frontier, "In PyTorch").
     shared: (W_g, W_u, W_d) of an always-on expert added with weight 1, or None.
     idx: forced routing (int [T, k]); when given, gates are computed for it.
+    scoring, n_group, topk_group: router variant (see ``route``).
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
     E = len(experts)
-    r, p, idx, g = route(x, w_r, k, b_r, renormalize, idx)
+    r, p, idx, g, nt = route(x, w_r, k, b_r, renormalize, idx, scoring, n_group, topk_group)
     counts, f, P, aux = load_balance_stats(p, idx, E)
     disp = dispatch(idx, E, cap)
     R_kept = int(disp.offsets[-1])
@@ -265,7 +332,7 @@ def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: b
     if shared is not None:
         y += swiglu_ffn(x, *shared)
     return Result(y=y, logits=r, p=p, idx=idx, gate=g, counts=counts, f=f, P=P, aux=aux,
-                  disp=disp, near_tie=near_ties(p, k))
+                  disp=disp, near_tie=nt)
 
 
 def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared=None) -> np.ndarray:

@@ -68,7 +68,7 @@ def pin_router_worked_examples():
             for e, v in ex["top_logits"].items():
                 logits[int(e)] = v
         x, w_r = _logit_inputs(logits)
-        r, p, idx, g = mo.route(x, w_r, ex["k"])
+        r, p, idx, g = mo.route(x, w_r, ex["k"])[:4]
         assert list(idx[0]) == ex["experts"], (ex["source"], idx[0])
         tol = 0.5 * 10 ** (-ex["decimals"])
         assert np.allclose(g[0], ex["gates"], atol=tol + 1e-12), (ex["source"], g[0])
@@ -191,7 +191,7 @@ def pin_dense_swiglu_special_case():
 def pin_gates_sum_to_one():
     x, w_r, experts, b_r, _ = _tiny_layer(3, T=40, E=7, bias=True)
     for k in (1, 2, 3, 7):
-        _, p, idx, g = mo.route(x, w_r, k, b_r)
+        _, p, idx, g = mo.route(x, w_r, k, b_r)[:4]
         assert np.allclose(g.sum(axis=1), 1.0, atol=1e-14)
         assert np.all(np.diff(g, axis=1) <= 1e-15)       # slots in descending gate order
         # chosen experts are the k most probable
@@ -208,14 +208,14 @@ def pin_tie_break():
     x = g.standard_normal((T, d))
     w_r = np.zeros((E, d))
     for k in (1, 2, 4):
-        _, p, idx, gt = mo.route(x, w_r, k)
+        _, p, idx, gt = mo.route(x, w_r, k)[:4]
         assert np.all(idx == np.arange(k)[None, :])
         assert np.allclose(gt, 1.0 / k, atol=1e-15)
         counts, f, P, aux = mo.load_balance_stats(p, idx, E)
         assert np.allclose(P, 1.0 / E, atol=1e-15)
     # a tie between two non-top experts also goes to the lower index
     x1, w1 = _logit_inputs([0.5, 1.0, 0.5, 0.5, 2.0])
-    _, _, idx, _ = mo.route(x1, w1, 3)
+    _, _, idx, _ = mo.route(x1, w1, 3)[:4]
     assert list(idx[0]) == [4, 1, 0]
 
 
@@ -228,7 +228,7 @@ def pin_aux_balanced():
         x[t, t % E] = 1.0
     w_r = np.zeros((E, d))
     w_r[:, :E] = c * np.eye(E)
-    _, p, idx, _ = mo.route(x, w_r, 1)
+    _, p, idx, _ = mo.route(x, w_r, 1)[:4]
     counts, f, P, aux = mo.load_balance_stats(p, idx, E)
     assert np.all(counts == m)
     assert np.allclose(f, 1.0 / E, atol=1e-15) and np.allclose(P, 1.0 / E, atol=1e-15)
@@ -236,27 +236,27 @@ def pin_aux_balanced():
     # unbalanced routing has aux > 1: everything to expert 0
     x0 = np.zeros((T, d))
     x0[:, 0] = 1.0
-    _, p0, idx0, _ = mo.route(x0, w_r, 1)
+    _, p0, idx0, _ = mo.route(x0, w_r, 1)[:4]
     assert mo.load_balance_stats(p0, idx0, E)[3] > 1.5
     # f counts all k choices: sums to 1 at any k, and is 1/E when k = E
     x2, w2, _, _, _ = _tiny_layer(5, T=30, E=6)
-    _, pE, iE, _ = mo.route(x2, w2, 6)
+    _, pE, iE, _ = mo.route(x2, w2, 6)[:4]
     assert np.allclose(mo.load_balance_stats(pE, iE, 6)[1], 1.0 / 6, atol=1e-15)
     for k in (1, 2, 3):
-        _, p2, i2, _ = mo.route(x2, w2, k)
+        _, p2, i2, _ = mo.route(x2, w2, k)[:4]
         assert abs(mo.load_balance_stats(p2, i2, 6)[1].sum() - 1.0) < 1e-14
         assert np.allclose(mo.load_balance_stats(p2, i2, 6)[2], p2.mean(axis=0))
 
 
 def pin_near_ties():
     x, w_r = _logit_inputs([1.0, 1.0 + 5e-7, 0.0, 1.0 + 1e-5])
-    _, p, _, _ = mo.route(x, w_r, 2)
+    _, p, _, _ = mo.route(x, w_r, 2)[:4]
     # p is about 0.3 for the three near-equal logits: the 2nd/3rd gap (experts 1
     # and 0) is about 1.5e-7 < 1e-6, the 1st/2nd gap about 2.8e-6 > 1e-6
     assert list(mo.near_ties(p, 2)) == [0]
     assert list(mo.near_ties(p, 1)) == []
     x2, w2 = _logit_inputs([3.0, 1.0, 0.0])
-    _, p2, _, _ = mo.route(x2, w2, 1)
+    _, p2, _, _ = mo.route(x2, w2, 1)[:4]
     assert list(mo.near_ties(p2, 1)) == [] and list(mo.near_ties(p2, 3)) == []
 
 
@@ -358,6 +358,73 @@ def pin_per_token_path():
 def pin_rel_err():
     a = np.array([[3.0, -4.0]])
     assert abs(mo.rel_err(a + np.array([[0.0, 0.1]]), a) - 0.1 / math.sqrt(12.5)) < 1e-15
+
+
+
+
+
+# --------------------------------------------------------------------------- DeepSeek-V3 style router
+
+def pin_sigmoid_selects_like_softmax():
+    """sigmoid and softmax are both increasing in the logit, so without a bias and group
+    limit they choose the same experts in the same order; only the gate values differ."""
+    g = _rng(21)
+    x, w_r = g.standard_normal((40, 9)), g.standard_normal((16, 9))
+    for k in (1, 3, 8):
+        i_soft = mo.route(x, w_r, k)[2]
+        r, s, i_sig, gt, _ = mo.route(x, w_r, k, scoring="sigmoid")
+        assert np.array_equal(i_soft, i_sig)
+        sel = 1.0 / (1.0 + np.exp(-np.take_along_axis(r, i_sig.astype(np.int64), axis=1)))
+        assert np.allclose(gt, sel / sel.sum(axis=1, keepdims=True), rtol=1e-14, atol=0)
+        assert np.allclose(gt.sum(axis=1), 1.0, atol=1e-14)
+        raw = mo.route(x, w_r, k, scoring="sigmoid", renormalize=False)[3]
+        assert np.allclose(raw, sel, rtol=1e-14, atol=0)
+
+
+def pin_selection_bias_only():
+    """A bias moves the choice but never enters the gate values."""
+    x, w_r = _logit_inputs([1.0, 0.5, -0.5, 0.2])
+    b = np.array([0.0, 0.0, 10.0, 0.0])
+    r, s, idx, gt, _ = mo.route(x, w_r, 2, b_r=b, scoring="sigmoid")
+    assert list(idx[0]) == [2, 0]
+    s2, s0 = 1 / (1 + math.exp(0.5)), 1 / (1 + math.exp(-1.0))
+    assert abs(gt[0, 0] - s2 / (s2 + s0)) < 1e-15 and abs(gt[0, 1] - s0 / (s2 + s0)) < 1e-15
+    # P averages the affinities, not the biased scores
+    assert np.allclose(s[0], 1 / (1 + np.exp(-np.array([1.0, 0.5, -0.5, 0.2]))), rtol=1e-15)
+
+
+def pin_group_limit():
+    """Group limit: a worked case, and the two limits where it changes nothing."""
+    # 8 experts in 4 groups of 2; only the best group may be used
+    x, w_r = _logit_inputs([3.0, -2.0, 2.5, 2.4, 0.0, 0.1, -1.0, -3.0])
+    for scoring in ("softmax", "sigmoid"):
+        idx = mo.route(x, w_r, 2, scoring=scoring, n_group=4, topk_group=1)[2]
+        assert list(idx[0]) == [0, 1], (scoring, idx)      # expert 2 (2.5) is in a dropped group
+        idx = mo.route(x, w_r, 3, scoring=scoring, n_group=4, topk_group=2)[2]
+        assert list(idx[0]) == [0, 2, 3], (scoring, idx)
+    g = _rng(22)
+    x, w_r, b = g.standard_normal((30, 7)), g.standard_normal((12, 7)), g.standard_normal(12) * 0.1
+    for scoring in ("softmax", "sigmoid"):
+        free = mo.route(x, w_r, 4, b_r=b, scoring=scoring)[2]
+        assert np.array_equal(mo.route(x, w_r, 4, b_r=b, scoring=scoring, n_group=3, topk_group=3)[2], free)
+        assert np.array_equal(mo.route(x, w_r, 4, b_r=b, scoring=scoring, n_group=12, topk_group=4)[2], free)
+
+
+def pin_grouped_bruteforce():
+    """Sigmoid scoring, selection bias and group limit against the pure-Python brute force."""
+    for seed, T, d, de, E, k, ng, tg, cap in [(31, 6, 5, 3, 8, 2, 4, 2, -1), (32, 7, 4, 4, 6, 3, 3, 2, 3),
+                                              (33, 5, 6, 2, 8, 4, 2, 1, -1)]:
+        x, w_r, experts, b_r, sh = _tiny_layer(seed, T=T, d=d, d_e=de, E=E, bias=True, shared=(seed == 32))
+        b_r = b_r * 0.2
+        res = mo.moe_forward(x, w_r, experts, k, cap, b_r, True, sh, scoring="sigmoid", n_group=ng,
+                             topk_group=tg)
+        yb, ib, gb = bf.moe_dense_bruteforce(x.tolist(), w_r.tolist(),
+                                             [tuple(m.tolist() for m in ex) for ex in experts], k, cap,
+                                             b_r.tolist(), True, None if sh is None else
+                                             tuple(m.tolist() for m in sh), "sigmoid", ng, tg)
+        assert np.array_equal(res.idx, np.array(ib))
+        assert np.allclose(res.gate, np.array(gb), rtol=0, atol=1e-14)
+        assert np.allclose(res.y, np.array(yb), rtol=1e-12, atol=1e-12)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

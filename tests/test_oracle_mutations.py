@@ -13,7 +13,7 @@ from oracle import moe_oracle as mo
 
 _orig = {name: getattr(mo, name) for name in
          ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
-          "capacity", "dispatch", "near_ties"]}
+          "capacity", "dispatch", "near_ties", "sigmoid", "group_limited_top_k", "route"]}
 
 
 def _softmax_no_shift(r):
@@ -110,6 +110,40 @@ def _near_ties_off_by_one(p, k, threshold=mo.NEAR_TIE):
     return _orig["near_ties"](p, k + 1 if k + 1 < p.shape[1] else k, threshold)
 
 
+def _sigmoid_sign(z):
+    return 1.0 / (1.0 + np.exp(z))
+
+
+def _group_score_sum(score, k, n_group, topk_group):
+    T, E = score.shape
+    gs = E // n_group
+    gscore = score.reshape(T, n_group, gs).sum(axis=2)
+    gorder = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, gorder, True, axis=1)
+    return mo.top_k(np.where(np.repeat(allowed, gs, axis=1), score, -np.inf), k)
+
+
+def _group_ignored(score, k, n_group, topk_group):
+    return mo.top_k(score, k)
+
+
+def _group_interleaved(score, k, n_group, topk_group):
+    T, E = score.shape
+    perm = np.argsort(np.arange(E) % n_group, kind="stable")        # experts of group g: e % n_group == g
+    idx = _orig["group_limited_top_k"](score[:, perm], k, n_group, topk_group)
+    return perm[idx].astype(np.int32)
+
+
+def _route_bias_in_gates(x, w_r, k, b_r=None, renormalize=True, idx=None, scoring="softmax", n_group=1,
+                         topk_group=1):
+    r, p, idx, g, nt = _orig["route"](x, w_r, k, b_r, renormalize, idx, scoring, n_group, topk_group)
+    if scoring == "sigmoid" and b_r is not None:
+        sel = np.take_along_axis(p + np.asarray(b_r)[None, :], idx.astype(np.int64), axis=1)
+        g = sel / sel.sum(axis=1, keepdims=True) if renormalize else sel
+    return r, p, idx, g, nt
+
+
 MUTANTS = [
     ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
     ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
@@ -121,6 +155,9 @@ MUTANTS = [
     ("capacity", _capacity_no_k), ("capacity", _capacity_ceil),
     ("dispatch", _dispatch_keep_last), ("dispatch", _dispatch_no_cap),
     ("near_ties", _near_ties_off_by_one),
+    ("sigmoid", _sigmoid_sign), ("group_limited_top_k", _group_score_sum),
+    ("group_limited_top_k", _group_ignored), ("group_limited_top_k", _group_interleaved),
+    ("route", _route_bias_in_gates),
 ]
 
 
