@@ -135,7 +135,8 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
     t_up = time.time() - t0
     cap = -1 if w.capacity_factor is None else moe.moe_capacity(w.T, w.k, w.E, w.capacity_factor)
     shape = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
-                           d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32)
+                           d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32,
+                           scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group, topk_group=w.topk_group)
     out = moe.alloc_forward(shape)
     ev = HipEvents()
     nst = moe._lib.MOE_NUM_STAGES

@@ -33,7 +33,10 @@
  *
  * Supported shapes (else MOE_ERR_UNSUPPORTED or MOE_ERR_SHAPE):
  *   T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 16); d, d_e, d_e_shared multiples of 128;
- *   d_e_shared >= 0 (0 = no shared expert); T*k < 2^31; dtype in {MOE_F32, MOE_BF16}.
+ *   d_e_shared >= 0 (0 = no shared expert); T*k < 2^31; dtype in {MOE_F32, MOE_BF16};
+ *   scoring in {MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID}; 1 <= n_group <= 64 dividing E;
+ *   1 <= topk_group <= n_group; k <= topk_group * E / n_group; T*d*elem_size < 2^32 for
+ *   moe_forward (its gather uses 32-bit byte offsets).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -66,7 +69,23 @@ typedef struct {
   int32_t renormalize; /* 1: gates renormalised over the k chosen; 0: raw softmax p */
   int32_t d_e_shared;  /* hidden width of the always-on shared expert; 0 = none */
   int32_t dtype;       /* moe_dtype of x and all weights */
+  int32_t scoring;     /* moe_scoring: how router logits become scores (see below) */
+  int32_t n_group;     /* expert groups (consecutive blocks of E / n_group); 1 = no group limit */
+  int32_t topk_group;  /* groups a token may use (1 <= topk_group <= n_group; 1 when n_group = 1) */
 } moe_shape;
+
+/* Router scoring.
+ * MOE_SCORE_SOFTMAX: p = softmax(r + b) over all E; the k largest p are chosen; gates are p
+ *   renormalised over the k (or raw p).  b, if given, is part of the logits.
+ * MOE_SCORE_SIGMOID: the DeepSeek-V3 rule (AI Engineering Illustrated, "The router is small but
+ *   it decides everything" and "Fix 2 nudges a bias instead"; jacopoparretti.dev, "Experts and a
+ *   router" and "A bias"): an independent affinity s = sigmoid(r) per expert; b is added to s
+ *   only to choose the k experts; gates are the chosen s renormalised over the k (or raw s).
+ *   P averages s.
+ * Group limit (both scorings; jacopoparretti.dev, "Smaller experts, more of them"): with
+ * n_group > 1 a token may only use experts of its topk_group best groups, a group's score being
+ * its best member's selection score; ties go to the lower group index. */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
 
 /* ---------------------------------------------------------------- host-only helpers
  * No device access; usable on a machine without a GPU. */
@@ -86,16 +105,18 @@ const char *moe_status_str(moe_status status);
 
 /* ---------------------------------------------------------------- device calls */
 
-/* Router: logits, softmax, top-k, gates and the Switch load-balance statistics
- * (kevinluzbetak.com page, load-balancing fixes and the layer's auxiliary-loss code).
+/* Router: logits, scores (softmax or sigmoid, see moe_scoring), top-k (group-limited when
+ * n_group > 1), gates and the Switch load-balance statistics (kevinluzbetak.com page,
+ * load-balancing fixes and the layer's auxiliary-loss code).
  *   x      [T, d]        dtype     token rows
  *   w_r    [E, d]        dtype     router weight
- *   b_r    [E]           fp32      per-expert logit bias, or NULL
+ *   b_r    [E]           fp32      per-expert bias (logit bias for softmax, selection-only bias
+ *                                  for sigmoid), or NULL
  *   idx    [T, k]        int32     out: chosen experts, descending gate; idx[:,0] = top-1
  *   gate   [T, k]        fp32      out: gates
  *   counts [E]           int32     out: assignments per expert over all k choices, before capacity
  *   f      [E]           fp32      out: counts / (T*k)      (0 when T = 0)
- *   P      [E]           fp32      out: mean over tokens of p (0 when T = 0)
+ *   P      [E]           fp32      out: mean over tokens of p (softmax) or s (sigmoid); 0 if T = 0
  *   aux    [1]           fp32      out: E * sum_e f_e P_e (no loss weight applied)
  * Logits, softmax and selection are fp32; bf16 inputs are multiplied exactly and summed
  * in fp32. */

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_NUM_STAGES = 8
 STAGE_NAMES = ["router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
@@ -21,7 +22,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 class MoeShape(C.Structure):
     _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("d_e", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("capacity", C.c_int32), ("renormalize", C.c_int32), ("d_e_shared", C.c_int32),
-                ("dtype", C.c_int32)]
+                ("dtype", C.c_int32), ("scoring", C.c_int32), ("n_group", C.c_int32), ("topk_group", C.c_int32)]
 
 
 # every symbol include/moe.h declares, with its argument and result types

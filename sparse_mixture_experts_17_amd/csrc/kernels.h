@@ -13,11 +13,12 @@ constexpr int kRouteTokens = 16;
 
 inline int route_blocks(int T) { return (T + kRouteTokens - 1) / kRouteTokens; }
 
-// Router: fp32 logits via MFMA, softmax, top-k (lowest index on ties), gates,
-// per-block partial sums of p and per-block expert histograms.
+// Router: fp32 logits via MFMA, softmax or sigmoid scores, top-k (optionally limited to the
+// best topk_group of n_group expert groups; lowest index on ties), gates, per-block partial
+// sums of p (or s) and per-block expert histograms.
 hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d,
-                         int E, int k, int renorm, int32_t* idx, float* gate, float* p_part,
-                         int32_t* hist, hipStream_t stream);
+                         int E, int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx,
+                         float* gate, float* p_part, int32_t* hist, hipStream_t stream);
 
 // Per-chunk expert histograms of an index array (dispatch without the router).
 hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t stream);

@@ -54,6 +54,11 @@ moe_status check_shape(const moe_shape* s) {
   if (s->T < 0 || s->d < 1 || s->d_e < 1 || s->E < 1 || s->k < 1 || s->k > s->E || s->d_e_shared < 0)
     return MOE_ERR_SHAPE;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->scoring != MOE_SCORE_SOFTMAX && s->scoring != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (s->n_group < 1 || s->topk_group < 1 || s->topk_group > s->n_group || s->E % s->n_group != 0)
+    return MOE_ERR_SHAPE;
+  if ((long long)s->k > (long long)s->topk_group * (s->E / s->n_group)) return MOE_ERR_SHAPE;
+  if (s->n_group > 64) return MOE_ERR_UNSUPPORTED;
   if (s->E > 1024 || s->k > 16) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 || s->d_e % 128 || s->d_e_shared % 128) return MOE_ERR_UNSUPPORTED;
   if ((long long)s->T * s->k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
@@ -99,8 +104,8 @@ moe_status run_router(const moe_shape& s, const void* x, const void* w_r, const 
   const Layout L = layout(s);
   const int nb = route_blocks(s.T);
   if (s.T > 0)
-    MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, idx, gate,
-                          at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
+    MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, s.scoring, s.n_group,
+                          s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
   MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts,
                       kept, offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm1, at<int32_t>(ws, L.tstart1),
                       bm2, at<int32_t>(ws, L.tstart2), st));
@@ -252,8 +257,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   int32_t* ts2 = at<int32_t>(ws, L.tstart2);
   MOE_MARK(MOE_STAGE_ROUTER);
   if (s.T > 0)
-    MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, idx, gate,
-                          at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
+    MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, s.scoring, s.n_group,
+                          s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
   MOE_MARK(MOE_STAGE_SCAN);
   MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts, kept,
                       offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm, ts1, bm, ts2, st));

@@ -53,15 +53,18 @@ __device__ __forceinline__ void router_tiles(const char* xrow, const char* const
 template <typename T>
 __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
                                                      const float* __restrict__ b_r, int T_, int d, int E,
-                                                     int k, int renorm, int32_t* __restrict__ idx,
+                                                     int k, int renorm, int scoring, int n_group,
+                                                     int topk_group, int32_t* __restrict__ idx,
                                                      float* __restrict__ gate, float* __restrict__ p_part,
                                                      int32_t* __restrict__ hist) {
   constexpr int TB = kRouteTokens;
   const int ksplit = router_ksplit(E);
+  const bool sigm = scoring == 1;
   extern __shared__ float smem[];
   float* logits = smem;                          // [TB][E]  (partials: [ksplit][TB][E])
   float* psum = smem + ksplit * TB * E;          // [4][E]
-  int* lhist = (int*)(psum + 4 * E);             // [E]
+  float* selrow = psum + 4 * E;                  // [4][E]  selection scores of a wave's token
+  int* lhist = (int*)(selrow + 4 * E);           // [E]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -108,12 +111,16 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
   for (int i = tid; i < TB * E; i += 256) {          // fixed-order sum of the K parts, then bias
     float v = logits[i];
     for (int p = 1; p < ksplit; ++p) v += logits[p * TB * E + i];
-    logits[i] = v + (b_r ? b_r[i % E] : 0.f);
+    logits[i] = v + ((b_r && !sigm) ? b_r[i % E] : 0.f);   // softmax: the bias is part of the logit
   }
   __syncthreads();
 
-  // ---- phase 2: softmax and top-k, one token per wave at a time
+  // ---- phase 2: scores and top-k, one token per wave at a time
+  // Lane l holds experts e = 64 q + l.  sel = the selection score (logit for softmax, affinity
+  // plus bias for sigmoid); num = the gate numerator (exp(r - max) or the affinity).
   const int nq = (E + 63) / 64;   // <= 16
+  const int gsz = E / n_group;
+  float* srow = selrow + wave * E;
   float pacc[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) pacc[q] = 0.f;
@@ -129,29 +136,73 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
       v[q] = (q < nq && e < E) ? logits[tl * E + e] : -INFINITY;
       m = fmaxf(m, v[q]);
     }
-    m = wave_max(m);
-    float ex[16];
-    float s = 0.f;
+    float inv = 1.f;
+    float sel[16];
+    if (!sigm) {
+      m = wave_max(m);
+      float s = 0.f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      ex[q] = (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
-      s += ex[q];
+      for (int q = 0; q < 16; ++q) s += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
+      s = wave_sum(s);
+      inv = 1.f / s;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        pacc[q] += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m) * inv;
+        sel[q] = v[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = q * 64 + lane;
+        const bool ok = v[q] != -INFINITY;
+        const float a = ok ? 1.f / (1.f + expf(-v[q])) : 0.f;
+        pacc[q] += a;
+        sel[q] = ok ? a + (b_r ? b_r[e] : 0.f) : -INFINITY;
+      }
     }
-    s = wave_sum(s);
-    const float inv = 1.f / s;
+    if (n_group > 1) {
+      // best selection score per group (lanes < n_group), then the topk_group best groups
 #pragma unroll
-    for (int q = 0; q < 16; ++q) pacc[q] += ex[q] * inv;
+      for (int q = 0; q < 16; ++q) {
+        const int e = q * 64 + lane;
+        if (q < nq && e < E) srow[e] = sel[q];
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      float gbest = -INFINITY;
+      if (lane < n_group)
+        for (int i = 0; i < gsz; ++i) gbest = fmaxf(gbest, srow[lane * gsz + i]);
+      uint64_t allowed = 0;
+      for (int r = 0; r < topk_group; ++r) {
+        float bv = (lane < n_group && !((allowed >> lane) & 1ull)) ? gbest : -INFINITY;
+        int bg = lane < n_group ? lane : 0x7fffffff;
+        if ((allowed >> lane) & 1ull) bg = 0x7fffffff;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          float ov = __shfl_xor(bv, o, kWave);
+          int og = __shfl_xor(bg, o, kWave);
+          if (ov > bv || (ov == bv && og < bg)) { bv = ov; bg = og; }
+        }
+        allowed |= 1ull << bg;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = q * 64 + lane;
+        if (q < nq && e < E && !((allowed >> (e / gsz)) & 1ull)) sel[q] = -INFINITY;
+      }
+      __builtin_amdgcn_wave_barrier();       // srow is reused by this wave's next token
+    }
 
     uint32_t taken = 0;
     int my_e = 0;
-    float my_ex = 0.f, selsum = 0.f;
+    float my_num = 0.f, numsum = 0.f;
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int be = 0x7fffffff;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {     // ascending expert index within the lane: '>' keeps the lowest
         int e = q * 64 + lane;
-        if (q < nq && e < E && !((taken >> q) & 1u) && v[q] > bv) { bv = v[q]; be = e; }
+        if (q < nq && e < E && !((taken >> q) & 1u) && sel[q] > bv) { bv = sel[q]; be = e; }
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
@@ -160,13 +211,14 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
         if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
       }
       if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      float exj = expf(bv - m);
-      selsum += exj;
-      if (lane == j) { my_e = be; my_ex = exj; }
+      const float lg = logits[tl * E + be];                       // the chosen expert's logit
+      const float num = sigm ? 1.f / (1.f + expf(-lg)) : expf(lg - m);
+      numsum += num;
+      if (lane == j) { my_e = be; my_num = num; }
     }
     if (lane < k) {
       idx[(size_t)t * k + lane] = my_e;
-      gate[(size_t)t * k + lane] = renorm ? my_ex / selsum : my_ex * inv;
+      gate[(size_t)t * k + lane] = renorm ? my_num / numsum : (sigm ? my_num : my_num * inv);
       atomicAdd(&lhist[my_e], 1);
     }
   }
@@ -185,20 +237,21 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E,
-                         int k, int renorm, int32_t* idx, float* gate, float* p_part, int32_t* hist,
-                         hipStream_t stream) {
+                         int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx, float* gate,
+                         float* p_part, int32_t* hist, hipStream_t stream) {
   const int nb = route_blocks(T);
-  const size_t lds = (size_t)(router_ksplit(E) * kRouteTokens * E + 4 * E) * sizeof(float) + (size_t)E * sizeof(int);
+  const size_t lds =
+      (size_t)(router_ksplit(E) * kRouteTokens * E + 8 * E) * sizeof(float) + (size_t)E * sizeof(int);
   if (dtype == 1) {
     auto kern = router_kernel<uint16_t>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const uint16_t*)x, (const uint16_t*)w_r, b_r,
-                       T, d, E, k, renorm, idx, gate, p_part, hist);
+                       T, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part, hist);
   } else {
     auto kern = router_kernel<float>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const float*)x, (const float*)w_r, b_r, T, d,
-                       E, k, renorm, idx, gate, p_part, hist);
+                       E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part, hist);
   }
   return hipGetLastError();
 }

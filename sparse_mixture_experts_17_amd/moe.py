@@ -18,8 +18,10 @@ TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 
 def make_shape(T: int, d: int, d_e: int, E: int, k: int, capacity: int = -1, renormalize: bool = True,
-               d_e_shared: int = 0, dtype: int = MOE_BF16) -> MoeShape:
-    return MoeShape(T, d, d_e, E, k, capacity, int(bool(renormalize)), d_e_shared, dtype)
+               d_e_shared: int = 0, dtype: int = MOE_BF16, scoring: int = 0, n_group: int = 1,
+               topk_group: int = 1) -> MoeShape:
+    return MoeShape(T, d, d_e, E, k, capacity, int(bool(renormalize)), d_e_shared, dtype, scoring, n_group,
+                    topk_group)
 
 
 def _ptr(t):

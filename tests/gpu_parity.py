@@ -36,7 +36,13 @@ def log(msg):
 def shape_of(w: wl.Workload, T=None):
     cap = -1 if w.capacity_factor is None else moe.moe_capacity(w.T, w.k, w.E, w.capacity_factor)
     return moe.make_shape(w.T if T is None else T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
-                          d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32), cap
+                          d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32,
+                          scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group,
+                          topk_group=w.topk_group), cap
+
+
+def router_kw(w: wl.Workload) -> dict:
+    return dict(scoring=w.scoring, n_group=w.n_group, topk_group=w.topk_group)
 
 
 def oracle_cap(w: wl.Workload) -> int:
@@ -58,16 +64,16 @@ def experts_f64(inp, es, threads=16):
 def check_routing(w, inp, idx, gate, counts, f, P, aux):
     """Steps 1-2; returns (p, near-tie tokens, flipped tokens)."""
     x = f64(inp.x, w)
-    r, p, own_idx, _ = mo.route(x, f64(inp.w_r, w), w.k, inp.b_r, w.renormalize)
-    nt = mo.near_ties(p, w.k)
+    r, p, own_idx, _, nt = mo.route(x, f64(inp.w_r, w), w.k, inp.b_r, w.renormalize, **router_kw(w))
     mask = np.ones(w.T, bool)
     mask[nt] = False
     assert np.array_equal(idx[mask], own_idx[mask]), \
         f"routing differs on {np.nonzero((idx != own_idx).any(1) & mask)[0][:10]}"
     flipped = [int(t) for t in nt if not np.array_equal(idx[t], own_idx[t])]
     for t in flipped:          # a near tie may go either way, but the choice must be a valid top-k
-        kth = np.sort(p[t])[::-1][w.k - 1]
-        assert len(set(idx[t])) == w.k and np.all(p[t, idx[t]] >= kth - 1e-6)
+        sel = p[t] if w.scoring == "softmax" else p[t] + (0 if inp.b_r is None else inp.b_r)
+        kth = np.sort(sel[own_idx[t]])[0]
+        assert len(set(idx[t])) == w.k and np.all(sel[idx[t]] >= kth - 1e-6)
     g_ref = mo.gates(p, idx, w.renormalize)
     assert np.max(np.abs(gate - g_ref)) <= 1e-5, np.max(np.abs(gate - g_ref))
     c_ref, f_ref, P_ref, aux_ref = mo.load_balance_stats(p, idx, w.E)
@@ -118,7 +124,7 @@ def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
     if sample is None:
         ex = experts_f64(inp, range(w.E))
         ref = mo.moe_forward(x, f64(inp.w_r, w), [ex[e] for e in range(w.E)], w.k, cap, inp.b_r, w.renormalize,
-                             sh, idx=h["idx"])
+                             sh, idx=h["idx"], **router_kw(w))
         y_ref, y = ref.y, h["y"]
     else:
         toks = np.asarray(sample)

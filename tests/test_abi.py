@@ -51,10 +51,20 @@ def _shape(**kw):
     (dict(k=9), 2), (dict(k=0), 2), (dict(T=-1), 2), (dict(E=0), 2), (dict(d_e_shared=-128), 2),
     (dict(E=1025, k=2), 3), (dict(k=17, E=32), 3), (dict(d=500), 3), (dict(d_e=1000), 3),
     (dict(d_e_shared=100), 3), (dict(dtype=7), 3),
+    (dict(scoring=2), 3), (dict(scoring=-1), 3), (dict(n_group=0), 2), (dict(n_group=3), 2),
+    (dict(n_group=4, topk_group=0), 2), (dict(n_group=4, topk_group=5), 2),
+    (dict(n_group=8, topk_group=1, k=2), 2), (dict(E=256, n_group=128, topk_group=2), 3),
 ])
 def test_shape_validation(kw, status):
     n = C.c_size_t()
     assert _lib.lib().moe_workspace_bytes(C.byref(_shape(**kw)), C.byref(n)) == status
+
+
+@pytest.mark.parametrize("kw", [dict(scoring=1), dict(n_group=4, topk_group=2), dict(E=256, k=8, n_group=64,
+                                                                                       topk_group=2, scoring=1)])
+def test_shape_validation_accepts_router_variants(kw):
+    n = C.c_size_t()
+    assert _lib.lib().moe_workspace_bytes(C.byref(_shape(**kw)), C.byref(n)) == 0
 
 
 def test_workspace_bytes_grows_with_shape():

@@ -37,6 +37,16 @@ SMALL = [
     wl.scaled(BASE["mixtral_prefill"], name="dense_E1", T=130, d=256, d_e=256, E=1, k=1),
     wl.scaled(BASE["mixtral_prefill"], name="k_equals_E", T=50, d=128, d_e=128, E=4, k=4),
     wl.scaled(BASE["mixtral_prefill"], name="one_token", T=1, d=128, d_e=256, E=8, k=2),
+    wl.scaled(BASE["deepseek_v3_grouped"], name="sigmoid_grouped", T=300, d=512, d_e=256, E=256, k=8,
+              d_e_shared=256),
+    wl.scaled(BASE["deepseek_v3_grouped"], name="sigmoid_plain", T=200, d=256, d_e=128, E=16, k=3, d_e_shared=0,
+              n_group=1, topk_group=1, router_bias_var=None),
+    wl.scaled(BASE["deepseek_v3_grouped"], name="sigmoid_raw_gates", T=150, d=256, d_e=128, E=32, k=4,
+              d_e_shared=0, n_group=4, topk_group=2, renormalize=False),
+    wl.scaled(BASE["mixtral_prefill"], name="softmax_grouped", T=180, d=256, d_e=128, E=48, k=3, n_group=6,
+              topk_group=2, router_bias_var=0.5),
+    wl.scaled(BASE["mixtral_prefill"], name="grouped_64", T=33, d=128, d_e=128, E=1024, k=16, n_group=64,
+              topk_group=3),
 ]
 
 
@@ -46,7 +56,7 @@ def test_forward_small(w):
     gp.run_forward(w, repeat_check=True)
 
 
-FULL = ["tiny_fp32", "switch_capacity", "mixtral_decode", "mixtral_prefill", "deepseek_v3"]
+FULL = ["tiny_fp32", "switch_capacity", "mixtral_decode", "mixtral_prefill", "deepseek_v3", "deepseek_v3_grouped"]
 
 
 @needs_gpu
@@ -58,7 +68,7 @@ def test_forward_full_size(name):
     if w.T <= 64:
         sample = None
     else:
-        n = 24 if name == "deepseek_v3" else 48
+        n = 24 if name.startswith("deepseek_v3") else 48
         sample = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, n, replace=False)]))
     res = gp.run_forward(w, sample=sample)
     if name == "switch_capacity":
@@ -70,10 +80,12 @@ def _upload_i32(a):
 
 
 @needs_gpu
-def test_split_calls_compose():
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid_grouped"])
+def test_split_calls_compose(scoring):
     """moe_route -> moe_permute -> moe_expert_ffn (+ shared) -> moe_combine equals moe_forward."""
+    extra = {} if scoring == "softmax" else dict(scoring="sigmoid", n_group=4, topk_group=2, router_bias_var=1e-3)
     w = wl.scaled(BASE["deepseek_v3"], name="split", T=211, d=256, d_e=128, E=16, k=3, d_e_shared=256,
-                  capacity_factor=1.1)
+                  capacity_factor=1.1, **extra)
     inp = wl.make_inputs(w)
     dev = upload(inp)
     shape, cap = gp.shape_of(w)

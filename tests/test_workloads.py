@@ -44,6 +44,7 @@ def test_laws():
 
 def test_workload_table():
     names = list(wl.WORKLOADS)
-    assert names == ["tiny_fp32", "switch_capacity", "mixtral_prefill", "mixtral_decode", "deepseek_v3"]
+    assert names[:5] == ["tiny_fp32", "switch_capacity", "mixtral_prefill", "mixtral_decode", "deepseek_v3"]
+    assert wl.get("deepseek_v3_grouped").scoring == "sigmoid"
     assert wl.get("deepseek_v3").d_e_shared == 2048
     assert wl.get("tiny_fp32").dtype == "f32"

@@ -56,6 +56,9 @@ class Workload:
     router_bias_var: float | None = None   # variance of the per-expert logit bias
     d_e_shared: int = 0    # 0: no shared expert
     renormalize: bool = True
+    scoring: str = "softmax"   # "softmax", or "sigmoid" (the bias then only steers selection)
+    n_group: int = 1           # expert groups for group-limited routing
+    topk_group: int = 1        # groups a token may use
     note: str = ""
 
 
@@ -72,6 +75,10 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
     Workload("deepseek_v3", T=4096, d=7168, d_e=2048, E=256, k=8, dtype="bf16",
              d_e_shared=2048,
              note="DeepSeek-V3 fine-grained layer: 256 routed + 1 shared expert"),
+    Workload("deepseek_v3_grouped", T=4096, d=7168, d_e=2048, E=256, k=8, dtype="bf16",
+             d_e_shared=2048, scoring="sigmoid", n_group=8, topk_group=4, router_bias_var=1e-4,
+             note="the DeepSeek-V3 router rule on the same shape: sigmoid affinities, a selection-only "
+                  "per-expert bias (std 0.01), each token limited to 4 of 8 expert groups"),
 ]}
 
 
