@@ -25,13 +25,19 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 
+# Per-source flags.  The large-tile GEMM keeps its accumulators in VGPRs (MFMA VGPR form)
+# and its operands in AGPRs; with the default heuristic its 4 x 48 accumulator tiles go
+# to AGPRs and every MFMA pays copies.
+FILE_FLAGS = {"grouped_gemm_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -1,0 +1,147 @@
+// Pieces shared by the grouped-GEMM kernels (internal to the library).
+#pragma once
+
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+struct GemmArgs {
+  const void* A;            // [rows, K] activations in expert order, or token rows (a_rows)
+  const int32_t* a_rows;    // NULL, or row of A for each expert-ordered row (gather in the load)
+  const void* B0;           // [G, N, K] gate (gated) or down weights
+  const void* B1;           // [G, N, K] up weights (gated only)
+  const int32_t* offsets;   // [G+1] or NULL (dense: one group of dense_rows)
+  const int32_t* tstart;    // [G+1] first m-tile of each group (unused when dense)
+  int G, dense_rows, N, K;
+  void* C;                  // [rows, N]  (dtype for gated, fp32 for down)
+};
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
+constexpr int kBufFlags = 0x00020000;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the LDS ring.  __syncthreads() would also wait for every
+// outstanding global load (its release fence), which would drain the ring; here each
+// wave has already waited for the loads it needs (vmcnt) and for its own LDS reads
+// (lgkmcnt), so a bare s_barrier is enough.  The empty asm statements keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct TileCoord {
+  int g, nt, row0, rows;   // group (expert), n-tile, first row, valid rows (<= BM)
+};
+
+// Tile order: group by group (expert), and inside a group in super-tiles of all its
+// m-tiles x GN n-tiles, GN chosen so one super-tile is about one XCD's worth of
+// concurrent blocks.  Blocks that run together then share their weight tile (same
+// n-tile, all m-tiles of the group: weights leave HBM once) and their activation
+// rows (same m-tile, neighbouring n-tiles) in the XCD's L2.
+__device__ __forceinline__ TileCoord tile_coord(const GemmArgs& args, int L, int ntn, int mt_live, int bpx, int BM) {
+  const int32_t* __restrict__ offsets = args.offsets;
+  const int32_t* __restrict__ tstart = args.tstart;
+  const int mq = L / ntn;                              // any m-tile index in L's group range
+  int g = 0, t0g = 0, t1g = mt_live;
+  if (offsets) {
+    int a = 0, b = args.G - 1;                         // largest g with tstart[g] <= mq
+    while (a < b) {
+      int mid = (a + b + 1) >> 1;
+      if (tstart[mid] <= mq) a = mid; else b = mid - 1;
+    }
+    g = a;
+    t0g = tstart[g];
+    t1g = tstart[g + 1];
+  }
+  const int Me = t1g - t0g;                            // m-tiles of this group
+  const int l = L - t0g * ntn;
+  const int GN = max(1, bpx / Me);
+  const int full = ntn / GN;
+  int m, nt;
+  if (l < full * Me * GN) {
+    const int sb = l / (Me * GN), w = l - sb * (Me * GN);
+    m = w % Me;
+    nt = sb * GN + w / Me;
+  } else {
+    const int w = l - full * Me * GN;
+    m = w % Me;
+    nt = full * GN + w / Me;
+  }
+  TileCoord tc;
+  tc.g = g;
+  tc.nt = nt;
+  if (offsets) {
+    tc.row0 = offsets[g] + m * BM;
+    tc.rows = min(BM, offsets[g + 1] - tc.row0);
+  } else {
+    tc.row0 = m * BM;
+    tc.rows = min(BM, args.dense_rows - tc.row0);
+  }
+  return tc;
+}
+
+// Epilogue: lane holds rows 4*(lane/16)+q of each 16x16 tile, column lane%16.  The gated
+// product stores SiLU(a) * b in the activation type, the plain one fp32.
+template <typename Cfg, typename Acc>
+__device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0, const Acc& acc1, int wm, int wn,
+                                           int lane, int nt, int row0, int rows) {
+  using T = typename Cfg::Elem;
+  const int N = args.N;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm * Cfg::WTM + i * 16 + (lane >> 4) * 4 + q;
+        const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
+        if (r < rows) {
+          const size_t o = (size_t)(row0 + r) * N + col;
+          if constexpr (Cfg::NB == 2) {
+            const float a = acc0[i][j][q], b = acc1[i][j][q];
+            const float h = __fdividef(a, 1.f + __expf(-a)) * b;   // SiLU(a) * b (fast exp/divide: the
+                                                                    // result is rounded to bf16)
+            ((T*)args.C)[o] = ElemOut<T>::from_f32(h);
+          } else {
+            ((float*)args.C)[o] = acc0[i][j][q];
+          }
+        }
+      }
+}
+
+// Persistent grid: #CUs x occupancy blocks (at most one per tile), a multiple of the XCD count.
+template <typename Cfg, void (*KERN)(GemmArgs)>
+static hipError_t launch_kernel(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
+  static const int occ = [] {
+    (void)hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERN, Cfg::NT, Cfg::LDS) != hipSuccess || n < 1) n = 1;
+    return n;
+  }();
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return hipErrorInvalidDevice;
+  const long long max_live = (long long)max_tiles_m * (a.N / Cfg::BN_);
+  long long grid = std::min<long long>(max_live, (long long)cus * occ);
+  grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
+  if (grid < kNumXcd) grid = kNumXcd;
+  hipLaunchKernelGGL(KERN, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS, stream, a);
+  return hipGetLastError();
+}
+
+// bf16 down projection with many rows per expert (4 waves, 192-row tiles; in
+// grouped_gemm_large.hip).
+hipError_t launch_gemm_large_bf16(const GemmArgs& a, int max_tiles_m, hipStream_t stream);
+constexpr int kLargeBf16BlockM = 192;
+
+}  // namespace moe

@@ -27,26 +27,13 @@
 // L = 0 .. live-1 and each XCD (blocks b with b % 8 == x) walks its own contiguous
 // eighth of L, so tiles that share operands run on the same L2 (see the tile order
 // in the kernel).
-#include <algorithm>
-
-#include "common.h"
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace moe {
 
-struct GemmArgs {
-  const void* A;            // [rows, K] activations in expert order, or token rows (a_rows)
-  const int32_t* a_rows;    // NULL, or row of A for each expert-ordered row (gather in the load)
-  const void* B0;           // [G, N, K] gate (gated) or down weights
-  const void* B1;           // [G, N, K] up weights (gated only)
-  const int32_t* offsets;   // [G+1] or NULL (dense: one group of dense_rows)
-  const int32_t* tstart;    // [G+1] first m-tile of each group (unused when dense)
-  int G, dense_rows, N, K;
-  void* C;                  // [rows, N]  (dtype for gated, fp32 for down)
-};
-
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES>
 struct GemmTile {
+  using Elem = T;
   static constexpr int NT = WM * WN * kWave;
   static constexpr int BM_ = BM, BN_ = BN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -58,19 +45,27 @@ struct GemmTile {
   static constexpr int BKE = 8 * EPP;                               // elements of K per stage
   static constexpr int A_IT = (BM * 8 + NT - 1) / NT;
   static constexpr int B_IT = (BROWS * 8 + NT - 1) / NT;
-  static constexpr int STAGE = (BM + BROWS) * ROWB;
-  static constexpr int NSTAGE = STAGES;                            // LDS ring depth
-  static constexpr int LDS = STAGES * STAGE;
+  // LDS: a ring of STAGES activation slots, then a ring of BSTAGES weight slots
+  static constexpr int A_SLOT = BM * ROWB, B_SLOT = BROWS * ROWB;
+  static constexpr int B_BASE = STAGES * A_SLOT;
+  static constexpr int LDS = STAGES * A_SLOT + BSTAGES * B_SLOT;
   static constexpr int NW = WM * WN;
-  // buffer loads per stage issued by the wave with the fewest (the last one); waiting
-  // until at most LPS * n are outstanding leaves n newer stages in flight
-  static constexpr int LPS = [] {
+  // buffer loads per K step issued by the wave with the fewest (the last one); waiting
+  // until at most LPS * n are outstanding leaves n newer steps in flight
+  static constexpr int LPS_A = [] {
     int n = 0;
     for (int it = 0; it < A_IT; ++it) n += (it * NT + (NW - 1) * kWave < BM * 8);
+    return n;
+  }();
+  static constexpr int LPS_B = [] {
+    int n = 0;
     for (int it = 0; it < B_IT; ++it) n += (it * NT + (NW - 1) * kWave < BROWS * 8);
     return n;
   }();
+  static constexpr int LPS = LPS_A + LPS_B;
   static_assert(LPS * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(BSTAGES == STAGES || (STAGES == 2 && BSTAGES == 3), "weight ring: same depth, or 3 with 2");
+  static_assert(LDS <= 160 * 1024, "LDS per workgroup");
   // Skip MFMAs of 16-row subtiles that hold no rows.  Worth a branch only where most
   // subtiles can be empty (the stream and decode tiles); the large tile keeps a
   // branch-free inner loop.
@@ -79,25 +74,6 @@ struct GemmTile {
 };
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
-
-// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
-constexpr int kBufFlags = 0x00020000;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier for the LDS ring.  __syncthreads() would also wait for every
-// outstanding global load (its release fence), which would drain the ring; here each
-// wave has already waited for the loads it needs (vmcnt) and for its own LDS reads
-// (lgkmcnt), so a bare s_barrier is enough.  The empty asm statements keep the
-// compiler from moving memory operations across it.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Wait until the oldest in-flight K step has landed, leaving `ahead` newer ones in flight.
 template <int LPS, int STAGES>
@@ -113,26 +89,34 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   }
 }
 
-// Enqueue one K step of A and B tiles into an LDS stage (asynchronous; completion is
-// tracked by vmcnt).  Wave-uniform branches only.
+// Enqueue one K step of the A (activation) or B (weight) tile into an LDS slot
+// (asynchronous; completion is tracked by vmcnt).  Wave-uniform branches only.
 template <typename Cfg>
-__device__ __forceinline__ void issue_stage(char* As, uint32_t kb, __amdgpu_buffer_rsrc_t rsA,
-                                            __amdgpu_buffer_rsrc_t rsB0, __amdgpu_buffer_rsrc_t rsB1,
-                                            const uint32_t* voffA, const uint32_t* voffB, int wave) {
-  char* Bs = As + Cfg::BM_ * 128;
+__device__ __forceinline__ void issue_a(char* As, uint32_t kb, __amdgpu_buffer_rsrc_t rsA, const uint32_t* voffA,
+                                        int wave) {
+  constexpr int NT = Cfg::NT;
 #pragma unroll
   for (int it = 0; it < Cfg::A_IT; ++it) {
-    const int q0 = it * Cfg::NT + wave * kWave;
-    if (q0 < Cfg::BM_ * 8)
+    const int q0 = it * NT + wave * kWave;
+    if (Cfg::A_IT * NT == Cfg::BM_ * 8 || q0 < Cfg::BM_ * 8)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (__attribute__((address_space(3))) void*)(As + q0 * 16), 16,
                                                voffA[it], kb, 0, 0);
   }
+}
+
+template <typename Cfg>
+__device__ __forceinline__ void issue_b(char* Bs, uint32_t kb, __amdgpu_buffer_rsrc_t rsB0,
+                                        __amdgpu_buffer_rsrc_t rsB1, const uint32_t* voffB, int wave) {
+  constexpr int NT = Cfg::NT, RPI = NT / 8;            // tile rows covered by one load of every wave
 #pragma unroll
   for (int it = 0; it < Cfg::B_IT; ++it) {
-    const int q0 = it * Cfg::NT + wave * kWave;
-    if (q0 < Cfg::BROWS * 8) {
+    const int q0 = it * NT + wave * kWave;
+    if (Cfg::B_IT * NT == Cfg::BROWS * 8 || q0 < Cfg::BROWS * 8) {
       auto* dst = (__attribute__((address_space(3))) void*)(Bs + q0 * 16);
-      if (Cfg::NB == 2 && (q0 >> 3) >= Cfg::BN_)                 // up rows of the gated product
+      // up rows of the gated product: decided per unrolled step when the gate/up split
+      // falls on a step boundary
+      const bool up = Cfg::NB == 2 && (Cfg::BN_ % RPI == 0 ? it * RPI >= Cfg::BN_ : (q0 >> 3) >= Cfg::BN_);
+      if (up)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, voffB[it], kb, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, voffB[it], kb, 0, 0);
@@ -140,21 +124,42 @@ __device__ __forceinline__ void issue_stage(char* As, uint32_t kb, __amdgpu_buff
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES>
+// Per-lane 32-bit buffer offsets of one tile's global -> LDS pieces.  Lane L of a wave's
+// buffer_load_dwordx4 ... lds writes LDS bytes [base + 16 L, base + 16 L + 16), so each
+// lane loads the global piece that belongs at that swizzled LDS position.  Rows past
+// `rows` repeat the last valid row: their results are never stored.
+template <typename Cfg>
+__device__ __forceinline__ void tile_offsets(const GemmArgs& args, int wave, int lane, int row0, int rows,
+                                             size_t row_stride, uint32_t* voffA, uint32_t* voffB) {
+#pragma unroll
+  for (int it = 0; it < Cfg::A_IT; ++it) {
+    const int q = it * Cfg::NT + wave * kWave + lane, r = q >> 3;
+    const int cl = (q & 7) ^ ((r >> 1) & 7);
+    const int rr = min(r, rows - 1);
+    const size_t arow = args.a_rows ? (size_t)args.a_rows[row0 + rr] : (size_t)rr;
+    voffA[it] = (uint32_t)(arow * row_stride + cl * 16);
+  }
+#pragma unroll
+  for (int it = 0; it < Cfg::B_IT; ++it) {
+    const int q = it * Cfg::NT + wave * kWave + lane, r = q >> 3;
+    const int cl = (q & 7) ^ ((r >> 1) & 7);
+    voffB[it] = (uint32_t)((Cfg::NB == 2 && r >= Cfg::BN_ ? r - Cfg::BN_ : r) * row_stride + cl * 16);
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES>;
-  constexpr int NT = Cfg::NT, TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB, BROWS = Cfg::BROWS;
-  constexpr int A_IT = Cfg::A_IT, B_IT = Cfg::B_IT, EPP = Cfg::EPP, BKE = Cfg::BKE, STAGE = Cfg::STAGE;
+  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES>;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB;
+  constexpr int A_IT = Cfg::A_IT, B_IT = Cfg::B_IT, BKE = Cfg::BKE;
   extern __shared__ __align__(16) char lds[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
   const int wm = wave / WN, wn = wave % WN;
-  const int N = args.N, K = args.K, G = args.G;
+  const int N = args.N, K = args.K;
   const int ntn = N / BN;
-  const int32_t* __restrict__ offsets = args.offsets;
-  const int32_t* __restrict__ tstart = args.tstart;
-  const int mt_live = offsets ? tstart[G] : (args.dense_rows + BM - 1) / BM;
+  const int mt_live = args.offsets ? args.tstart[args.G] : (args.dense_rows + BM - 1) / BM;
   const int live = mt_live * ntn;
   const int xcd = blockIdx.x % kNumXcd, j0 = blockIdx.x / kNumXcd, bpx = gridDim.x / kNumXcd;
   const int lo = (int)((long long)live * xcd / kNumXcd);
@@ -163,45 +168,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const size_t row_stride = (size_t)K * sizeof(T);   // bytes per row of A and of every weight
 
   for (int L = lo + j0; L < hi; L += bpx) {
-    // Tile order: group by group (expert), and inside a group in super-tiles of all its
-    // m-tiles x GN n-tiles, GN chosen so one super-tile is about one XCD's worth of
-    // concurrent blocks.  Blocks that run together then share their weight tile (same
-    // n-tile, all m-tiles of the group: weights leave HBM once) and their activation
-    // rows (same m-tile, neighbouring n-tiles) in the XCD's L2.
-    const int mq = L / ntn;                            // any m-tile index in L's group range
-    int g = 0, t0g = 0, t1g = mt_live;
-    if (offsets) {
-      int a = 0, b = G - 1;                            // largest g with tstart[g] <= mq
-      while (a < b) {
-        int mid = (a + b + 1) >> 1;
-        if (tstart[mid] <= mq) a = mid; else b = mid - 1;
-      }
-      g = a;
-      t0g = tstart[g];
-      t1g = tstart[g + 1];
-    }
-    const int Me = t1g - t0g;                          // m-tiles of this group
-    const int l = L - t0g * ntn;
-    const int GN = max(1, bpx / Me);
-    const int full = ntn / GN;
-    int m, nt;
-    if (l < full * Me * GN) {
-      const int sb = l / (Me * GN), w = l - sb * (Me * GN);
-      m = w % Me;
-      nt = sb * GN + w / Me;
-    } else {
-      const int w = l - full * Me * GN;
-      m = w % Me;
-      nt = full * GN + w / Me;
-    }
-    int row0, rows;
-    if (offsets) {
-      row0 = offsets[g] + m * BM;
-      rows = min(BM, offsets[g + 1] - row0);
-    } else {
-      row0 = m * BM;
-      rows = min(BM, args.dense_rows - row0);
-    }
+    const TileCoord tc = tile_coord(args, L, ntn, mt_live, bpx, BM);
+    const int g = tc.g, nt = tc.nt, row0 = tc.row0, rows = tc.rows;
     // Buffer resources over this tile's A rows and B rows; per-lane 32-bit offsets are fixed
     // for the tile and the K step rides in the scalar offset.
     const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride);
@@ -211,28 +179,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, 0x7fffffff, kBufFlags);
     const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, 0x7fffffff, kBufFlags);
 
-    // Global -> LDS without a register round trip (buffer_load_dwordx4 ... lds): lane L of a
-    // wave instruction writes LDS bytes [base + 16 L, base + 16 L + 16), so each lane loads
-    // the global piece that belongs at that swizzled LDS position.  Rows past `rows` repeat
-    // the last valid row: their results are never stored.
     uint32_t voffA[A_IT], voffB[B_IT];
-#pragma unroll
-    for (int it = 0; it < A_IT; ++it) {
-      const int q = it * NT + wave * kWave + lane, r = q >> 3;
-      const int cl = (q & 7) ^ ((r >> 1) & 7);
-      const int rr = min(r, rows - 1);
-      const size_t arow = args.a_rows ? (size_t)args.a_rows[row0 + rr] : (size_t)rr;
-      voffA[it] = (uint32_t)(arow * row_stride + cl * 16);
-    }
-#pragma unroll
-    for (int it = 0; it < B_IT; ++it) {
-      const int q = it * NT + wave * kWave + lane, r = q >> 3;
-      const int cl = (q & 7) ^ ((r >> 1) & 7);
-      voffB[it] = (uint32_t)((GATED && r >= BN ? r - BN : r) * row_stride + cl * 16);
-    }
-    auto issue = [&](int ks, int s) {
-      issue_stage<Cfg>(lds + s * STAGE, (uint32_t)ks * 128, rsA, rsB0, rsB1, voffA, voffB, wave);
-    };
+    tile_offsets<Cfg>(args, wave, lane, row0, rows, row_stride, voffA, voffB);
+    auto a_slot = [&](int s) { return lds + s * Cfg::A_SLOT; };
+    auto b_slot = [&](int s) { return lds + Cfg::B_BASE + s * Cfg::B_SLOT; };
 
     f32x4_t acc0[TM][TN], acc1[TM][TN];
 #pragma unroll
@@ -246,9 +196,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     // One K step from LDS stage s: 2 chunks of 64 bytes.  The A fragment of the next
     // subtile (and at the chunk boundary the next chunk's B fragments) is read before
     // the current subtile's MFMAs are issued, so LDS latency hides behind MFMA work.
-    auto compute = [&](int s) {
-      const char* As = lds + s * STAGE;
-      const char* Bs = As + BM * 128;
+    auto compute = [&](const char* As, const char* Bs) {
       const int ra = wm * Cfg::WTM + (lane & 15);
       const int rb = wn * Cfg::WTN + (lane & 15);
       auto rdA = [&](int i, int kc) {
@@ -285,80 +233,76 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       }
     };
 
-    // STAGES-deep ring: up to STAGES-1 K steps in flight while one is consumed.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // previous tile's stores drained
+    if constexpr (BSTAGES == STAGES) {
+      // STAGES-deep ring: up to STAGES-1 K steps in flight while one is consumed.
 #pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-      if (p < nks) issue(p, p);
-    int slot = 0;
-    for (int ks = 0; ks < nks; ++ks) {
-      wait_stage<Cfg::LPS, STAGES>(min(STAGES - 2, nks - 1 - ks));   // step ks has landed
-      block_barrier();                                  // ... for every wave; slot ks-1 is free
-      if (ks + STAGES - 1 < nks) issue(ks + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
-      compute(slot);
-      slot = slot + 1 == STAGES ? 0 : slot + 1;
+      for (int p = 0; p < STAGES - 1; ++p)
+        if (p < nks) {
+          issue_a<Cfg>(a_slot(p), (uint32_t)p * 128, rsA, voffA, wave);
+          issue_b<Cfg>(b_slot(p), (uint32_t)p * 128, rsB0, rsB1, voffB, wave);
+        }
+      int slot = 0;
+      for (int ks = 0; ks < nks; ++ks) {
+        wait_stage<Cfg::LPS, STAGES>(min(STAGES - 2, nks - 1 - ks));   // step ks has landed
+        block_barrier();                                // ... for every wave; slot ks-1 is free
+        if (ks + STAGES - 1 < nks) {
+          const int fs = slot == 0 ? STAGES - 1 : slot - 1;
+          issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsA, voffA, wave);
+          issue_b<Cfg>(b_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsB0, rsB1, voffB, wave);
+        }
+        compute(a_slot(slot), b_slot(slot));
+        slot = slot + 1 == STAGES ? 0 : slot + 1;
+      }
+    } else {
+      // Weights two K steps ahead, activations one.  Issue order A(0) B(0) B(1), then per
+      // step A(ks+1) B(ks+2): when step ks is consumed the only newer loads than A(ks) are
+      // those of B(ks+1), so waiting until at most LPS_B are outstanding lands A(ks), B(ks).
+      issue_a<Cfg>(a_slot(0), 0, rsA, voffA, wave);
+      issue_b<Cfg>(b_slot(0), 0, rsB0, rsB1, voffB, wave);
+      if (nks > 1) issue_b<Cfg>(b_slot(1), 128, rsB0, rsB1, voffB, wave);
+      int bs = 0;                                       // weight slot of step ks
+      for (int ks = 0; ks < nks; ++ks) {
+        if (ks + 1 < nks) wait_vmcnt<Cfg::LPS_B>();
+        else wait_vmcnt<0>();
+        block_barrier();                                // step ks visible; slots of ks-1 free
+        if (ks + 1 < nks) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * 128, rsA, voffA, wave);
+        if (ks + 2 < nks)
+          issue_b<Cfg>(b_slot(bs == 0 ? 2 : bs - 1), (uint32_t)(ks + 2) * 128, rsB0, rsB1, voffB, wave);
+        compute(a_slot(ks & 1), b_slot(bs));
+        bs = bs == 2 ? 0 : bs + 1;
+      }
     }
     __syncthreads();                                    // LDS free for the next tile
 
-    // epilogue: lane holds rows 4*(lane/16)+q of each 16x16 tile, column lane%16
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = wm * Cfg::WTM + i * 16 + (lane >> 4) * 4 + q;
-          const int col = nt * BN + wn * Cfg::WTN + j * 16 + (lane & 15);
-          if (r < rows) {
-            const size_t o = (size_t)(row0 + r) * N + col;
-            if constexpr (GATED) {
-              const float a = acc0[i][j][q], b = acc1[i][j][q];
-              const float h = a / (1.f + expf(-a)) * b;     // SiLU(a) * b
-              ((T*)args.C)[o] = ElemOut<T>::from_f32(h);
-            } else {
-              ((float*)args.C)[o] = acc0[i][j][q];
-            }
-          }
-        }
+    store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, nt, row0, rows);
   }
 }
 
 // ------------------------------------------------------------------------------ launch
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES>
 static hipError_t launch_cfg(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
-  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES>;
-  auto kern = grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES>;
-  static const int occ = [&] {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Cfg::NT, Cfg::LDS) != hipSuccess || n < 1) n = 1;
-    return n;
-  }();
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return hipErrorInvalidDevice;
-  const long long max_live = (long long)max_tiles_m * (a.N / BN);
-  long long grid = std::min<long long>(max_live, (long long)cus * occ);
-  grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  if (grid < kNumXcd) grid = kNumXcd;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS, stream, a);
-  return hipGetLastError();
+  return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES>,
+                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES>>(a, max_tiles_m, stream);
 }
 
-int gemm_block_m(GemmKind kind) { return kind == kGemmLarge ? 256 : (kind == kGemmStream ? 160 : 16); }
+int gemm_block_m(GemmKind kind, int dtype, bool gated) {
+  if (kind == kGemmLarge) return dtype == 1 && !gated ? kLargeBf16BlockM : 256;
+  return kind == kGemmStream ? 160 : 16;
+}
 
 template <typename T, bool GATED>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
     case kGemmLarge:
-      // 8 waves, 2 LDS stages: LDS bandwidth, not latency, is the limit here
+      if constexpr (sizeof(T) == 2 && !GATED) return launch_gemm_large_bf16(a, max_tiles_m, s);
+      // 8 waves; activations in a 2-deep ring, weights (the HBM stream) in a 3-deep one
       if constexpr (GATED) {
-        return launch_cfg<T, 256, 128, 4, 2, GATED, 2>(a, max_tiles_m, s);   // 64x(64+64) per wave
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3>(a, max_tiles_m, s);   // 64x(64+64) per wave
       } else {
-        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2>(a, max_tiles_m, s);
-        return launch_cfg<T, 256, 128, 4, 2, GATED, 2>(a, max_tiles_m, s);
+        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2, 3>(a, max_tiles_m, s);
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3>(a, max_tiles_m, s);
       }
     case kGemmStream:
       // weight streaming with ~100-250 rows per expert: wide weight tiles, 3-deep ring so

@@ -46,7 +46,8 @@ hipError_t launch_combine(const float* o, const int32_t* row_of, const float* ga
 
 // Grouped GEMM tile configurations (one kernel template; see grouped_gemm.hip).
 enum GemmKind { kGemmLarge = 0, kGemmStream = 1, kGemmDecode = 2 };
-int gemm_block_m(GemmKind kind);
+// Tile rows of the kernel that `kind` selects for the gate/up (gated) or down product.
+int gemm_block_m(GemmKind kind, int dtype, bool gated);
 
 // Gate/up product with the SiLU(a) * b epilogue:  h[r, n] = SiLU(A_r W_g[e]^T) * (A_r W_u[e]^T).
 // A_r is row r of A, or row a_rows[r] of A when a_rows != NULL (the dispatch gather done by

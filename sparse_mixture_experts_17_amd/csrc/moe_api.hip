@@ -199,13 +199,12 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int3
   const long long R = (long long)s.T * s.k;
   if (R == 0) return MOE_OK;
   const GemmKind kind = choose_kind(R, s.E, s.capacity);
-  const int bm = gemm_block_m(kind);
+  const int bm1 = gemm_block_m(kind, s.dtype, true), bm2 = gemm_block_m(kind, s.dtype, false);
   int32_t* ts1 = at<int32_t>(ws, L.tstart1);
   int32_t* ts2 = at<int32_t>(ws, L.tstart2);
-  MOE_HIP(launch_tile_sched(offsets, s.E, bm, ts1, bm, ts2, st));
-  const int tiles = max_m_tiles(R, s.E, -1, bm);
-  return run_ffn(s, s.E, x_perm, offsets, ts1, ts2, kind, tiles, tiles, 0, s.d_e, w_gate, w_up, w_down,
-                 at<void>(ws, L.h), o, st);
+  MOE_HIP(launch_tile_sched(offsets, s.E, bm1, ts1, bm2, ts2, st));
+  return run_ffn(s, s.E, x_perm, offsets, ts1, ts2, kind, max_m_tiles(R, s.E, -1, bm1), max_m_tiles(R, s.E, -1, bm2),
+                 0, s.d_e, w_gate, w_up, w_down, at<void>(ws, L.h), o, st);
 }
 
 moe_status moe_combine(const moe_shape* shape, const float* o, const int32_t* row_of, const float* gate,
@@ -251,7 +250,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
 
   const long long R = (long long)s.T * s.k;
   const GemmKind kind = choose_kind(std::max<long long>(R, 1), s.E, s.capacity);
-  const int bm = gemm_block_m(kind);
+  const int bm1 = gemm_block_m(kind, s.dtype, true), bm2 = gemm_block_m(kind, s.dtype, false);
   const int nb = route_blocks(s.T);
   int32_t* ts1 = at<int32_t>(ws, L.tstart1);
   int32_t* ts2 = at<int32_t>(ws, L.tstart2);
@@ -261,7 +260,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
                           s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
   MOE_MARK(MOE_STAGE_SCAN);
   MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts, kept,
-                      offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm, ts1, bm, ts2, st));
+                      offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm1, ts1, bm2, ts2, st));
   // The forward pass does not materialise x_perm: the permute stage produces the row
   // indices and the gate/up GEMM gathers token rows of x through them as it loads.
   MOE_MARK(MOE_STAGE_PERMUTE);
@@ -269,25 +268,23 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
     MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
                                offsets, row_token, row_of, nullptr, st));
   MOE_MARK(MOE_STAGE_GATE_UP);
-  const int tiles = max_m_tiles(R, s.E, s.capacity, bm);
   if (s.T > 0) {
-    MOE_HIP(launch_gemm_gateup(kind, s.dtype, x, row_token, w_gate, w_up, offsets, ts1, s.E, 0, tiles, s.d_e, s.d,
-                               at<void>(ws, L.h), st));
+    MOE_HIP(launch_gemm_gateup(kind, s.dtype, x, row_token, w_gate, w_up, offsets, ts1, s.E, 0,
+                               max_m_tiles(R, s.E, s.capacity, bm1), s.d_e, s.d, at<void>(ws, L.h), st));
     MOE_MARK(MOE_STAGE_DOWN);
-    MOE_HIP(launch_gemm_down(kind, s.dtype, at<void>(ws, L.h), w_down, offsets, ts2, s.E, 0, tiles, s.d, s.d_e,
-                             at<float>(ws, L.o), st));
+    MOE_HIP(launch_gemm_down(kind, s.dtype, at<void>(ws, L.h), w_down, offsets, ts2, s.E, 0,
+                             max_m_tiles(R, s.E, s.capacity, bm2), s.d, s.d_e, at<float>(ws, L.o), st));
   }
   MOE_MARK(MOE_STAGE_SHARED_GATE_UP);
   const float* shared_out = nullptr;
   if (s.d_e_shared > 0 && s.T > 0) {
     const GemmKind sk = choose_kind(s.T, 1, -1);
-    const int sbm = gemm_block_m(sk);
-    const int stiles = (s.T + sbm - 1) / sbm;
-    MOE_HIP(launch_gemm_gateup(sk, s.dtype, x, nullptr, ws_gate, ws_up, nullptr, nullptr, 1, s.T, stiles,
-                               s.d_e_shared, s.d, at<void>(ws, L.sh_h), st));
+    const int sbm1 = gemm_block_m(sk, s.dtype, true), sbm2 = gemm_block_m(sk, s.dtype, false);
+    MOE_HIP(launch_gemm_gateup(sk, s.dtype, x, nullptr, ws_gate, ws_up, nullptr, nullptr, 1, s.T,
+                               (s.T + sbm1 - 1) / sbm1, s.d_e_shared, s.d, at<void>(ws, L.sh_h), st));
     MOE_MARK(MOE_STAGE_SHARED_DOWN);
-    MOE_HIP(launch_gemm_down(sk, s.dtype, at<void>(ws, L.sh_h), ws_down, nullptr, nullptr, 1, s.T, stiles, s.d,
-                             s.d_e_shared, at<float>(ws, L.sh_o), st));
+    MOE_HIP(launch_gemm_down(sk, s.dtype, at<void>(ws, L.sh_h), ws_down, nullptr, nullptr, 1, s.T,
+                             (s.T + sbm2 - 1) / sbm2, s.d, s.d_e_shared, at<float>(ws, L.sh_o), st));
     shared_out = at<float>(ws, L.sh_o);
   }
   MOE_MARK(MOE_STAGE_COMBINE);

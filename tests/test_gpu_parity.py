@@ -30,6 +30,7 @@ SMALL = [
     wl.scaled(BASE["switch_capacity"], name="capacity_top2", T=500, d=128, d_e=256, E=8, k=2, capacity_factor=1.0),
     wl.scaled(BASE["mixtral_prefill"], name="mixtral_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill"], name="mixtral_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill"], name="large_tiles_d384", T=1600, d=384, d_e=256, E=4, k=2),
     wl.scaled(BASE["mixtral_decode"], name="mixtral_decode_small", T=16, d=512, d_e=1024, E=8, k=2),
     wl.scaled(BASE["deepseek_v3"], name="deepseek_small", T=300, d=512, d_e=256, E=256, k=8, d_e_shared=256),
     wl.scaled(BASE["deepseek_v3"], name="deepseek_shared_large", T=1100, d=256, d_e=128, E=32, k=4, d_e_shared=384),
