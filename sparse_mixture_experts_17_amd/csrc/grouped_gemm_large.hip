@@ -24,6 +24,7 @@ struct LargeTile {
   static constexpr int TM = WTM / 16, TN = WTN / 16, TNB = TN * NB;
   static constexpr int A_SLOT = BM_ * 64, B_SLOT = BROWS * 64, SLOT = A_SLOT + B_SLOT;
   static constexpr int NSLOT = 4, PF = 4;                // ring slots; loads run PF steps ahead
+  static_assert(PF <= NSLOT && PF >= 2, "step s+PF reuses the slot of step s");
   static constexpr int LDS = NSLOT * SLOT;
   static constexpr int A_IT = BM_ * 4 / NT, B_IT = BROWS * 4 / NT;
   static constexpr int LPS = A_IT + B_IT;                // loads per step, every wave
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_large_kernel(GemmArgs args) 
     // step s of the ring; past the last step the loads repeat the last one into a slot
     // nobody reads again, which keeps every step's instruction stream the same
     auto issue = [&](int s) {
-      large_issue<Cfg>(lds + (s & (Cfg::NSLOT - 1)) * Cfg::SLOT, (uint32_t)min(s, nks - 1) * 64, rsA, rsB0, rsB1,
+      large_issue<Cfg>(lds + (s % Cfg::NSLOT) * Cfg::SLOT, (uint32_t)min(s, nks - 1) * 64, rsA, rsB0, rsB1,
                        voffA, voffB, wave);
     };
 
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_large_kernel(GemmArgs args) 
     u32x4_t fa0[TM], fb0[TNB], fa1[TM], fb1[TNB];
 
     auto read = [&](int s, u32x4_t* fa, u32x4_t* fb) {
-      const char* sl = lds + (s & (Cfg::NSLOT - 1)) * Cfg::SLOT;
+      const char* sl = lds + (s % Cfg::NSLOT) * Cfg::SLOT;
 #pragma unroll
       for (int i = 0; i < TM; ++i) fa[i] = *(const u32x4_t*)(sl + offA + i * 16 * 64);
 #pragma unroll
