@@ -10,7 +10,8 @@ stored element type, so the oracle sees the same values the GPU receives.
 
 Modules
   moe_oracle   the layer: router, softmax, top-k, gates, aux statistics,
-               capacity dispatch, SwiGLU experts, combine, near-tie report
+               capacity dispatch, SwiGLU experts, combine, near-tie report,
+               and the FP8 (E4M3) weight decode
   bruteforce   pure-Python evaluation of the dense "every expert, unchosen
                gates zero" form, for tiny inputs
   param_count  parameter and FLOP arithmetic of whole MoE models

@@ -364,6 +364,37 @@ def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared
     return y
 
 
+# --------------------------------------------------------------------------- FP8 expert weights
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Exact value of each one-byte FP8 E4M3 code, float64.
+
+    The pages store expert weights in one byte per parameter (jacopoparretti.dev,
+    "Memory": the DeepSeek-V3 weights ship in FP8; AI Engineering Illustrated, "Trade-offs
+    to weigh": small-batch MoE is bound by reading weights, which quantising attacks)
+    without fixing the encoding.  E4M3 here is the OCP 8-bit float: sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent 0 holds the subnormals m/8 * 2^-6; there
+    are no infinities and S.1111.111 is NaN, so the largest finite value is 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = c >> 7
+    ex = (c >> 3) & 15
+    man = c & 7
+    mag = np.where(ex == 0, (man / 8.0) * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    val = np.where(sign == 1, -mag, mag)
+    return np.where((ex == 15) & (man == 7), np.nan, val)
+
+
+def dequantize_rows(codes, scale) -> np.ndarray:
+    """W[n, :] = scale[n] * e4m3(codes[n, :]): one fp32 scale per output row (channel).
+
+    The pages do not say how FP8 weights are scaled; one scale per output channel is the
+    plainest reading, and a row scale factors out of each output's dot product.
+    """
+    w = e4m3_decode(codes)
+    return w * np.asarray(scale, np.float64).reshape(-1, 1)
+
+
 def rel_err(y, y_ref) -> float:
     """max |y - y_ref| / rms(y_ref): the output tolerance measure."""
     y = np.asarray(y, np.float64)

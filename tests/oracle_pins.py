@@ -427,4 +427,44 @@ def pin_grouped_bruteforce():
         assert np.allclose(res.y, np.array(yb), rtol=1e-12, atol=1e-12)
 
 
+def pin_e4m3_library():
+    """Every one of the 256 E4M3 codes decodes as torch's float8_e4m3fn does (an
+    independent implementation of the same OCP format), NaN in the same places."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = mo.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))   # -0 stays -0
+
+
+def pin_e4m3_fixed_points():
+    """Values the format definition fixes: one, the largest finite value, the smallest
+    normal and subnormal, the largest subnormal, NaN, and order along the codes."""
+    d = mo.e4m3_decode
+    assert d(np.array([0x38]))[0] == 1.0
+    assert d(np.array([0x7E]))[0] == 448.0 and d(np.array([0xFE]))[0] == -448.0
+    assert d(np.array([0x08]))[0] == 2.0 ** -6
+    assert d(np.array([0x01]))[0] == 2.0 ** -9
+    assert d(np.array([0x07]))[0] == 7 * 2.0 ** -9
+    assert d(np.array([0x40]))[0] == 2.0 and d(np.array([0x3C]))[0] == 1.5
+    assert np.isnan(d(np.array([0x7F]))[0]) and np.isnan(d(np.array([0xFF]))[0])
+    pos = d(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)                              # strictly increasing
+    assert np.array_equal(d(np.arange(0x80, 0xFF, dtype=np.uint8)), -pos)
+
+
+def pin_dequantize_rows():
+    """Each row is its decoded codes times that row's scale (non-square, so a scale
+    applied along the wrong axis fails)."""
+    rng = _rng(11)
+    codes = rng.integers(0, 0x7F, size=(3, 5)).astype(np.uint8)
+    scale = np.array([0.5, 2.0, 0.125], np.float32)
+    w = mo.dequantize_rows(codes, scale)
+    for n in range(3):
+        assert np.array_equal(w[n], mo.e4m3_decode(codes[n]) * float(scale[n]))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

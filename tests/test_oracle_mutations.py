@@ -13,7 +13,8 @@ from oracle import moe_oracle as mo
 
 _orig = {name: getattr(mo, name) for name in
          ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
-          "capacity", "dispatch", "near_ties", "sigmoid", "group_limited_top_k", "route"]}
+          "capacity", "dispatch", "near_ties", "sigmoid", "group_limited_top_k", "route", "e4m3_decode",
+          "dequantize_rows"]}
 
 
 def _softmax_no_shift(r):
@@ -144,6 +145,33 @@ def _route_bias_in_gates(x, w_r, k, b_r=None, renormalize=True, idx=None, scorin
     return r, p, idx, g, nt
 
 
+def _e4m3_bias8(codes):
+    return _orig["e4m3_decode"](codes) / 2.0
+
+
+def _e4m3_no_subnormals(codes):
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    v = _orig["e4m3_decode"](codes)
+    ex, man = (c >> 3) & 15, c & 7
+    sub = (ex == 0) & (man > 0)
+    mag = (1.0 + man / 8.0) * 2.0 ** -7
+    return np.where(sub, np.where(c >> 7 == 1, -mag, mag), v)
+
+
+def _e4m3_mantissa_16(codes):
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    v = _orig["e4m3_decode"](codes)
+    ex, man = (c >> 3) & 15, c & 7
+    mag = (1.0 + man / 16.0) * np.exp2(ex - 7.0)
+    return np.where((ex > 0) & ~np.isnan(v), np.where(c >> 7 == 1, -mag, mag), v)
+
+
+def _dequant_columns(codes, scale):
+    w = mo.e4m3_decode(codes)
+    sc = np.resize(np.asarray(scale, np.float64), w.shape[1])
+    return w * sc.reshape(1, -1)
+
+
 MUTANTS = [
     ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
     ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
@@ -158,6 +186,8 @@ MUTANTS = [
     ("sigmoid", _sigmoid_sign), ("group_limited_top_k", _group_score_sum),
     ("group_limited_top_k", _group_ignored), ("group_limited_top_k", _group_interleaved),
     ("route", _route_bias_in_gates),
+    ("e4m3_decode", _e4m3_bias8), ("e4m3_decode", _e4m3_no_subnormals), ("e4m3_decode", _e4m3_mantissa_16),
+    ("dequantize_rows", _dequant_columns),
 ]
 
 
