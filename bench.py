@@ -131,12 +131,14 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
     else:                                    # same experts and router (same streams), new tokens
         import workloads.device as wd
         dev = wd.DeviceInputs(wd._to_dev(inp.x, w.dtype, "cuda"), dev_weights.w_r, dev_weights.b_r,
-                              dev_weights.w_gate, dev_weights.w_up, dev_weights.w_down, dev_weights.shared)
+                              dev_weights.w_gate, dev_weights.w_up, dev_weights.w_down, dev_weights.shared,
+                              dev_weights.scales, dev_weights.shared_scales)
     t_up = time.time() - t0
     cap = -1 if w.capacity_factor is None else moe.moe_capacity(w.T, w.k, w.E, w.capacity_factor)
     shape = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
                            d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32,
-                           scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group, topk_group=w.topk_group)
+                           scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group, topk_group=w.topk_group,
+                           wfmt=moe.MOE_W_FP8_E4M3 if w.weights == "fp8_e4m3" else moe.MOE_W_NATIVE)
     out = moe.alloc_forward(shape)
     ev = HipEvents()
     nst = moe._lib.MOE_NUM_STAGES
@@ -145,7 +147,7 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
 
     def call(events=None):
         moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared, out=out,
-                    stage_events=events)
+                    stage_events=events, scales=dev.scales, shared_scales=dev.shared_scales)
 
     def kernel_events():
         arr = (C.c_void_p * (nst + 1))()
@@ -196,14 +198,16 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
 def layer_work(w, R_kept, touched):
     """Algorithmic FLOPs and bytes of one layer call (per unit figures x units)."""
     s = 2 if w.dtype == "bf16" else 4
+    sw = 1 if w.weights == "fp8_e4m3" else s          # bytes per expert weight (FP8: + 4 per row scale)
     flops_gate_up = 4 * w.d * w.d_e * R_kept
     flops_down = 2 * w.d * w.d_e * R_kept
     flops_router = 2 * w.d * w.E * w.T
     flops_shared = 6 * w.d * w.d_e_shared * w.T
-    bytes_gate_up = touched * 2 * w.d * w.d_e * s + R_kept * w.d * s + R_kept * w.d_e * s
-    bytes_down = touched * w.d * w.d_e * s + R_kept * w.d_e * s + R_kept * w.d * 4
-    bytes_layer = (touched * 3 * w.d * w.d_e * s + w.E * w.d * s + w.T * w.d * s + w.T * w.d * 4 + w.T * w.k * 8
-                   + 3 * w.d * w.d_e_shared * s)
+    rs = 4 if w.weights == "fp8_e4m3" else 0
+    bytes_gate_up = touched * 2 * w.d_e * (w.d * sw + rs) + R_kept * w.d * s + R_kept * w.d_e * s
+    bytes_down = touched * w.d * (w.d_e * sw + rs) + R_kept * w.d_e * s + R_kept * w.d * 4
+    bytes_layer = (touched * 3 * w.d * w.d_e * sw + touched * (2 * w.d_e + w.d) * rs + w.E * w.d * s
+                   + w.T * w.d * s + w.T * w.d * 4 + w.T * w.k * 8 + 3 * w.d * w.d_e_shared * sw)
     return dict(flops_gate_up=flops_gate_up, flops_down=flops_down, flops_layer=flops_gate_up + flops_down +
                 flops_router + flops_shared, bytes_gate_up=bytes_gate_up, bytes_down=bytes_down,
                 bytes_layer=bytes_layer)
@@ -311,6 +315,23 @@ def main():
             "stages_ms": dec["stages"], "experts_touched": dec["touched"], "ms_per_step_unmarked": dec["plain_ms"],
             "roofline": {"kernel": "grouped_gemm gate_up (decode tiles)", "bound": "hbm", "achieved": gb,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
+            "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        }
+    if not a.no_secondary and w.name == "mixtral_prefill":
+        print("[bench] secondary: mixtral_decode_fp8 (FP8 E4M3 expert weights)", file=sys.stderr, flush=True)
+        del info["dev"]
+        torch.cuda.empty_cache()
+        dec = run_gpu("mixtral_decode_fp8", max(a.steps, 20), a.warmup)
+        wd = dec["w"]
+        dwork = layer_work(wd, dec["R_kept"], dec["touched"])
+        dms = dec["total_ms"] / max(a.steps, 20)
+        gb = dwork["bytes_gate_up"] / (dec["kernel_ms"] / 1e3) / 1e9
+        line["secondary_fp8"] = {
+            "workload": wd.name, "value": wd.T / (dms / 1e3), "unit": "tokens/s", "ms_per_step": dms,
+            "stages_ms": dec["stages"], "experts_touched": dec["touched"], "ms_per_step_unmarked": dec["plain_ms"],
+            "roofline": {"kernel": "grouped_gemm gate_up (decode tiles, FP8 weights)", "bound": "hbm",
+                         "achieved": gb, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
                          "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
             "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
         }

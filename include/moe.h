@@ -36,7 +36,8 @@
  *   d_e_shared >= 0 (0 = no shared expert); T*k < 2^31; dtype in {MOE_F32, MOE_BF16};
  *   scoring in {MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID}; 1 <= n_group <= 64 dividing E;
  *   1 <= topk_group <= n_group; k <= topk_group * E / n_group; T*d*elem_size < 2^32 for
- *   moe_forward (its gather uses 32-bit byte offsets).
+ *   moe_forward (its gather uses 32-bit byte offsets); wfmt in {MOE_W_NATIVE, MOE_W_FP8_E4M3},
+ *   FP8 weights only with dtype MOE_BF16.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -72,7 +73,27 @@ typedef struct {
   int32_t scoring;     /* moe_scoring: how router logits become scores (see below) */
   int32_t n_group;     /* expert groups (consecutive blocks of E / n_group); 1 = no group limit */
   int32_t topk_group;  /* groups a token may use (1 <= topk_group <= n_group; 1 when n_group = 1) */
+  int32_t wfmt;        /* moe_wfmt of the expert weights (router weight: always dtype) */
 } moe_shape;
+
+/* Storage of the expert weights (routed and shared).
+ * MOE_W_NATIVE:   weights in the shape's dtype.
+ * MOE_W_FP8_E4M3: one byte per weight, OCP FP8 E4M3 (bias 7, subnormals, no infinities,
+ *   S.1111.111 = NaN; largest finite 448), plus one fp32 scale per output row: the
+ *   weight is scale[row] * e4m3(code).  The pages keep expert weights in one byte per
+ *   parameter (jacopoparretti.dev, "Memory") because small batches are bound by reading
+ *   them (AI Engineering Illustrated, "Trade-offs to weigh").  Products run in bf16 on the
+ *   decoded codes (exact in bf16) with fp32 accumulation; the row scale multiplies each
+ *   output before SiLU (gate/up) or before it is written (down). */
+typedef enum { MOE_W_NATIVE = 0, MOE_W_FP8_E4M3 = 1 } moe_wfmt;
+
+/* Row scales of FP8 expert weights (device pointers, fp32; G = E for routed experts, 1 for
+ * the shared expert). */
+typedef struct {
+  const float *gate;   /* [G, d_e]  scale of each row of W_g */
+  const float *up;     /* [G, d_e]  scale of each row of W_u */
+  const float *down;   /* [G, d]    scale of each row of W_d */
+} moe_wscales;
 
 /* Router scoring.
  * MOE_SCORE_SOFTMAX: p = softmax(r + b) over all E; the k largest p are chosen; gates are p
@@ -144,16 +165,17 @@ moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *idx
  * x_perm go through expert e; offsets[E] <= T*k.
  *   x_perm  [T*k, d]          dtype
  *   offsets [E+1]             int32
- *   w_gate  [E, d_e, d]       dtype
- *   w_up    [E, d_e, d]       dtype
- *   w_down  [E, d, d_e]       dtype
+ *   w_gate  [E, d_e, d]       dtype, or uint8 E4M3 codes (wfmt MOE_W_FP8_E4M3)
+ *   w_up    [E, d_e, d]       same
+ *   w_down  [E, d, d_e]       same
+ *   scales  row scales of the three (required iff wfmt = MOE_W_FP8_E4M3, else ignored)
  *   o       [T*k, d]          fp32      out: rows < offsets[E]; the rest untouched
  * The hidden activation is rounded to dtype between the two products (bf16 RNE for
  * MOE_BF16).  The shared expert is this call with E = 1, k = 1, d_e = d_e_shared and
  * offsets = {0, T}. */
 moe_status moe_expert_ffn(const moe_shape *shape, const void *x_perm, const int32_t *offsets,
-                          const void *w_gate, const void *w_up, const void *w_down, float *o,
-                          void *ws, size_t ws_bytes, void *stream);
+                          const void *w_gate, const void *w_up, const void *w_down,
+                          const moe_wscales *scales, float *o, void *ws, size_t ws_bytes, void *stream);
 
 /* Gate-weighted combine back to token order (the layer's weighted sum,
  * Zero to Frontier "The MoE layer" equation):
@@ -167,6 +189,8 @@ moe_status moe_combine(const moe_shape *shape, const float *o, const int32_t *ro
 /* The whole layer: route -> dispatch -> grouped experts (+ shared expert) -> combine.
  * Arguments as in the split calls; ws_gate/ws_up ([d_e_shared, d]) and ws_down
  * ([d, d_e_shared]) are the shared expert's weights, required iff d_e_shared > 0.
+ * scales / shared_scales: row scales of the routed / shared expert weights, required
+ * (shared_scales iff d_e_shared > 0) when wfmt = MOE_W_FP8_E4M3, else ignored.
  * offsets [E+1], row_token [T*k] and row_of [T, k] are optional outputs (NULL: kept in the
  * workspace).
  * stage_events: NULL, or a host array of MOE_NUM_STAGES + 1 hipEvent_t (created by the
@@ -191,6 +215,7 @@ typedef enum {
 moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_r, const float *b_r,
                        const void *w_gate, const void *w_up, const void *w_down,
                        const void *ws_gate, const void *ws_up, const void *ws_down,
+                       const moe_wscales *scales, const moe_wscales *shared_scales,
                        float *y, int32_t *idx, float *gate, int32_t *counts, int32_t *kept,
                        float *f, float *P, float *aux,
                        int32_t *offsets, int32_t *row_token, int32_t *row_of,

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_W_NATIVE, MOE_W_FP8_E4M3 = 0, 1
 MOE_NUM_STAGES = 8
 STAGE_NAMES = ["router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
@@ -22,7 +23,13 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 class MoeShape(C.Structure):
     _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("d_e", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("capacity", C.c_int32), ("renormalize", C.c_int32), ("d_e_shared", C.c_int32),
-                ("dtype", C.c_int32), ("scoring", C.c_int32), ("n_group", C.c_int32), ("topk_group", C.c_int32)]
+                ("dtype", C.c_int32), ("scoring", C.c_int32), ("n_group", C.c_int32), ("topk_group", C.c_int32),
+                ("wfmt", C.c_int32)]
+
+
+class MoeWScales(C.Structure):
+    """Row scales of FP8 expert weights (device pointers)."""
+    _fields_ = [("gate", C.c_void_p), ("up", C.c_void_p), ("down", C.c_void_p)]
 
 
 # every symbol include/moe.h declares, with its argument and result types
@@ -33,9 +40,11 @@ SIGNATURES = {
     "moe_status_str": (C.c_char_p, [C.c_int]),
     "moe_route": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_permute": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
-    "moe_expert_ffn": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_expert_ffn": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, C.POINTER(MoeWScales), _P, _P,
+                                 C.c_size_t, _P]),
     "moe_combine": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P]),
-    "moe_forward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 20 + [_P, C.c_size_t, _P, _P]),
+    "moe_forward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 9 + [C.POINTER(MoeWScales)] * 2 + [_P] * 11
+                    + [_P, C.c_size_t, _P, _P]),
 }
 
 _lib = None

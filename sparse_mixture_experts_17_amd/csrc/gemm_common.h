@@ -13,6 +13,8 @@ struct GemmArgs {
   const int32_t* a_rows;    // NULL, or row of A for each expert-ordered row (gather in the load)
   const void* B0;           // [G, N, K] gate (gated) or down weights
   const void* B1;           // [G, N, K] up weights (gated only)
+  const float* S0;          // [G, N] row scales of B0 (FP8 weights), else unused
+  const float* S1;          // [G, N] row scales of B1 (FP8 weights, gated), else unused
   const int32_t* offsets;   // [G+1] or NULL (dense: one group of dense_rows)
   const int32_t* tstart;    // [G+1] first m-tile of each group (unused when dense)
   int G, dense_rows, N, K;
@@ -37,6 +39,10 @@ __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// 64-byte LDS rows: 4 pieces of 16 bytes, XOR-swizzled by row pair (conflict-free
+// 16-byte reads of one piece by 16 consecutive rows).
+__device__ __forceinline__ int swz64(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
 
 struct TileCoord {
   int g, nt, row0, rows;   // group (expert), n-tile, first row, valid rows (<= BM)
@@ -93,7 +99,7 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& args, int L, int
 // product stores SiLU(a) * b in the activation type, the plain one fp32.
 template <typename Cfg, typename Acc>
 __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0, const Acc& acc1, int wm, int wn,
-                                           int lane, int nt, int row0, int rows) {
+                                           int lane, int g, int nt, int row0, int rows) {
   using T = typename Cfg::Elem;
   const int N = args.N;
 #pragma unroll
@@ -106,7 +112,16 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
         const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
         if (r < rows) {
           const size_t o = (size_t)(row0 + r) * N + col;
-          if constexpr (Cfg::NB == 2) {
+          if constexpr (Cfg::W8_) {                       // row scales of FP8 weights
+            const size_t sc = (size_t)g * N + col;
+            if constexpr (Cfg::NB == 2) {
+              const float a = acc0[i][j][q] * args.S0[sc], b = acc1[i][j][q] * args.S1[sc];
+              const float h = __fdividef(a, 1.f + __expf(-a)) * b;
+              ((T*)args.C)[o] = ElemOut<T>::from_f32(h);
+            } else {
+              ((float*)args.C)[o] = acc0[i][j][q] * args.S0[sc];
+            }
+          } else if constexpr (Cfg::NB == 2) {
             const float a = acc0[i][j][q], b = acc1[i][j][q];
             const float h = __fdividef(a, 1.f + __expf(-a)) * b;   // SiLU(a) * b (fast exp/divide: the
                                                                     // result is rounded to bf16)

@@ -31,9 +31,11 @@
 
 namespace moe {
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES,
+          bool W8 = false>
 struct GemmTile {
   using Elem = T;
+  static constexpr bool W8_ = W8;                                   // FP8 E4M3 weights, row scales
   static constexpr int NT = WM * WN * kWave;
   static constexpr int BM_ = BM, BN_ = BN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -43,10 +45,12 @@ struct GemmTile {
   static constexpr int ROWB = 128;                                  // bytes of K per row per stage
   static constexpr int EPP = Mfma<T>::kElemsPerPiece;               // elements per 16-byte piece
   static constexpr int BKE = 8 * EPP;                               // elements of K per stage
+  static constexpr int PPR_B = W8 ? 4 : 8;                          // 16-byte weight pieces per row per step
+  static constexpr int ROWB_B = PPR_B * 16;
   static constexpr int A_IT = (BM * 8 + NT - 1) / NT;
-  static constexpr int B_IT = (BROWS * 8 + NT - 1) / NT;
+  static constexpr int B_IT = (BROWS * PPR_B + NT - 1) / NT;
   // LDS: a ring of STAGES activation slots, then a ring of BSTAGES weight slots
-  static constexpr int A_SLOT = BM * ROWB, B_SLOT = BROWS * ROWB;
+  static constexpr int A_SLOT = BM * ROWB, B_SLOT = BROWS * ROWB_B;
   static constexpr int B_BASE = STAGES * A_SLOT;
   static constexpr int LDS = STAGES * A_SLOT + BSTAGES * B_SLOT;
   static constexpr int NW = WM * WN;
@@ -59,7 +63,7 @@ struct GemmTile {
   }();
   static constexpr int LPS_B = [] {
     int n = 0;
-    for (int it = 0; it < B_IT; ++it) n += (it * NT + (NW - 1) * kWave < BROWS * 8);
+    for (int it = 0; it < B_IT; ++it) n += (it * NT + (NW - 1) * kWave < BROWS * PPR_B);
     return n;
   }();
   static constexpr int LPS = LPS_A + LPS_B;
@@ -71,6 +75,7 @@ struct GemmTile {
   // branch-free inner loop.
   static constexpr bool SKIP_ROWS = BM != 256;
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
+  static_assert(!W8 || sizeof(T) == 2, "FP8 weights go with bf16 activations");
 };
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
@@ -107,15 +112,15 @@ __device__ __forceinline__ void issue_a(char* As, uint32_t kb, __amdgpu_buffer_r
 template <typename Cfg>
 __device__ __forceinline__ void issue_b(char* Bs, uint32_t kb, __amdgpu_buffer_rsrc_t rsB0,
                                         __amdgpu_buffer_rsrc_t rsB1, const uint32_t* voffB, int wave) {
-  constexpr int NT = Cfg::NT, RPI = NT / 8;            // tile rows covered by one load of every wave
+  constexpr int NT = Cfg::NT, PPR = Cfg::PPR_B, RPI = NT / PPR;   // rows covered by one load of every wave
 #pragma unroll
   for (int it = 0; it < Cfg::B_IT; ++it) {
     const int q0 = it * NT + wave * kWave;
-    if (Cfg::B_IT * NT == Cfg::BROWS * 8 || q0 < Cfg::BROWS * 8) {
+    if (Cfg::B_IT * NT == Cfg::BROWS * PPR || q0 < Cfg::BROWS * PPR) {
       auto* dst = (__attribute__((address_space(3))) void*)(Bs + q0 * 16);
       // up rows of the gated product: decided per unrolled step when the gate/up split
       // falls on a step boundary
-      const bool up = Cfg::NB == 2 && (Cfg::BN_ % RPI == 0 ? it * RPI >= Cfg::BN_ : (q0 >> 3) >= Cfg::BN_);
+      const bool up = Cfg::NB == 2 && (Cfg::BN_ % RPI == 0 ? it * RPI >= Cfg::BN_ : q0 / PPR >= Cfg::BN_);
       if (up)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, voffB[it], kb, 0, 0);
       else
@@ -130,7 +135,8 @@ __device__ __forceinline__ void issue_b(char* Bs, uint32_t kb, __amdgpu_buffer_r
 // `rows` repeat the last valid row: their results are never stored.
 template <typename Cfg>
 __device__ __forceinline__ void tile_offsets(const GemmArgs& args, int wave, int lane, int row0, int rows,
-                                             size_t row_stride, uint32_t* voffA, uint32_t* voffB) {
+                                             size_t row_stride, size_t row_stride_b, uint32_t* voffA,
+                                             uint32_t* voffB) {
 #pragma unroll
   for (int it = 0; it < Cfg::A_IT; ++it) {
     const int q = it * Cfg::NT + wave * kWave + lane, r = q >> 3;
@@ -141,15 +147,24 @@ __device__ __forceinline__ void tile_offsets(const GemmArgs& args, int wave, int
   }
 #pragma unroll
   for (int it = 0; it < Cfg::B_IT; ++it) {
-    const int q = it * Cfg::NT + wave * kWave + lane, r = q >> 3;
-    const int cl = (q & 7) ^ ((r >> 1) & 7);
-    voffB[it] = (uint32_t)((Cfg::NB == 2 && r >= Cfg::BN_ ? r - Cfg::BN_ : r) * row_stride + cl * 16);
+    const int q = it * Cfg::NT + wave * kWave + lane;
+    const int r = Cfg::W8_ ? q >> 2 : q >> 3;
+    const int cl = Cfg::W8_ ? (q & 3) ^ ((r >> 1) & 3) : (q & 7) ^ ((r >> 1) & 7);
+    voffB[it] = (uint32_t)((Cfg::NB == 2 && r >= Cfg::BN_ ? r - Cfg::BN_ : r) * row_stride_b + cl * 16);
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES>
+// Eight E4M3 codes (two dwords) as eight bf16 values, exactly (every E4M3 value is a bf16).
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES, bool W8>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES>;
+  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, W8>;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB;
   constexpr int A_IT = Cfg::A_IT, B_IT = Cfg::B_IT, BKE = Cfg::BKE;
   extern __shared__ __align__(16) char lds[];
@@ -165,7 +180,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int lo = (int)((long long)live * xcd / kNumXcd);
   const int hi = (int)((long long)live * (xcd + 1) / kNumXcd);
   const int nks = K / BKE;
-  const size_t row_stride = (size_t)K * sizeof(T);   // bytes per row of A and of every weight
+  const size_t row_stride = (size_t)K * sizeof(T);   // bytes per row of A
+  const size_t row_stride_b = W8 ? (size_t)K : row_stride;   // bytes per weight row
+  constexpr uint32_t KB_B = Cfg::ROWB_B;              // weight bytes per row per K step
 
   for (int L = lo + j0; L < hi; L += bpx) {
     const TileCoord tc = tile_coord(args, L, ntn, mt_live, bpx, BM);
@@ -173,14 +190,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     // Buffer resources over this tile's A rows and B rows; per-lane 32-bit offsets are fixed
     // for the tile and the K step rides in the scalar offset.
     const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride);
-    const char* B0b = (const char*)args.B0 + ((size_t)g * N + (size_t)nt * BN) * row_stride;
-    const char* B1b = GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride : B0b;
+    const char* B0b = (const char*)args.B0 + ((size_t)g * N + (size_t)nt * BN) * row_stride_b;
+    const char* B1b = GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride_b : B0b;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, 0x7fffffff, kBufFlags);
     const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, 0x7fffffff, kBufFlags);
     const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, 0x7fffffff, kBufFlags);
 
     uint32_t voffA[A_IT], voffB[B_IT];
-    tile_offsets<Cfg>(args, wave, lane, row0, rows, row_stride, voffA, voffB);
+    tile_offsets<Cfg>(args, wave, lane, row0, rows, row_stride, row_stride_b, voffA, voffB);
     auto a_slot = [&](int s) { return lds + s * Cfg::A_SLOT; };
     auto b_slot = [&](int s) { return lds + Cfg::B_BASE + s * Cfg::B_SLOT; };
 
@@ -199,6 +216,37 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     auto compute = [&](const char* As, const char* Bs) {
       const int ra = wm * Cfg::WTM + (lane & 15);
       const int rb = wn * Cfg::WTN + (lane & 15);
+      if constexpr (W8) {
+        // FP8 weights: one 16-byte LDS read per weight subtile gives lane group q = lane >> 4
+        // the codes of K elements 16q .. 16q+15 of the step; the MFMA of half h takes
+        // 16q + 8h .. 16q + 8h + 7 from both operands (the same permutation of the
+        // contraction index on A and B leaves every dot product unchanged), so the A
+        // fragment of half h is 16-byte piece 2q + h of the activation row.
+        u32x4_t raw[TN * NB];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          raw[j] = *(const u32x4_t*)(Bs + swz64(rb + j * 16, lane >> 4));
+          if constexpr (GATED) raw[TN + j] = *(const u32x4_t*)(Bs + swz64(BN + rb + j * 16, lane >> 4));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4_t b[TN * NB];
+#pragma unroll
+          for (int j = 0; j < TN * NB; ++j) b[j] = e4m3x8_to_bf16(raw[j][2 * h], raw[j][2 * h + 1]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {
+              const u32x4_t a = *(const u32x4_t*)(As + swz(ra + i * 16, 2 * (lane >> 4) + h));
+#pragma unroll
+              for (int j = 0; j < TN; ++j) {
+                Mfma<T>::step(acc0[i][j], a, b[j]);
+                if constexpr (GATED) Mfma<T>::step(acc1[i][j], a, b[TN + j]);
+              }
+            }
+          }
+        }
+        return;
+      }
       auto rdA = [&](int i, int kc) {
         const int r = ra + i * 16;
         return *(const u32x4_t*)(As + swz(r, kc * 4 + (lane >> 4)));
@@ -240,7 +288,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       for (int p = 0; p < STAGES - 1; ++p)
         if (p < nks) {
           issue_a<Cfg>(a_slot(p), (uint32_t)p * 128, rsA, voffA, wave);
-          issue_b<Cfg>(b_slot(p), (uint32_t)p * 128, rsB0, rsB1, voffB, wave);
+          issue_b<Cfg>(b_slot(p), (uint32_t)p * KB_B, rsB0, rsB1, voffB, wave);
         }
       int slot = 0;
       for (int ks = 0; ks < nks; ++ks) {
@@ -249,7 +297,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         if (ks + STAGES - 1 < nks) {
           const int fs = slot == 0 ? STAGES - 1 : slot - 1;
           issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsA, voffA, wave);
-          issue_b<Cfg>(b_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsB0, rsB1, voffB, wave);
+          issue_b<Cfg>(b_slot(fs), (uint32_t)(ks + STAGES - 1) * KB_B, rsB0, rsB1, voffB, wave);
         }
         compute(a_slot(slot), b_slot(slot));
         slot = slot + 1 == STAGES ? 0 : slot + 1;
@@ -260,7 +308,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       // those of B(ks+1), so waiting until at most LPS_B are outstanding lands A(ks), B(ks).
       issue_a<Cfg>(a_slot(0), 0, rsA, voffA, wave);
       issue_b<Cfg>(b_slot(0), 0, rsB0, rsB1, voffB, wave);
-      if (nks > 1) issue_b<Cfg>(b_slot(1), 128, rsB0, rsB1, voffB, wave);
+      if (nks > 1) issue_b<Cfg>(b_slot(1), KB_B, rsB0, rsB1, voffB, wave);
       int bs = 0;                                       // weight slot of step ks
       for (int ks = 0; ks < nks; ++ks) {
         if (ks + 1 < nks) wait_vmcnt<Cfg::LPS_B>();
@@ -268,73 +316,79 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         block_barrier();                                // step ks visible; slots of ks-1 free
         if (ks + 1 < nks) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * 128, rsA, voffA, wave);
         if (ks + 2 < nks)
-          issue_b<Cfg>(b_slot(bs == 0 ? 2 : bs - 1), (uint32_t)(ks + 2) * 128, rsB0, rsB1, voffB, wave);
+          issue_b<Cfg>(b_slot(bs == 0 ? 2 : bs - 1), (uint32_t)(ks + 2) * KB_B, rsB0, rsB1, voffB, wave);
         compute(a_slot(ks & 1), b_slot(bs));
         bs = bs == 2 ? 0 : bs + 1;
       }
     }
     __syncthreads();                                    // LDS free for the next tile
 
-    store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, nt, row0, rows);
+    store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, g, nt, row0, rows);
   }
 }
 
 // ------------------------------------------------------------------------------ launch
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES,
+          bool W8 = false>
 static hipError_t launch_cfg(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
-  return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES>,
-                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES>>(a, max_tiles_m, stream);
+  return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, W8>,
+                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, W8>>(a, max_tiles_m, stream);
 }
 
-int gemm_block_m(GemmKind kind, int dtype, bool gated) {
-  if (kind == kGemmLarge) return dtype == 1 && !gated ? kLargeBf16BlockM : 256;
+int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt) {
+  if (kind == kGemmLarge) return dtype == 1 && !gated && wfmt == 0 ? kLargeBf16BlockM : 256;
   return kind == kGemmStream ? 160 : 16;
 }
 
-template <typename T, bool GATED>
+template <typename T, bool GATED, bool W8>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
     case kGemmLarge:
-      if constexpr (sizeof(T) == 2 && !GATED) return launch_gemm_large_bf16(a, max_tiles_m, s);
+      if constexpr (sizeof(T) == 2 && !GATED && !W8) return launch_gemm_large_bf16(a, max_tiles_m, s);
       // 8 waves; activations in a 2-deep ring, weights (the HBM stream) in a 3-deep one
       if constexpr (GATED) {
-        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3>(a, max_tiles_m, s);   // 64x(64+64) per wave
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, W8>(a, max_tiles_m, s);   // 64x(64+64) per wave
       } else {
-        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2, 3>(a, max_tiles_m, s);
-        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3>(a, max_tiles_m, s);
+        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2, 3, W8>(a, max_tiles_m, s);
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, W8>(a, max_tiles_m, s);
       }
     case kGemmStream:
       // weight streaming with ~100-250 rows per expert: wide weight tiles, 3-deep ring so
       // two K steps of weights are in flight per CU
       if constexpr (GATED) {
-        return launch_cfg<T, 160, 128, 2, 4, GATED, 3>(a, max_tiles_m, s);   // 80x(32+32) per wave
+        return launch_cfg<T, 160, 128, 2, 4, GATED, 3, 3, W8>(a, max_tiles_m, s);   // 80x(32+32) per wave
       } else {
-        if (a.N % 256 == 0) return launch_cfg<T, 160, 256, 2, 4, GATED, 3>(a, max_tiles_m, s);
-        return launch_cfg<T, 160, 128, 2, 4, GATED, 3>(a, max_tiles_m, s);
+        if (a.N % 256 == 0) return launch_cfg<T, 160, 256, 2, 4, GATED, 3, 3, W8>(a, max_tiles_m, s);
+        return launch_cfg<T, 160, 128, 2, 4, GATED, 3, 3, W8>(a, max_tiles_m, s);
       }
     default:
       // decode: a few rows per expert, 4-deep ring; the down product has half the weight
       // rows of gate/up, so narrower tiles give it as many blocks streaming in parallel
-      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, 4>(a, max_tiles_m, s);
-      else return launch_cfg<T, 16, 32, 1, 2, GATED, 4>(a, max_tiles_m, s);
+      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, 4, 4, W8>(a, max_tiles_m, s);
+      else return launch_cfg<T, 16, 32, 1, 2, GATED, 4, 4, W8>(a, max_tiles_m, s);
   }
 }
 
-hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const int32_t* a_rows, const void* Wg,
-                              const void* Wu, const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
-                              int max_tiles_m, int N, int K, void* H, hipStream_t stream) {
-  GemmArgs a{A, a_rows, Wg, Wu, offsets, tstart, G, dense_rows, N, K, H};
-  return dtype == 1 ? dispatch_kind<uint16_t, true>(kind, a, max_tiles_m, stream)
-                    : dispatch_kind<float, true>(kind, a, max_tiles_m, stream);
+hipError_t launch_gemm_gateup(GemmKind kind, int dtype, int wfmt, const void* A, const int32_t* a_rows,
+                              const void* Wg, const void* Wu, const float* Sg, const float* Su,
+                              const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
+                              int N, int K, void* H, hipStream_t stream) {
+  GemmArgs a{A, a_rows, Wg, Wu, Sg, Su, offsets, tstart, G, dense_rows, N, K, H};
+  if (dtype == 1)
+    return wfmt == 1 ? dispatch_kind<uint16_t, true, true>(kind, a, max_tiles_m, stream)
+                     : dispatch_kind<uint16_t, true, false>(kind, a, max_tiles_m, stream);
+  return dispatch_kind<float, true, false>(kind, a, max_tiles_m, stream);
 }
 
-hipError_t launch_gemm_down(GemmKind kind, int dtype, const void* H, const void* Wd, const int32_t* offsets,
-                            const int32_t* tstart, int G, int dense_rows, int max_tiles_m, int N, int K, float* O,
-                            hipStream_t stream) {
-  GemmArgs a{H, nullptr, Wd, nullptr, offsets, tstart, G, dense_rows, N, K, O};
-  return dtype == 1 ? dispatch_kind<uint16_t, false>(kind, a, max_tiles_m, stream)
-                    : dispatch_kind<float, false>(kind, a, max_tiles_m, stream);
+hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, const void* Wd, const float* Sd,
+                            const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
+                            int N, int K, float* O, hipStream_t stream) {
+  GemmArgs a{H, nullptr, Wd, nullptr, Sd, nullptr, offsets, tstart, G, dense_rows, N, K, O};
+  if (dtype == 1)
+    return wfmt == 1 ? dispatch_kind<uint16_t, false, true>(kind, a, max_tiles_m, stream)
+                     : dispatch_kind<uint16_t, false, false>(kind, a, max_tiles_m, stream);
+  return dispatch_kind<float, false, false>(kind, a, max_tiles_m, stream);
 }
 
 }  // namespace moe

@@ -13,11 +13,11 @@
 
 namespace moe {
 
-__device__ __forceinline__ int swz64(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
 
 template <typename T, int BN, bool GATED>
 struct LargeTile {
   using Elem = T;
+  static constexpr bool W8_ = false;
   static constexpr int NT = 256, WM = 2, WN = 2;
   static constexpr int BM_ = kLargeBf16BlockM, BN_ = BN, NB = GATED ? 2 : 1, BROWS = BN * NB;
   static constexpr int WTM = BM_ / WM, WTN = BN / WN;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_large_kernel(GemmArgs args) 
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();                                    // LDS free for the next tile
 
-    store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, nt, row0, rows);
+    store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, g, nt, row0, rows);
   }
 }
 

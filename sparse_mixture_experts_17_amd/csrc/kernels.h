@@ -47,19 +47,21 @@ hipError_t launch_combine(const float* o, const int32_t* row_of, const float* ga
 // Grouped GEMM tile configurations (one kernel template; see grouped_gemm.hip).
 enum GemmKind { kGemmLarge = 0, kGemmStream = 1, kGemmDecode = 2 };
 // Tile rows of the kernel that `kind` selects for the gate/up (gated) or down product.
-int gemm_block_m(GemmKind kind, int dtype, bool gated);
+int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt);
 
 // Gate/up product with the SiLU(a) * b epilogue:  h[r, n] = SiLU(A_r W_g[e]^T) * (A_r W_u[e]^T).
 // A_r is row r of A, or row a_rows[r] of A when a_rows != NULL (the dispatch gather done by
 // the loads; the byte offset a_rows[r] * K * elem must stay below 2^32).
 // offsets == NULL means one group of `dense_rows` rows.  tstart = per-group tile starts.
-hipError_t launch_gemm_gateup(GemmKind kind, int dtype, const void* A, const int32_t* a_rows, const void* Wg,
-                              const void* Wu, const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
-                              int max_tiles_m, int N, int K, void* H, hipStream_t stream);
+// wfmt 1: Wg, Wu hold E4M3 codes and Sg, Su [G, N] their row scales (bf16 activations).
+hipError_t launch_gemm_gateup(GemmKind kind, int dtype, int wfmt, const void* A, const int32_t* a_rows,
+                              const void* Wg, const void* Wu, const float* Sg, const float* Su,
+                              const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
+                              int N, int K, void* H, hipStream_t stream);
 
-// Down projection:  o[r, n] = H_e W_d[e]^T, fp32 out.
-hipError_t launch_gemm_down(GemmKind kind, int dtype, const void* H, const void* Wd, const int32_t* offsets,
-                            const int32_t* tstart, int G, int dense_rows, int max_tiles_m, int N, int K,
-                            float* O, hipStream_t stream);
+// Down projection:  o[r, n] = H_e W_d[e]^T, fp32 out (times Sd[e, n] for FP8 weights).
+hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, const void* Wd, const float* Sd,
+                            const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
+                            int N, int K, float* O, hipStream_t stream);
 
 }  // namespace moe

@@ -12,16 +12,24 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import MOE_BF16, MOE_F32, MoeShape, check, lib
+from ._lib import MOE_BF16, MOE_F32, MoeShape, MoeWScales, check, lib
 
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 
 def make_shape(T: int, d: int, d_e: int, E: int, k: int, capacity: int = -1, renormalize: bool = True,
                d_e_shared: int = 0, dtype: int = MOE_BF16, scoring: int = 0, n_group: int = 1,
-               topk_group: int = 1) -> MoeShape:
+               topk_group: int = 1, wfmt: int = 0) -> MoeShape:
     return MoeShape(T, d, d_e, E, k, capacity, int(bool(renormalize)), d_e_shared, dtype, scoring, n_group,
-                    topk_group)
+                    topk_group, wfmt)
+
+
+def _scales(sc):
+    """(gate, up, down) row-scale tensors -> MoeWScales pointer, or NULL."""
+    if sc is None:
+        return None
+    g, u, d = sc
+    return C.pointer(MoeWScales(_ptr(g), _ptr(u), _ptr(d)))
 
 
 def _ptr(t):
@@ -80,10 +88,11 @@ def moe_permute(shape, x, idx, kept, offsets, row_token, row_of, x_perm, ws, str
                                            _stream(stream)))
 
 
-def moe_expert_ffn(shape, x_perm, offsets, w_gate, w_up, w_down, o, ws, stream=None) -> None:
+def moe_expert_ffn(shape, x_perm, offsets, w_gate, w_up, w_down, scales, o, ws, stream=None) -> None:
+    """scales: None, or the (gate, up, down) row-scale tensors of FP8 weights."""
     check("moe_expert_ffn", lib().moe_expert_ffn(C.byref(shape), _ptr(x_perm), _ptr(offsets), _ptr(w_gate),
-                                                 _ptr(w_up), _ptr(w_down), _ptr(o), _ptr(ws), _nbytes(ws),
-                                                 _stream(stream)))
+                                                 _ptr(w_up), _ptr(w_down), _scales(scales), _ptr(o), _ptr(ws),
+                                                 _nbytes(ws), _stream(stream)))
 
 
 def moe_combine(shape, o, row_of, gate, shared_out, y, stream=None) -> None:
@@ -91,12 +100,14 @@ def moe_combine(shape, o, row_of, gate, shared_out, y, stream=None) -> None:
                                            _ptr(y), _stream(stream)))
 
 
-def moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, idx, gate, counts, kept,
-                f, P, aux, offsets, row_token, row_of, ws, stream=None, stage_events=None) -> None:
-    """stage_events: None, or a ctypes array of MOE_NUM_STAGES + 1 hipEvent_t handles."""
+def moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, scales, shared_scales, y, idx,
+                gate, counts, kept, f, P, aux, offsets, row_token, row_of, ws, stream=None, stage_events=None) -> None:
+    """scales / shared_scales: None, or (gate, up, down) row-scale tensors of FP8 weights.
+    stage_events: None, or a ctypes array of MOE_NUM_STAGES + 1 hipEvent_t handles."""
     check("moe_forward", lib().moe_forward(
         C.byref(shape), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
-        _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(idx), _ptr(gate), _ptr(counts), _ptr(kept), _ptr(f), _ptr(P),
+        _ptr(ws_up), _ptr(ws_down), _scales(scales), _scales(shared_scales), _ptr(y), _ptr(idx), _ptr(gate),
+        _ptr(counts), _ptr(kept), _ptr(f), _ptr(P),
         _ptr(aux), _ptr(offsets), _ptr(row_token), _ptr(row_of), _ptr(ws), _nbytes(ws), _stream(stream),
         stage_events))
 
@@ -140,10 +151,12 @@ def alloc_forward(shape: MoeShape, device="cuda") -> ForwardOutputs:
 
 
 def forward(shape: MoeShape, x, w_r, b_r, w_gate, w_up, w_down, shared=None, out: ForwardOutputs | None = None,
-            stream=None, stage_events=None) -> ForwardOutputs:
-    """Run the whole layer; returns the outputs (allocating them unless `out` is given)."""
+            stream=None, stage_events=None, scales=None, shared_scales=None) -> ForwardOutputs:
+    """Run the whole layer; returns the outputs (allocating them unless `out` is given).
+    scales / shared_scales: (gate, up, down) row scales when the weights are FP8 codes."""
     out = out or alloc_forward(shape, x.device)
     sg, su, sd = shared if shared is not None else (None, None, None)
-    moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, sg, su, sd, out.y, out.idx, out.gate, out.counts,
-                out.kept, out.f, out.P, out.aux, out.offsets, out.row_token, out.row_of, out.ws, stream, stage_events)
+    moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, sg, su, sd, scales, shared_scales, out.y, out.idx,
+                out.gate, out.counts, out.kept, out.f, out.P, out.aux, out.offsets, out.row_token, out.row_of, out.ws,
+                stream, stage_events)
     return out

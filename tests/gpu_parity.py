@@ -38,7 +38,7 @@ def shape_of(w: wl.Workload, T=None):
     return moe.make_shape(w.T if T is None else T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
                           d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32,
                           scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group,
-                          topk_group=w.topk_group), cap
+                          topk_group=w.topk_group, wfmt=moe.MOE_W_FP8_E4M3 if w.weights == "fp8_e4m3" else 0), cap
 
 
 def router_kw(w: wl.Workload) -> dict:
@@ -53,10 +53,26 @@ def f64(a, w):
     return wl.as_f64(a, w.dtype)
 
 
+def expert_f64(inp, e):
+    """Float64 weights of routed expert e as the GPU sees them (FP8 codes decoded by the
+    oracle and scaled per row)."""
+    if inp.wl.weights == "fp8_e4m3":
+        return tuple(mo.dequantize_rows(q, sc) for q, sc in inp.expert_q(e))
+    return tuple(f64(m, inp.wl) for m in inp.expert(e))
+
+
+def shared_f64(inp):
+    if inp.wl.weights == "fp8_e4m3":
+        sq = inp.shared_q()
+        return None if sq is None else tuple(mo.dequantize_rows(q, sc) for q, sc in sq)
+    sh = inp.shared()
+    return None if sh is None else tuple(f64(m, inp.wl) for m in sh)
+
+
 def experts_f64(inp, es, threads=16):
     """{e: float64 weights} for the experts in es, drawn in parallel on the host."""
     def one(e):
-        return e, tuple(f64(m, inp.wl) for m in inp.expert(e))
+        return e, expert_f64(inp, e)
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
         return dict(ex.map(one, sorted(set(int(e) for e in es))))
 
@@ -101,12 +117,14 @@ def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
     dev = upload(inp)
     shape, cap = shape_of(w)
     assert cap == oracle_cap(w)
-    out = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+    out = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared,
+                      scales=dev.scales, shared_scales=dev.shared_scales)
     torch.cuda.synchronize()
     h = {k: getattr(out, k).cpu().numpy() for k in
          ["y", "idx", "gate", "counts", "kept", "f", "P", "aux", "offsets", "row_token", "row_of"]}
     if repeat_check:
-        out2 = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+        out2 = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared,
+                           scales=dev.scales, shared_scales=dev.shared_scales)
         torch.cuda.synchronize()
         R = int(h["offsets"][-1])                # row_token past R is left untouched
         for k in h:
@@ -119,8 +137,7 @@ def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
     p, nt, flipped = check_routing(w, inp, h["idx"], h["gate"], h["counts"], h["f"], h["P"], h["aux"][0])
     disp = check_dispatch(w, h["idx"], cap, h["kept"], h["offsets"], h["row_token"], h["row_of"])
     x = f64(inp.x, w)
-    sh = inp.shared()
-    sh = None if sh is None else tuple(f64(m, w) for m in sh)
+    sh = shared_f64(inp)
     if sample is None:
         ex = experts_f64(inp, range(w.E))
         ref = mo.moe_forward(x, f64(inp.w_r, w), [ex[e] for e in range(w.E)], w.k, cap, inp.b_r, w.renormalize,

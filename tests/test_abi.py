@@ -54,6 +54,7 @@ def _shape(**kw):
     (dict(scoring=2), 3), (dict(scoring=-1), 3), (dict(n_group=0), 2), (dict(n_group=3), 2),
     (dict(n_group=4, topk_group=0), 2), (dict(n_group=4, topk_group=5), 2),
     (dict(n_group=8, topk_group=1, k=2), 2), (dict(E=256, n_group=128, topk_group=2), 3),
+    (dict(wfmt=2), 3), (dict(wfmt=-1), 3), (dict(wfmt=1, dtype=moe.MOE_F32), 3),
 ])
 def test_shape_validation(kw, status):
     n = C.c_size_t()
@@ -91,6 +92,17 @@ def _args(n):
     return [FAKE] * n
 
 
+def _ffn(lib, s, a, ws_bytes, scales=None):
+    """moe_expert_ffn with pointers a = x_perm, offsets, wg, wu, wd, o, ws."""
+    return lib.moe_expert_ffn(C.byref(s), *a[:5], scales, a[5], a[6], ws_bytes, None)
+
+
+def _fwd(lib, s, a, ws_bytes, scales=None, shared_scales=None):
+    """moe_forward with pointers a = x w_r b_r w_gate w_up w_down ws_gate ws_up ws_down y idx gate counts
+    kept f P aux offsets row_token row_of ws."""
+    return lib.moe_forward(C.byref(s), *a[:9], scales, shared_scales, *a[9:20], a[20], ws_bytes, None, None)
+
+
 def test_device_calls_reject_null_and_small_workspace():
     lib = _lib.lib()
     s = _shape()
@@ -110,13 +122,13 @@ def test_device_calls_reject_null_and_small_workspace():
         b = list(a)
         b[i] = None
         assert lib.moe_permute(C.byref(s), *b[:7], b[7], ws_need, None) == 1, i
-    # moe_expert_ffn: x_perm, offsets, wg, wu, wd, o, ws
+    # moe_expert_ffn: x_perm, offsets, wg, wu, wd, (scales), o, ws
     a = _args(7)
-    assert lib.moe_expert_ffn(C.byref(s), *a[:6], a[6], 0, None) == 4
+    assert _ffn(lib, s, a, 0) == 4
     for i in range(7):
         b = list(a)
         b[i] = None
-        assert lib.moe_expert_ffn(C.byref(s), *b[:6], b[6], ws_need, None) == 1, i
+        assert _ffn(lib, s, b, ws_need) == 1, i
     # moe_combine: o, row_of, gate, shared (optional), y
     for i in (0, 1, 2, 4):
         b = _args(5)
@@ -128,15 +140,43 @@ def test_device_calls_reject_null_and_small_workspace():
     #        row_token row_of ws; b_r, the shared weights and offsets/row_token/row_of are optional
     for i in (2, 6, 7, 8, 17, 18, 19):
         a[i] = None
-    assert lib.moe_forward(C.byref(s), *a[:20], a[20], 10, None, None) == 4
+    assert _fwd(lib, s, a, 10) == 4
     for i in (0, 1, 3, 4, 5, 9, 10, 11, 12, 13, 14, 15, 16, 20):
         b = list(a)
         b[i] = None
-        assert lib.moe_forward(C.byref(s), *b[:20], b[20], ws_need, None, None) == 1, i
+        assert _fwd(lib, s, b, ws_need) == 1, i
     # shared expert weights are required when d_e_shared > 0
     s2 = _shape(d_e_shared=256)
-    assert lib.moe_forward(C.byref(s2), *a[:20], a[20], moe.moe_workspace_bytes(s2), None, None) == 1
+    assert _fwd(lib, s2, a, moe.moe_workspace_bytes(s2)) == 1
     # shape errors come first
     bad = _shape(k=9)
-    assert lib.moe_forward(C.byref(bad), *_args(20), FAKE, 1 << 40, None, None) == 2
+    assert _fwd(lib, bad, _args(21), 1 << 40) == 2
     assert lib.moe_route(None, *_args(9), FAKE, 1 << 40, None) == 1
+
+
+def test_fp8_weights_need_scales():
+    """FP8 weights: every row-scale pointer is required; native weights ignore them."""
+    lib = _lib.lib()
+    s = _shape(wfmt=moe.MOE_W_FP8_E4M3, dtype=moe.MOE_BF16)
+    assert moe.moe_workspace_bytes(s) > 0
+    ws_need = moe.moe_workspace_bytes(s)
+    a = _args(7)
+    assert _ffn(lib, s, a, ws_need) == 1                                  # no scales
+    for miss in range(3):
+        ptrs = [FAKE] * 3
+        ptrs[miss] = None
+        assert _ffn(lib, s, a, ws_need, C.byref(_lib.MoeWScales(*ptrs))) == 1, miss
+    full = _lib.MoeWScales(FAKE, FAKE, FAKE)
+    assert _ffn(lib, s, a, 0, C.byref(full)) == 4                         # scales accepted; workspace next
+    f = _args(21)
+    for i in (2, 6, 7, 8, 17, 18, 19):
+        f[i] = None
+    assert _fwd(lib, s, f, ws_need) == 1
+    assert _fwd(lib, s, f, 10, C.byref(full)) == 4
+    s2 = _shape(wfmt=moe.MOE_W_FP8_E4M3, dtype=moe.MOE_BF16, d_e_shared=256)
+    f2 = list(f)
+    f2[6] = f2[7] = f2[8] = FAKE
+    assert _fwd(lib, s2, f2, 10, C.byref(full)) == 1                      # shared scales missing
+    assert _fwd(lib, s2, f2, 10, C.byref(full), C.byref(full)) == 4
+    native = _shape()
+    assert _ffn(lib, native, a, 0) == 4                                   # native: scales not needed

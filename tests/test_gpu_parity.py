@@ -48,6 +48,15 @@ SMALL = [
               topk_group=2, router_bias_var=0.5),
     wl.scaled(BASE["mixtral_prefill"], name="grouped_64", T=33, d=128, d_e=128, E=1024, k=16, n_group=64,
               topk_group=3),
+    # FP8 E4M3 expert weights in every tile configuration
+    wl.scaled(BASE["mixtral_decode_fp8"], name="fp8_decode_tiles", T=16, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_decode_fp8"], name="fp8_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_fp8"], name="fp8_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_fp8"], name="fp8_large_d384", T=1600, d=384, d_e=256, E=4, k=2),
+    wl.scaled(BASE["deepseek_v3_fp8"], name="fp8_deepseek_small", T=300, d=512, d_e=256, E=256, k=8,
+              d_e_shared=256),
+    wl.scaled(BASE["deepseek_v3_fp8"], name="fp8_shared_large", T=1100, d=256, d_e=128, E=32, k=4, d_e_shared=384,
+              capacity_factor=1.0),
 ]
 
 
@@ -57,7 +66,8 @@ def test_forward_small(w):
     gp.run_forward(w, repeat_check=True)
 
 
-FULL = ["tiny_fp32", "switch_capacity", "mixtral_decode", "mixtral_prefill", "deepseek_v3", "deepseek_v3_grouped"]
+FULL = ["tiny_fp32", "switch_capacity", "mixtral_decode", "mixtral_prefill", "deepseek_v3", "deepseek_v3_grouped",
+        "mixtral_decode_fp8", "mixtral_prefill_fp8", "deepseek_v3_fp8"]
 
 
 @needs_gpu
@@ -81,16 +91,18 @@ def _upload_i32(a):
 
 
 @needs_gpu
-@pytest.mark.parametrize("scoring", ["softmax", "sigmoid_grouped"])
-def test_split_calls_compose(scoring):
+@pytest.mark.parametrize("variant", ["softmax", "sigmoid_grouped", "fp8_weights"])
+def test_split_calls_compose(variant):
     """moe_route -> moe_permute -> moe_expert_ffn (+ shared) -> moe_combine equals moe_forward."""
-    extra = {} if scoring == "softmax" else dict(scoring="sigmoid", n_group=4, topk_group=2, router_bias_var=1e-3)
+    extra = {"softmax": {}, "fp8_weights": dict(weights="fp8_e4m3"),
+             "sigmoid_grouped": dict(scoring="sigmoid", n_group=4, topk_group=2, router_bias_var=1e-3)}[variant]
     w = wl.scaled(BASE["deepseek_v3"], name="split", T=211, d=256, d_e=128, E=16, k=3, d_e_shared=256,
                   capacity_factor=1.1, **extra)
     inp = wl.make_inputs(w)
     dev = upload(inp)
     shape, cap = gp.shape_of(w)
-    ref = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+    ref = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared,
+                      scales=dev.scales, shared_scales=dev.shared_scales)
     T, d, E, k = w.T, w.d, w.E, w.k
     ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     i32, f32 = torch.int32, torch.float32
@@ -108,13 +120,14 @@ def test_split_calls_compose(scoring):
     x_perm = torch.zeros((T * k, d), dtype=dev.x.dtype, device="cuda")
     moe.moe_permute(shape, dev.x, idx, kept, offsets, row_token, row_of, x_perm, ws)
     o = torch.zeros((T * k, d), dtype=f32, device="cuda")
-    moe.moe_expert_ffn(shape, x_perm, offsets, dev.w_gate, dev.w_up, dev.w_down, o, ws)
-    sshape = moe.make_shape(T, d, w.d_e_shared, 1, 1, dtype=shape.dtype)
+    moe.moe_expert_ffn(shape, x_perm, offsets, dev.w_gate, dev.w_up, dev.w_down, dev.scales, o, ws)
+    sshape = moe.make_shape(T, d, w.d_e_shared, 1, 1, dtype=shape.dtype, wfmt=shape.wfmt)
     sws = torch.empty(moe.moe_workspace_bytes(sshape), dtype=torch.uint8, device="cuda")
     s_out = torch.zeros((T, d), dtype=f32, device="cuda")
     soff = _upload_i32([0, T])
     moe.moe_expert_ffn(sshape, dev.x, soff, dev.shared[0].unsqueeze(0).contiguous(),
-                       dev.shared[1].unsqueeze(0).contiguous(), dev.shared[2].unsqueeze(0).contiguous(), s_out, sws)
+                       dev.shared[1].unsqueeze(0).contiguous(), dev.shared[2].unsqueeze(0).contiguous(),
+                       dev.shared_scales, s_out, sws)
     y = torch.empty((T, d), dtype=f32, device="cuda")
     moe.moe_combine(shape, o, row_of, gate, s_out, y)
     torch.cuda.synchronize()
@@ -156,6 +169,8 @@ def test_expert_ffn_given_rows():
     """moe_expert_ffn on host-built expert-ordered rows, ragged groups incl. empty ones."""
     for w, rows in [(wl.scaled(BASE["tiny_fp32"], name="ffn32", T=200, d=256, d_e=256, E=5, k=1), [0, 57, 1, 0, 142]),
                     (wl.scaled(BASE["mixtral_prefill"], name="ffnbf", T=1300, d=256, d_e=512, E=3, k=1),
+                     [600, 0, 700]),
+                    (wl.scaled(BASE["mixtral_prefill_fp8"], name="ffn_fp8", T=1300, d=256, d_e=512, E=3, k=1),
                      [600, 0, 700])]:
         inp = wl.make_inputs(w)
         dev = upload(inp)
@@ -163,13 +178,13 @@ def test_expert_ffn_given_rows():
         offs = np.concatenate([[0], np.cumsum(rows)])
         o = torch.zeros((w.T, w.d), dtype=torch.float32, device="cuda")
         ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
-        moe.moe_expert_ffn(shape, dev.x, _upload_i32(offs), dev.w_gate, dev.w_up, dev.w_down, o, ws)
+        moe.moe_expert_ffn(shape, dev.x, _upload_i32(offs), dev.w_gate, dev.w_up, dev.w_down, dev.scales, o, ws)
         torch.cuda.synchronize()
         x = gp.f64(inp.x, w)
         ref = np.zeros((w.T, w.d))
         for e in range(w.E):
             if rows[e]:
-                ref[offs[e]:offs[e + 1]] = mo.swiglu_ffn(x[offs[e]:offs[e + 1]], *(gp.f64(m, w) for m in inp.expert(e)))
+                ref[offs[e]:offs[e + 1]] = mo.swiglu_ffn(x[offs[e]:offs[e + 1]], *gp.expert_f64(inp, e))
         err = mo.rel_err(o.cpu().numpy(), ref)
         assert err <= gp.TOL[w.dtype], err
 
@@ -206,8 +221,8 @@ def test_degenerate_inputs():
     out.aux.fill_(7)
     out.counts.fill_(7)
     e = torch.empty(0, device="cuda", dtype=torch.bfloat16)
-    moe.moe_forward(shape, e, e, None, e, e, e, None, None, None, out.y, out.idx, out.gate, out.counts, out.kept,
-                    out.f, out.P, out.aux, out.offsets, None, out.row_of, out.ws)
+    moe.moe_forward(shape, e, e, None, e, e, e, None, None, None, None, None, out.y, out.idx, out.gate, out.counts,
+                    out.kept, out.f, out.P, out.aux, out.offsets, None, out.row_of, out.ws)
     torch.cuda.synchronize()
     assert torch.all(out.f == 0) and torch.all(out.P == 0) and float(out.aux) == 0 and torch.all(out.counts == 0)
     assert torch.all(out.offsets == 0)

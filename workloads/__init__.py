@@ -59,6 +59,7 @@ class Workload:
     scoring: str = "softmax"   # "softmax", or "sigmoid" (the bias then only steers selection)
     n_group: int = 1           # expert groups for group-limited routing
     topk_group: int = 1        # groups a token may use
+    weights: str = "native"    # expert weights: "native" (dtype), or "fp8_e4m3" (codes + row scales)
     note: str = ""
 
 
@@ -79,6 +80,13 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
              d_e_shared=2048, scoring="sigmoid", n_group=8, topk_group=4, router_bias_var=1e-4,
              note="the DeepSeek-V3 router rule on the same shape: sigmoid affinities, a selection-only "
                   "per-expert bias (std 0.01), each token limited to 4 of 8 expert groups"),
+    Workload("mixtral_decode_fp8", T=16, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="fp8_e4m3",
+             note="Mixtral decode batch with FP8 E4M3 expert weights (one byte each, one fp32 scale per row)"),
+    Workload("mixtral_prefill_fp8", T=4096, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="fp8_e4m3",
+             note="Mixtral prefill batch with FP8 E4M3 expert weights"),
+    Workload("deepseek_v3_fp8", T=4096, d=7168, d_e=2048, E=256, k=8, dtype="bf16", d_e_shared=2048,
+             weights="fp8_e4m3",
+             note="DeepSeek-V3-shaped layer with FP8 E4M3 routed and shared expert weights"),
 ]}
 
 
@@ -110,6 +118,21 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def quantize_e4m3_rows(w: np.ndarray):
+    """FP8 E4M3 storage of a float32 weight matrix, one scale per row.
+
+    Checkpoint preparation, not part of the layer: scale = max|row| / 448 (1 for an
+    all-zero row), codes = the row divided by its scale, rounded to the nearest E4M3
+    value by torch's float8_e4m3fn conversion.  Returns (codes uint8 [n, k], scale f32 [n]).
+    """
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32))
+    amax = t.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (t / scale[:, None]).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy().copy(), scale.numpy().copy()
 
 
 # --------------------------------------------------------------------------- drawing
@@ -147,6 +170,27 @@ class Inputs:
             _draw(self.seed, (3, e, 0), (wl.d_e, wl.d), 1.0 / wl.d, wl.dtype),
             _draw(self.seed, (3, e, 1), (wl.d_e, wl.d), 1.0 / wl.d, wl.dtype),
             _draw(self.seed, (3, e, 2), (wl.d, wl.d_e), 1.0 / wl.d_e, wl.dtype),
+        )
+
+    def expert_q(self, e: int):
+        """FP8 workloads: ((codes, scale) of W_g, of W_u, of W_d) of routed expert e, from
+        the same float32 draws as ``expert``."""
+        wl = self.wl
+        return (
+            quantize_e4m3_rows(_draw(self.seed, (3, e, 0), (wl.d_e, wl.d), 1.0 / wl.d, "f32")),
+            quantize_e4m3_rows(_draw(self.seed, (3, e, 1), (wl.d_e, wl.d), 1.0 / wl.d, "f32")),
+            quantize_e4m3_rows(_draw(self.seed, (3, e, 2), (wl.d, wl.d_e), 1.0 / wl.d_e, "f32")),
+        )
+
+    def shared_q(self):
+        """FP8 workloads: the shared expert's ((codes, scale) x 3), or None."""
+        wl = self.wl
+        if wl.d_e_shared <= 0:
+            return None
+        return (
+            quantize_e4m3_rows(_draw(self.seed, (4, 0), (wl.d_e_shared, wl.d), 1.0 / wl.d, "f32")),
+            quantize_e4m3_rows(_draw(self.seed, (4, 1), (wl.d_e_shared, wl.d), 1.0 / wl.d, "f32")),
+            quantize_e4m3_rows(_draw(self.seed, (4, 2), (wl.d, wl.d_e_shared), 1.0 / wl.d_e_shared, "f32")),
         )
 
     def shared(self):
