@@ -86,10 +86,15 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   if constexpr (STAGES <= 2) {
     wait_vmcnt<0>();
   } else {
+    static_assert(STAGES <= 8, "deeper rings need more cases");
     switch (ahead) {
       case 0: wait_vmcnt<0>(); break;
       case 1: wait_vmcnt<LPS>(); break;
-      default: wait_vmcnt<2 * LPS>(); break;
+      case 2: wait_vmcnt<2 * LPS>(); break;
+      case 3: wait_vmcnt<(STAGES > 4 ? 3 : 2) * LPS>(); break;
+      case 4: wait_vmcnt<(STAGES > 5 ? 4 : 2) * LPS>(); break;
+      case 5: wait_vmcnt<(STAGES > 6 ? 5 : 2) * LPS>(); break;
+      default: wait_vmcnt<(STAGES > 7 ? 6 : 2) * LPS>(); break;
     }
   }
 }
@@ -341,6 +346,11 @@ int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt) {
   return kind == kGemmStream ? 160 : 16;
 }
 
+// LDS ring depth of the decode tiles: FP8 weights carry half the bytes per K step, so they
+// keep more steps in flight.
+template <bool W8>
+constexpr int kDecodeStages = W8 ? 4 : 4;
+
 template <typename T, bool GATED, bool W8>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
@@ -365,8 +375,9 @@ static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipS
     default:
       // decode: a few rows per expert, 4-deep ring; the down product has half the weight
       // rows of gate/up, so narrower tiles give it as many blocks streaming in parallel
-      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, 4, 4, W8>(a, max_tiles_m, s);
-      else return launch_cfg<T, 16, 32, 1, 2, GATED, 4, 4, W8>(a, max_tiles_m, s);
+      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, kDecodeStages<W8>, kDecodeStages<W8>, W8>(
+          a, max_tiles_m, s);
+      else return launch_cfg<T, 16, 32, 1, 2, GATED, kDecodeStages<W8>, kDecodeStages<W8>, W8>(a, max_tiles_m, s);
   }
 }
 
