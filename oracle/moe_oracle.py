@@ -395,6 +395,43 @@ def dequantize_rows(codes, scale) -> np.ndarray:
     return w * np.asarray(scale, np.float64).reshape(-1, 1)
 
 
+def e2m1_decode(nibbles) -> np.ndarray:
+    """Exact value of each 4-bit E2M1 element code (the OCP MX FP4 element), float64.
+
+    The pages cite expert weights kept in MXFP4 (AI Engineering Illustrated, "Total
+    parameters and active parameters are different budgets"; jacopoparretti.dev, "Speed
+    follows active, memory follows total") without defining it.  E2M1: sign bit, 2
+    exponent bits with bias 1, 1 mantissa bit; exponent 0 holds 0 and 0.5; the
+    magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN.
+    """
+    c = np.asarray(nibbles, dtype=np.uint8).astype(np.int64) & 15
+    sign = c >> 3
+    ex = (c >> 1) & 3
+    man = c & 1
+    mag = np.where(ex == 0, 0.5 * man, (1.0 + 0.5 * man) * np.exp2(ex - 1.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """Value of each E8M0 scale byte (the MX shared block scale): 2^(code - 127), 255 = NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def dequantize_mx_rows(packed, scales, block: int = 32) -> np.ndarray:
+    """W [n, k] from MXFP4 storage: packed [n, k/2] bytes, element 2j of a row in the low
+    nibble of byte j and element 2j+1 in the high nibble; scales [k/block, n] E8M0 bytes,
+    scales[b, r] shared by elements block*b .. block*b + block - 1 of row r.
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    n, half = packed.shape
+    codes = np.empty((n, 2 * half), dtype=np.uint8)
+    codes[:, 0::2] = packed & 15
+    codes[:, 1::2] = packed >> 4
+    sc = e8m0_decode(np.asarray(scales, dtype=np.uint8))          # [k/block, n]
+    return e2m1_decode(codes) * np.repeat(sc.T, block, axis=1)
+
+
 def rel_err(y, y_ref) -> float:
     """max |y - y_ref| / rms(y_ref): the output tolerance measure."""
     y = np.asarray(y, np.float64)

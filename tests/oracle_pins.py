@@ -467,4 +467,42 @@ def pin_dequantize_rows():
         assert np.array_equal(w[n], mo.e4m3_decode(codes[n]) * float(scale[n]))
 
 
+def pin_e2m1_table():
+    """The 16 E2M1 codes take the magnitudes the format fixes (0, 0.5, 1, 1.5, 2, 3, 4, 6),
+    the sign bit negates, and only the low four bits of a byte count."""
+    d = mo.e2m1_decode
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(d(np.arange(8, dtype=np.uint8))) == mags
+    neg = d(np.arange(8, 16, dtype=np.uint8))
+    assert list(-neg) == mags and np.signbit(neg[0])
+    assert np.array_equal(d(np.arange(16, 32, dtype=np.uint8)), d(np.arange(16, dtype=np.uint8)))
+
+
+def pin_e8m0_library():
+    """E8M0 scale bytes decode as torch's float8_e8m0fnu does (independent implementation)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = mo.e8m0_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert mo.e8m0_decode(np.array([127]))[0] == 1.0 and mo.e8m0_decode(np.array([130]))[0] == 8.0
+
+
+def pin_mx_dequantize():
+    """Packing and block scales: element 2j in the low nibble of byte j, the scale of block b
+    covering elements 32b .. 32b + 31 of its row (rows and blocks differ, so a transposed
+    scale or swapped nibbles fail)."""
+    rng = _rng(12)
+    n, k = 3, 64
+    codes = rng.integers(0, 16, size=(n, k)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    sc = np.array([[120, 127, 131], [125, 129, 133]], np.uint8)        # [k/32, n]
+    w = mo.dequantize_mx_rows(packed, sc)
+    for r in range(n):
+        for j in range(k):
+            assert w[r, j] == mo.e2m1_decode(codes[r, j:j + 1])[0] * 2.0 ** (int(sc[j // 32, r]) - 127)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

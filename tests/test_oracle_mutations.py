@@ -14,7 +14,7 @@ from oracle import moe_oracle as mo
 _orig = {name: getattr(mo, name) for name in
          ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
           "capacity", "dispatch", "near_ties", "sigmoid", "group_limited_top_k", "route", "e4m3_decode",
-          "dequantize_rows"]}
+          "dequantize_rows", "e2m1_decode", "e8m0_decode", "dequantize_mx_rows"]}
 
 
 def _softmax_no_shift(r):
@@ -172,6 +172,30 @@ def _dequant_columns(codes, scale):
     return w * sc.reshape(1, -1)
 
 
+def _e2m1_bias2(nibbles):
+    return _orig["e2m1_decode"](nibbles) / 2.0
+
+
+def _e2m1_no_subnormal(nibbles):
+    c = np.asarray(nibbles, np.uint8).astype(np.int64) & 15
+    v = _orig["e2m1_decode"](nibbles)
+    return np.where(((c >> 1) & 3) == 0, np.where(c >> 3 == 1, -1.0, 1.0) * (c & 1) * 1.0, v)
+
+
+def _e8m0_bias128(codes):
+    return _orig["e8m0_decode"](codes) / 2.0
+
+
+def _mx_nibbles_swapped(packed, scales, block=32):
+    p = np.asarray(packed, np.uint8)
+    return _orig["dequantize_mx_rows"](((p >> 4) | (p << 4)).astype(np.uint8), scales, block)
+
+
+def _mx_scales_transposed(packed, scales, block=32):
+    sc = np.asarray(scales, np.uint8)
+    return _orig["dequantize_mx_rows"](packed, np.resize(sc.T, sc.shape), block)
+
+
 MUTANTS = [
     ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
     ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
@@ -188,6 +212,8 @@ MUTANTS = [
     ("route", _route_bias_in_gates),
     ("e4m3_decode", _e4m3_bias8), ("e4m3_decode", _e4m3_no_subnormals), ("e4m3_decode", _e4m3_mantissa_16),
     ("dequantize_rows", _dequant_columns),
+    ("e2m1_decode", _e2m1_bias2), ("e2m1_decode", _e2m1_no_subnormal), ("e8m0_decode", _e8m0_bias128),
+    ("dequantize_mx_rows", _mx_nibbles_swapped), ("dequantize_mx_rows", _mx_scales_transposed),
 ]
 
 
