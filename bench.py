@@ -138,7 +138,8 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
     shape = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
                            d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32,
                            scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group, topk_group=w.topk_group,
-                           wfmt=moe.MOE_W_FP8_E4M3 if w.weights == "fp8_e4m3" else moe.MOE_W_NATIVE)
+                           wfmt={"native": moe.MOE_W_NATIVE, "fp8_e4m3": moe.MOE_W_FP8_E4M3,
+                                 "mxfp4": moe.MOE_W_MXFP4}[w.weights])
     out = moe.alloc_forward(shape)
     ev = HipEvents()
     nst = moe._lib.MOE_NUM_STAGES
@@ -192,18 +193,20 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
     R_kept = int(kept.sum())
     touched = int((kept > 0).sum())
     return dict(w=w, shape=shape, cap=cap, total_ms=total_ms, wall_s=t_wall, stages=stages, kernel_ms=kernel_ms,
+                steps=steps,
                 plain_ms=plain_ms, R_kept=R_kept, touched=touched, upload_s=t_up, dev=dev, inp=inp)
 
 
 def layer_work(w, R_kept, touched):
     """Algorithmic FLOPs and bytes of one layer call (per unit figures x units)."""
     s = 2 if w.dtype == "bf16" else 4
-    sw = 1 if w.weights == "fp8_e4m3" else s          # bytes per expert weight (FP8: + 4 per row scale)
+    sw = {"native": s, "fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}[w.weights]   # bytes per expert weight
+    # (MXFP4: half a byte per element plus one scale byte per 32; FP8: + a 4-byte scale per row)
     flops_gate_up = 4 * w.d * w.d_e * R_kept
     flops_down = 2 * w.d * w.d_e * R_kept
     flops_router = 2 * w.d * w.E * w.T
     flops_shared = 6 * w.d * w.d_e_shared * w.T
-    rs = 4 if w.weights == "fp8_e4m3" else 0
+    rs = 4 if w.weights == "fp8_e4m3" else 0           # bytes per weight row outside sw
     bytes_gate_up = touched * 2 * w.d_e * (w.d * sw + rs) + R_kept * w.d * s + R_kept * w.d_e * s
     bytes_down = touched * w.d * (w.d_e * sw + rs) + R_kept * w.d_e * s + R_kept * w.d * 4
     bytes_layer = (touched * 3 * w.d * w.d_e * sw + touched * (2 * w.d_e + w.d) * rs + w.E * w.d * s
@@ -211,6 +214,23 @@ def layer_work(w, R_kept, touched):
     return dict(flops_gate_up=flops_gate_up, flops_down=flops_down, flops_layer=flops_gate_up + flops_down +
                 flops_router + flops_shared, bytes_gate_up=bytes_gate_up, bytes_down=bytes_down,
                 bytes_layer=bytes_layer)
+
+
+def secondary_line(dec, fmt):
+    """JSON object of a decode run with quantised expert weights."""
+    wd = dec["w"]
+    steps = dec["steps"]
+    dwork = layer_work(wd, dec["R_kept"], dec["touched"])
+    dms = dec["total_ms"] / steps
+    gb = dwork["bytes_gate_up"] / (dec["kernel_ms"] / 1e3) / 1e9
+    return {
+        "workload": wd.name, "value": wd.T / (dms / 1e3), "unit": "tokens/s", "ms_per_step": dms,
+        "stages_ms": dec["stages"], "experts_touched": dec["touched"], "ms_per_step_unmarked": dec["plain_ms"],
+        "roofline": {"kernel": f"grouped_gemm gate_up (decode tiles, {fmt} weights)", "bound": "hbm",
+                     "achieved": gb, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
+                     "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
+        "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
+    }
 
 
 def cpu_baseline(info, target_s):
@@ -323,18 +343,12 @@ def main():
         del info["dev"]
         torch.cuda.empty_cache()
         dec = run_gpu("mixtral_decode_fp8", max(a.steps, 20), a.warmup)
-        wd = dec["w"]
-        dwork = layer_work(wd, dec["R_kept"], dec["touched"])
-        dms = dec["total_ms"] / max(a.steps, 20)
-        gb = dwork["bytes_gate_up"] / (dec["kernel_ms"] / 1e3) / 1e9
-        line["secondary_fp8"] = {
-            "workload": wd.name, "value": wd.T / (dms / 1e3), "unit": "tokens/s", "ms_per_step": dms,
-            "stages_ms": dec["stages"], "experts_touched": dec["touched"], "ms_per_step_unmarked": dec["plain_ms"],
-            "roofline": {"kernel": "grouped_gemm gate_up (decode tiles, FP8 weights)", "bound": "hbm",
-                         "achieved": gb, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
-                         "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
-            "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
-        }
+        line["secondary_fp8"] = secondary_line(dec, "FP8")
+        del dec
+        print("[bench] secondary: mixtral_decode_mxfp4 (MXFP4 expert weights)", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        dec = run_gpu("mixtral_decode_mxfp4", max(a.steps, 20), a.warmup)
+        line["secondary_mxfp4"] = secondary_line(dec, "MXFP4")
     if not a.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(info, a.cpu_seconds)

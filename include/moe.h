@@ -36,8 +36,8 @@
  *   d_e_shared >= 0 (0 = no shared expert); T*k < 2^31; dtype in {MOE_F32, MOE_BF16};
  *   scoring in {MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID}; 1 <= n_group <= 64 dividing E;
  *   1 <= topk_group <= n_group; k <= topk_group * E / n_group; T*d*elem_size < 2^32 for
- *   moe_forward (its gather uses 32-bit byte offsets); wfmt in {MOE_W_NATIVE, MOE_W_FP8_E4M3},
- *   FP8 weights only with dtype MOE_BF16.
+ *   moe_forward (its gather uses 32-bit byte offsets); wfmt in {MOE_W_NATIVE, MOE_W_FP8_E4M3,
+ *   MOE_W_MXFP4}, quantised weights only with dtype MOE_BF16.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -84,15 +84,23 @@ typedef struct {
  *   parameter (jacopoparretti.dev, "Memory") because small batches are bound by reading
  *   them (AI Engineering Illustrated, "Trade-offs to weigh").  Products run in bf16 on the
  *   decoded codes (exact in bf16) with fp32 accumulation; the row scale multiplies each
- *   output before SiLU (gate/up) or before it is written (down). */
-typedef enum { MOE_W_NATIVE = 0, MOE_W_FP8_E4M3 = 1 } moe_wfmt;
+ *   output before SiLU (gate/up) or before it is written (down).
+ * MOE_W_MXFP4: OCP MX FP4 (AI Engineering Illustrated, "Total parameters and active parameters
+ *   are different budgets": MoE weights kept in MXFP4).  Elements are E2M1 (bias 1; magnitudes
+ *   0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, element 2j of a row in the low nibble of byte j;
+ *   every 32 consecutive elements of a row share one E8M0 scale byte (2^(s-127); 255 = NaN).
+ *   Weights [G, rows, K/2] bytes; scales [G, K/32, rows] bytes (block-major).  Decoded values
+ *   (element x scale, exact in bf16) feed bf16 products with fp32 accumulation. */
+typedef enum { MOE_W_NATIVE = 0, MOE_W_FP8_E4M3 = 1, MOE_W_MXFP4 = 2 } moe_wfmt;
 
-/* Row scales of FP8 expert weights (device pointers, fp32; G = E for routed experts, 1 for
- * the shared expert). */
+/* Scales of quantised expert weights (device pointers; G = E for routed experts, 1 for the
+ * shared expert).  K is the contraction width of the matrix: d for W_g and W_u, d_e for W_d.
+ *   MOE_W_FP8_E4M3: fp32, one per row    gate, up [G, d_e];      down [G, d]
+ *   MOE_W_MXFP4:    E8M0 bytes per block  gate, up [G, d/32, d_e]; down [G, d_e/32, d] */
 typedef struct {
-  const float *gate;   /* [G, d_e]  scale of each row of W_g */
-  const float *up;     /* [G, d_e]  scale of each row of W_u */
-  const float *down;   /* [G, d]    scale of each row of W_d */
+  const void *gate;    /* scales of W_g */
+  const void *up;      /* scales of W_u */
+  const void *down;    /* scales of W_d */
 } moe_wscales;
 
 /* Router scoring.
@@ -165,10 +173,11 @@ moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *idx
  * x_perm go through expert e; offsets[E] <= T*k.
  *   x_perm  [T*k, d]          dtype
  *   offsets [E+1]             int32
- *   w_gate  [E, d_e, d]       dtype, or uint8 E4M3 codes (wfmt MOE_W_FP8_E4M3)
+ *   w_gate  [E, d_e, d]       dtype; uint8 E4M3 codes (MOE_W_FP8_E4M3); [E, d_e, d/2] packed
+ *                             E2M1 codes (MOE_W_MXFP4)
  *   w_up    [E, d_e, d]       same
- *   w_down  [E, d, d_e]       same
- *   scales  row scales of the three (required iff wfmt = MOE_W_FP8_E4M3, else ignored)
+ *   w_down  [E, d, d_e]       same ([E, d, d_e/2] for MOE_W_MXFP4)
+ *   scales  scales of the three (required iff wfmt != MOE_W_NATIVE, else ignored)
  *   o       [T*k, d]          fp32      out: rows < offsets[E]; the rest untouched
  * The hidden activation is rounded to dtype between the two products (bf16 RNE for
  * MOE_BF16).  The shared expert is this call with E = 1, k = 1, d_e = d_e_shared and
@@ -189,8 +198,8 @@ moe_status moe_combine(const moe_shape *shape, const float *o, const int32_t *ro
 /* The whole layer: route -> dispatch -> grouped experts (+ shared expert) -> combine.
  * Arguments as in the split calls; ws_gate/ws_up ([d_e_shared, d]) and ws_down
  * ([d, d_e_shared]) are the shared expert's weights, required iff d_e_shared > 0.
- * scales / shared_scales: row scales of the routed / shared expert weights, required
- * (shared_scales iff d_e_shared > 0) when wfmt = MOE_W_FP8_E4M3, else ignored.
+ * scales / shared_scales: scales of the routed / shared expert weights, required
+ * (shared_scales iff d_e_shared > 0) when wfmt != MOE_W_NATIVE, else ignored.
  * offsets [E+1], row_token [T*k] and row_of [T, k] are optional outputs (NULL: kept in the
  * workspace).
  * stage_events: NULL, or a host array of MOE_NUM_STAGES + 1 hipEvent_t (created by the

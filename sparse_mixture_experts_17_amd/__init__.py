@@ -7,7 +7,7 @@ Python binding: ``moe_route``, ``moe_permute``, ``moe_expert_ffn``,
 pointers and the current HIP stream through.
 """
 from ._lib import (LIB_PATH, MOE_BF16, MOE_F32, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX,  # noqa: F401
-                   MOE_W_FP8_E4M3, MOE_W_NATIVE, MoeError, MoeShape, MoeWScales, lib)
+                   MOE_W_FP8_E4M3, MOE_W_MXFP4, MOE_W_NATIVE, MoeError, MoeShape, MoeWScales, lib)
 from .moe import (ForwardOutputs, TORCH_DTYPE, alloc_forward, forward, make_shape, moe_capacity,  # noqa: F401
                   moe_combine, moe_expert_ffn, moe_forward, moe_permute, moe_route, moe_status_str,
                   moe_workspace_bytes)

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_W_NATIVE, MOE_W_FP8_E4M3 = 0, 1
+MOE_W_NATIVE, MOE_W_FP8_E4M3, MOE_W_MXFP4 = 0, 1, 2
 MOE_NUM_STAGES = 8
 STAGE_NAMES = ["router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
@@ -28,7 +28,7 @@ class MoeShape(C.Structure):
 
 
 class MoeWScales(C.Structure):
-    """Row scales of FP8 expert weights (device pointers)."""
+    """Scales of quantised expert weights (device pointers)."""
     _fields_ = [("gate", C.c_void_p), ("up", C.c_void_p), ("down", C.c_void_p)]
 
 

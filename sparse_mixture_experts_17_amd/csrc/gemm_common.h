@@ -13,8 +13,8 @@ struct GemmArgs {
   const int32_t* a_rows;    // NULL, or row of A for each expert-ordered row (gather in the load)
   const void* B0;           // [G, N, K] gate (gated) or down weights
   const void* B1;           // [G, N, K] up weights (gated only)
-  const float* S0;          // [G, N] row scales of B0 (FP8 weights), else unused
-  const float* S1;          // [G, N] row scales of B1 (FP8 weights, gated), else unused
+  const float* S0;          // scales of B0: FP8 [G, N] fp32 per row; MXFP4 [G, K/32, N] E8M0 bytes
+  const float* S1;          // scales of B1 (gated), same layout
   const int32_t* offsets;   // [G+1] or NULL (dense: one group of dense_rows)
   const int32_t* tstart;    // [G+1] first m-tile of each group (unused when dense)
   int G, dense_rows, N, K;
@@ -112,7 +112,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
         const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
         if (r < rows) {
           const size_t o = (size_t)(row0 + r) * N + col;
-          if constexpr (Cfg::W8_) {                       // row scales of FP8 weights
+          if constexpr (Cfg::WF_ == 1) {                   // row scales of FP8 weights
             const size_t sc = (size_t)g * N + col;
             if constexpr (Cfg::NB == 2) {
               const float a = acc0[i][j][q] * args.S0[sc], b = acc1[i][j][q] * args.S1[sc];

@@ -32,10 +32,11 @@
 namespace moe {
 
 template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES,
-          bool W8 = false>
+          int WF = 0>
 struct GemmTile {
   using Elem = T;
-  static constexpr bool W8_ = W8;                                   // FP8 E4M3 weights, row scales
+  // weight format: 0 native (dtype), 1 FP8 E4M3 with row scales, 2 MXFP4 (E2M1, E8M0 per 32)
+  static constexpr int WF_ = WF;
   static constexpr int NT = WM * WN * kWave;
   static constexpr int BM_ = BM, BN_ = BN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -45,12 +46,16 @@ struct GemmTile {
   static constexpr int ROWB = 128;                                  // bytes of K per row per stage
   static constexpr int EPP = Mfma<T>::kElemsPerPiece;               // elements per 16-byte piece
   static constexpr int BKE = 8 * EPP;                               // elements of K per stage
-  static constexpr int PPR_B = W8 ? 4 : 8;                          // 16-byte weight pieces per row per step
+  static constexpr int PPR_B = WF == 1 ? 4 : (WF == 2 ? 2 : 8);    // 16-byte weight pieces per row per step
   static constexpr int ROWB_B = PPR_B * 16;
   static constexpr int A_IT = (BM * 8 + NT - 1) / NT;
   static constexpr int B_IT = (BROWS * PPR_B + NT - 1) / NT;
   // LDS: a ring of STAGES activation slots, then a ring of BSTAGES weight slots
-  static constexpr int A_SLOT = BM * ROWB, B_SLOT = BROWS * ROWB_B;
+  // MXFP4: each step's two E8M0 scale bytes per weight row follow the codes in the weight slot
+  // ([block][row], block-major like the global scale arrays); wave 0 loads them
+  static constexpr int S_BYTES = WF == 2 ? 2 * BROWS : 0;
+  static constexpr int S_PIECES = S_BYTES / 16;
+  static constexpr int A_SLOT = BM * ROWB, B_SLOT = BROWS * ROWB_B + S_BYTES;
   static constexpr int B_BASE = STAGES * A_SLOT;
   static constexpr int LDS = STAGES * A_SLOT + BSTAGES * B_SLOT;
   static constexpr int NW = WM * WN;
@@ -66,7 +71,7 @@ struct GemmTile {
     for (int it = 0; it < B_IT; ++it) n += (it * NT + (NW - 1) * kWave < BROWS * PPR_B);
     return n;
   }();
-  static constexpr int LPS = LPS_A + LPS_B;
+  static constexpr int LPS = LPS_A + LPS_B;           // the last wave issues no scale loads
   static_assert(LPS * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(BSTAGES == STAGES || (STAGES == 2 && BSTAGES == 3), "weight ring: same depth, or 3 with 2");
   static_assert(LDS <= 160 * 1024, "LDS per workgroup");
@@ -75,7 +80,8 @@ struct GemmTile {
   // branch-free inner loop.
   static constexpr bool SKIP_ROWS = BM != 256;
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
-  static_assert(!W8 || sizeof(T) == 2, "FP8 weights go with bf16 activations");
+  static_assert(WF == 0 || sizeof(T) == 2, "quantised weights go with bf16 activations");
+  static_assert(S_PIECES <= kWave && NW > 1, "scale pieces: one instruction per matrix on wave 0");
 };
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
@@ -134,6 +140,24 @@ __device__ __forceinline__ void issue_b(char* Bs, uint32_t kb, __amdgpu_buffer_r
   }
 }
 
+// MXFP4 scale bytes of one K step (two blocks of 32) for the tile's weight rows, by wave 0:
+// lane q carries 16 rows' bytes of one block of one matrix (gate or up), so each matrix is
+// one instruction with the other matrix's lanes masked off.
+template <typename Cfg>
+__device__ __forceinline__ void issue_s(char* Ss, uint32_t kbs, __amdgpu_buffer_rsrc_t rsS0,
+                                        __amdgpu_buffer_rsrc_t rsS1, uint32_t voffS, int wave, int lane) {
+  if constexpr (Cfg::WF_ == 2) {
+    if (wave == 0) {
+      constexpr int PPM = Cfg::BN_ / 16;                          // pieces per matrix per block
+      const int m = (lane / PPM) % Cfg::NB;
+      auto* dst = (__attribute__((address_space(3))) void*)Ss;
+      if (lane < Cfg::S_PIECES && m == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS0, dst, 16, voffS, kbs, 0, 0);
+      if (Cfg::NB == 2 && lane < Cfg::S_PIECES && m == 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS1, dst, 16, voffS, kbs, 0, 0);
+    }
+  }
+}
+
 // Per-lane 32-bit buffer offsets of one tile's global -> LDS pieces.  Lane L of a wave's
 // buffer_load_dwordx4 ... lds writes LDS bytes [base + 16 L, base + 16 L + 16), so each
 // lane loads the global piece that belongs at that swizzled LDS position.  Rows past
@@ -153,10 +177,25 @@ __device__ __forceinline__ void tile_offsets(const GemmArgs& args, int wave, int
 #pragma unroll
   for (int it = 0; it < Cfg::B_IT; ++it) {
     const int q = it * Cfg::NT + wave * kWave + lane;
-    const int r = Cfg::W8_ ? q >> 2 : q >> 3;
-    const int cl = Cfg::W8_ ? (q & 3) ^ ((r >> 1) & 3) : (q & 7) ^ ((r >> 1) & 7);
+    const int r = q / Cfg::PPR_B;
+    const int cl = Cfg::WF_ == 1 ? (q & 3) ^ ((r >> 1) & 3)
+                                 : (Cfg::WF_ == 2 ? (q & 1) ^ ((r >> 2) & 1) : (q & 7) ^ ((r >> 1) & 7));
     voffB[it] = (uint32_t)((Cfg::NB == 2 && r >= Cfg::BN_ ? r - Cfg::BN_ : r) * row_stride_b + cl * 16);
   }
+}
+
+// Eight E2M1 codes (one dword, low nibble first) times a power-of-two block scale, as eight
+// bf16 values, exactly.
+__device__ __forceinline__ u32x4_t e2m1x8_to_bf16(uint32_t v, float scale) {
+  return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3))};
+}
+
+// An E8M0 scale byte as a float: 2^(s - 127) (s = 0 is the subnormal 2^-127), 255 = NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s == 0 ? 0x00400000u : (s == 255 ? 0x7FC00000u : s << 23));
 }
 
 // Eight E4M3 codes (two dwords) as eight bf16 values, exactly (every E4M3 value is a bf16).
@@ -167,9 +206,9 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES, bool W8>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES, int WF>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, W8>;
+  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF>;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB;
   constexpr int A_IT = Cfg::A_IT, B_IT = Cfg::B_IT, BKE = Cfg::BKE;
   extern __shared__ __align__(16) char lds[];
@@ -186,7 +225,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int hi = (int)((long long)live * (xcd + 1) / kNumXcd);
   const int nks = K / BKE;
   const size_t row_stride = (size_t)K * sizeof(T);   // bytes per row of A
-  const size_t row_stride_b = W8 ? (size_t)K : row_stride;   // bytes per weight row
+  const size_t row_stride_b = WF == 1 ? (size_t)K : (WF == 2 ? (size_t)K / 2 : row_stride);   // per weight row
   constexpr uint32_t KB_B = Cfg::ROWB_B;              // weight bytes per row per K step
 
   for (int L = lo + j0; L < hi; L += bpx) {
@@ -205,6 +244,24 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     tile_offsets<Cfg>(args, wave, lane, row0, rows, row_stride, row_stride_b, voffA, voffB);
     auto a_slot = [&](int s) { return lds + s * Cfg::A_SLOT; };
     auto b_slot = [&](int s) { return lds + Cfg::B_BASE + s * Cfg::B_SLOT; };
+    // MXFP4 block scales: [G, K/32, N] bytes per matrix; lane q of wave 0 loads 16 rows of one
+    // block of one matrix (see issue_s), each step advancing two blocks
+    __amdgpu_buffer_rsrc_t rsS0 = rsB0, rsS1 = rsB1;
+    uint32_t voffS = 0;
+    if constexpr (WF == 2) {
+      const size_t gs = (size_t)g * (K / 32) * N;
+      rsS0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S0 + gs), 0, 0x7fffffff, kBufFlags);
+      rsS1 = GATED ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S1 + gs), 0, 0x7fffffff, kBufFlags)
+                   : rsS0;
+      constexpr int PPM = BN / 16;
+      const int c = lane / (NB * PPM), p = lane % PPM;
+      voffS = (uint32_t)(c * N + nt * BN + 16 * p);
+    }
+    // one K step of weights (codes, and MXFP4 scales) into weight slot s
+    auto issue_w = [&](int s, int ks) {
+      issue_b<Cfg>(b_slot(s), (uint32_t)ks * KB_B, rsB0, rsB1, voffB, wave);
+      issue_s<Cfg>(b_slot(s) + Cfg::BROWS * Cfg::ROWB_B, (uint32_t)ks * 2 * N, rsS0, rsS1, voffS, wave, lane);
+    };
 
     f32x4_t acc0[TM][TN], acc1[TM][TN];
 #pragma unroll
@@ -221,7 +278,42 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     auto compute = [&](const char* As, const char* Bs) {
       const int ra = wm * Cfg::WTM + (lane & 15);
       const int rb = wn * Cfg::WTN + (lane & 15);
-      if constexpr (W8) {
+      if constexpr (WF == 2) {
+        // MXFP4 weights: an 8-byte LDS read per weight subtile gives lane group q = lane >> 4
+        // the codes of K elements 16q .. 16q+15 of the step (rows of 32 bytes, 16-byte pieces
+        // swizzled by row quad), and one byte the scale of their block (q >> 1); the same K
+        // permutation as FP8 pairs them with A pieces 2q + h.
+        const int q = lane >> 4;
+        const char* Ss = Bs + Cfg::BROWS * Cfg::ROWB_B;
+        uint32_t raw[TN * NB][2];
+        float sc[TN * NB];
+#pragma unroll
+        for (int j = 0; j < TN * NB; ++j) {
+          const int r = (j < TN ? 0 : BN - TN * 16) + rb + j * 16;
+          const uint2 v = *(const uint2*)(Bs + r * 32 + ((((q >> 1) ^ ((r >> 2) & 1)) << 4) | ((q & 1) << 3)));
+          raw[j][0] = v.x;
+          raw[j][1] = v.y;
+          sc[j] = e8m0_to_f32(*(const uint8_t*)(Ss + (q >> 1) * Cfg::BROWS + r));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4_t b[TN * NB];
+#pragma unroll
+          for (int j = 0; j < TN * NB; ++j) b[j] = e2m1x8_to_bf16(raw[j][h], sc[j]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {
+              const u32x4_t a = *(const u32x4_t*)(As + swz(ra + i * 16, 2 * (lane >> 4) + h));
+#pragma unroll
+              for (int j = 0; j < TN; ++j) {
+                Mfma<T>::step(acc0[i][j], a, b[j]);
+                if constexpr (GATED) Mfma<T>::step(acc1[i][j], a, b[TN + j]);
+              }
+            }
+          }
+        }
+        return;
+      } else if constexpr (WF == 1) {
         // FP8 weights: one 16-byte LDS read per weight subtile gives lane group q = lane >> 4
         // the codes of K elements 16q .. 16q+15 of the step; the MFMA of half h takes
         // 16q + 8h .. 16q + 8h + 7 from both operands (the same permutation of the
@@ -293,7 +385,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       for (int p = 0; p < STAGES - 1; ++p)
         if (p < nks) {
           issue_a<Cfg>(a_slot(p), (uint32_t)p * 128, rsA, voffA, wave);
-          issue_b<Cfg>(b_slot(p), (uint32_t)p * KB_B, rsB0, rsB1, voffB, wave);
+          issue_w(p, p);
         }
       int slot = 0;
       for (int ks = 0; ks < nks; ++ks) {
@@ -302,7 +394,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         if (ks + STAGES - 1 < nks) {
           const int fs = slot == 0 ? STAGES - 1 : slot - 1;
           issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsA, voffA, wave);
-          issue_b<Cfg>(b_slot(fs), (uint32_t)(ks + STAGES - 1) * KB_B, rsB0, rsB1, voffB, wave);
+          issue_w(fs, ks + STAGES - 1);
         }
         compute(a_slot(slot), b_slot(slot));
         slot = slot + 1 == STAGES ? 0 : slot + 1;
@@ -312,8 +404,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       // step A(ks+1) B(ks+2): when step ks is consumed the only newer loads than A(ks) are
       // those of B(ks+1), so waiting until at most LPS_B are outstanding lands A(ks), B(ks).
       issue_a<Cfg>(a_slot(0), 0, rsA, voffA, wave);
-      issue_b<Cfg>(b_slot(0), 0, rsB0, rsB1, voffB, wave);
-      if (nks > 1) issue_b<Cfg>(b_slot(1), KB_B, rsB0, rsB1, voffB, wave);
+      issue_w(0, 0);
+      if (nks > 1) issue_w(1, 1);
       int bs = 0;                                       // weight slot of step ks
       for (int ks = 0; ks < nks; ++ks) {
         if (ks + 1 < nks) wait_vmcnt<Cfg::LPS_B>();
@@ -321,7 +413,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         block_barrier();                                // step ks visible; slots of ks-1 free
         if (ks + 1 < nks) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * 128, rsA, voffA, wave);
         if (ks + 2 < nks)
-          issue_b<Cfg>(b_slot(bs == 0 ? 2 : bs - 1), (uint32_t)(ks + 2) * KB_B, rsB0, rsB1, voffB, wave);
+          issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
         compute(a_slot(ks & 1), b_slot(bs));
         bs = bs == 2 ? 0 : bs + 1;
       }
@@ -335,10 +427,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 // ------------------------------------------------------------------------------ launch
 
 template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES,
-          bool W8 = false>
+          int WF = 0>
 static hipError_t launch_cfg(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
-  return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, W8>,
-                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, W8>>(a, max_tiles_m, stream);
+  return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF>,
+                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF>>(a, max_tiles_m, stream);
 }
 
 int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt) {
@@ -348,36 +440,36 @@ int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt) {
 
 // LDS ring depth of the decode tiles: FP8 weights carry half the bytes per K step, so they
 // keep more steps in flight.
-template <bool W8>
-constexpr int kDecodeStages = W8 ? 4 : 4;
+template <int WF>
+constexpr int kDecodeStages = 4;
 
-template <typename T, bool GATED, bool W8>
+template <typename T, bool GATED, int WF>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
     case kGemmLarge:
-      if constexpr (sizeof(T) == 2 && !GATED && !W8) return launch_gemm_large_bf16(a, max_tiles_m, s);
+      if constexpr (sizeof(T) == 2 && !GATED && WF == 0) return launch_gemm_large_bf16(a, max_tiles_m, s);
       // 8 waves; activations in a 2-deep ring, weights (the HBM stream) in a 3-deep one
       if constexpr (GATED) {
-        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, W8>(a, max_tiles_m, s);   // 64x(64+64) per wave
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);   // 64x(64+64) per wave
       } else {
-        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2, 3, W8>(a, max_tiles_m, s);
-        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, W8>(a, max_tiles_m, s);
+        if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);
+        return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);
       }
     case kGemmStream:
       // weight streaming with ~100-250 rows per expert: wide weight tiles, 3-deep ring so
       // two K steps of weights are in flight per CU
       if constexpr (GATED) {
-        return launch_cfg<T, 160, 128, 2, 4, GATED, 3, 3, W8>(a, max_tiles_m, s);   // 80x(32+32) per wave
+        return launch_cfg<T, 160, 128, 2, 4, GATED, 3, 3, WF>(a, max_tiles_m, s);   // 80x(32+32) per wave
       } else {
-        if (a.N % 256 == 0) return launch_cfg<T, 160, 256, 2, 4, GATED, 3, 3, W8>(a, max_tiles_m, s);
-        return launch_cfg<T, 160, 128, 2, 4, GATED, 3, 3, W8>(a, max_tiles_m, s);
+        if (a.N % 256 == 0) return launch_cfg<T, 160, 256, 2, 4, GATED, 3, 3, WF>(a, max_tiles_m, s);
+        return launch_cfg<T, 160, 128, 2, 4, GATED, 3, 3, WF>(a, max_tiles_m, s);
       }
     default:
       // decode: a few rows per expert, 4-deep ring; the down product has half the weight
       // rows of gate/up, so narrower tiles give it as many blocks streaming in parallel
-      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, kDecodeStages<W8>, kDecodeStages<W8>, W8>(
+      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(
           a, max_tiles_m, s);
-      else return launch_cfg<T, 16, 32, 1, 2, GATED, kDecodeStages<W8>, kDecodeStages<W8>, W8>(a, max_tiles_m, s);
+      else return launch_cfg<T, 16, 32, 1, 2, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(a, max_tiles_m, s);
   }
 }
 
@@ -386,20 +478,24 @@ hipError_t launch_gemm_gateup(GemmKind kind, int dtype, int wfmt, const void* A,
                               const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
                               int N, int K, void* H, hipStream_t stream) {
   GemmArgs a{A, a_rows, Wg, Wu, Sg, Su, offsets, tstart, G, dense_rows, N, K, H};
-  if (dtype == 1)
-    return wfmt == 1 ? dispatch_kind<uint16_t, true, true>(kind, a, max_tiles_m, stream)
-                     : dispatch_kind<uint16_t, true, false>(kind, a, max_tiles_m, stream);
-  return dispatch_kind<float, true, false>(kind, a, max_tiles_m, stream);
+  if (dtype == 1) {
+    if (wfmt == 1) return dispatch_kind<uint16_t, true, 1>(kind, a, max_tiles_m, stream);
+    if (wfmt == 2) return dispatch_kind<uint16_t, true, 2>(kind, a, max_tiles_m, stream);
+    return dispatch_kind<uint16_t, true, 0>(kind, a, max_tiles_m, stream);
+  }
+  return dispatch_kind<float, true, 0>(kind, a, max_tiles_m, stream);
 }
 
 hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, const void* Wd, const float* Sd,
                             const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
                             int N, int K, float* O, hipStream_t stream) {
   GemmArgs a{H, nullptr, Wd, nullptr, Sd, nullptr, offsets, tstart, G, dense_rows, N, K, O};
-  if (dtype == 1)
-    return wfmt == 1 ? dispatch_kind<uint16_t, false, true>(kind, a, max_tiles_m, stream)
-                     : dispatch_kind<uint16_t, false, false>(kind, a, max_tiles_m, stream);
-  return dispatch_kind<float, false, false>(kind, a, max_tiles_m, stream);
+  if (dtype == 1) {
+    if (wfmt == 1) return dispatch_kind<uint16_t, false, 1>(kind, a, max_tiles_m, stream);
+    if (wfmt == 2) return dispatch_kind<uint16_t, false, 2>(kind, a, max_tiles_m, stream);
+    return dispatch_kind<uint16_t, false, 0>(kind, a, max_tiles_m, stream);
+  }
+  return dispatch_kind<float, false, 0>(kind, a, max_tiles_m, stream);
 }
 
 }  // namespace moe

@@ -17,7 +17,7 @@ namespace moe {
 template <typename T, int BN, bool GATED>
 struct LargeTile {
   using Elem = T;
-  static constexpr bool W8_ = false;
+  static constexpr int WF_ = 0;
   static constexpr int NT = 256, WM = 2, WN = 2;
   static constexpr int BM_ = kLargeBf16BlockM, BN_ = BN, NB = GATED ? 2 : 1, BROWS = BN * NB;
   static constexpr int WTM = BM_ / WM, WTN = BN / WN;

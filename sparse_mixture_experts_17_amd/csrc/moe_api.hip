@@ -58,8 +58,8 @@ moe_status check_shape(const moe_shape* s) {
   if (s->n_group < 1 || s->topk_group < 1 || s->topk_group > s->n_group || s->E % s->n_group != 0)
     return MOE_ERR_SHAPE;
   if ((long long)s->k > (long long)s->topk_group * (s->E / s->n_group)) return MOE_ERR_SHAPE;
-  if (s->wfmt != MOE_W_NATIVE && s->wfmt != MOE_W_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
-  if (s->wfmt == MOE_W_FP8_E4M3 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->wfmt != MOE_W_NATIVE && s->wfmt != MOE_W_FP8_E4M3 && s->wfmt != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (s->wfmt != MOE_W_NATIVE && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (s->n_group > 64) return MOE_ERR_UNSUPPORTED;
   if (s->E > 1024 || s->k > 16) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 || s->d_e % 128 || s->d_e_shared % 128) return MOE_ERR_UNSUPPORTED;
@@ -118,17 +118,17 @@ moe_status run_router(const moe_shape& s, const void* x, const void* w_r, const 
 const moe_wscales kNoScales = {nullptr, nullptr, nullptr};
 
 bool scales_ok(const moe_shape& s, const moe_wscales* sc) {
-  return s.wfmt != MOE_W_FP8_E4M3 || (sc && sc->gate && sc->up && sc->down);
+  return s.wfmt == MOE_W_NATIVE || (sc && sc->gate && sc->up && sc->down);
 }
 
 moe_status run_ffn(const moe_shape& s, int G, const void* A, const int32_t* offsets, const int32_t* tstart1,
                    const int32_t* tstart2, GemmKind kind, int tiles1, int tiles2, int dense_rows, int d_e,
                    const void* wg, const void* wu, const void* wd, const moe_wscales& sc, void* h, float* o,
                    hipStream_t st) {
-  MOE_HIP(launch_gemm_gateup(kind, s.dtype, s.wfmt, A, nullptr, wg, wu, sc.gate, sc.up, offsets, tstart1, G,
-                             dense_rows, tiles1, d_e, s.d, h, st));
-  MOE_HIP(launch_gemm_down(kind, s.dtype, s.wfmt, h, wd, sc.down, offsets, tstart2, G, dense_rows, tiles2, s.d, d_e,
-                           o, st));
+  MOE_HIP(launch_gemm_gateup(kind, s.dtype, s.wfmt, A, nullptr, wg, wu, (const float*)sc.gate, (const float*)sc.up,
+                             offsets, tstart1, G, dense_rows, tiles1, d_e, s.d, h, st));
+  MOE_HIP(launch_gemm_down(kind, s.dtype, s.wfmt, h, wd, (const float*)sc.down, offsets, tstart2, G, dense_rows,
+                           tiles2, s.d, d_e, o, st));
   return MOE_OK;
 }
 
@@ -217,7 +217,7 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int3
   int32_t* ts2 = at<int32_t>(ws, L.tstart2);
   MOE_HIP(launch_tile_sched(offsets, s.E, bm1, ts1, bm2, ts2, st));
   return run_ffn(s, s.E, x_perm, offsets, ts1, ts2, kind, max_m_tiles(R, s.E, -1, bm1), max_m_tiles(R, s.E, -1, bm2),
-                 0, s.d_e, w_gate, w_up, w_down, s.wfmt == MOE_W_FP8_E4M3 ? *scales : kNoScales, at<void>(ws, L.h), o,
+                 0, s.d_e, w_gate, w_up, w_down, s.wfmt != MOE_W_NATIVE ? *scales : kNoScales, at<void>(ws, L.h), o,
                  st);
 }
 
@@ -246,7 +246,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
     return MOE_ERR_NULL;
   if (s.d_e_shared > 0 && s.T > 0 && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_NULL;
   if (s.T > 0 && (!scales_ok(s, scales) || (s.d_e_shared > 0 && !scales_ok(s, shared_scales)))) return MOE_ERR_NULL;
-  const bool w8 = s.wfmt == MOE_W_FP8_E4M3;
+  const bool w8 = s.wfmt != MOE_W_NATIVE;
   const moe_wscales& sc = w8 && s.T > 0 ? *scales : kNoScales;
   const moe_wscales& ssc = w8 && s.T > 0 && s.d_e_shared > 0 ? *shared_scales : kNoScales;
   const Layout L = layout(s);
@@ -288,10 +288,11 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
                                offsets, row_token, row_of, nullptr, st));
   MOE_MARK(MOE_STAGE_GATE_UP);
   if (s.T > 0) {
-    MOE_HIP(launch_gemm_gateup(kind, s.dtype, s.wfmt, x, row_token, w_gate, w_up, sc.gate, sc.up, offsets, ts1, s.E,
-                               0, max_m_tiles(R, s.E, s.capacity, bm1), s.d_e, s.d, at<void>(ws, L.h), st));
+    MOE_HIP(launch_gemm_gateup(kind, s.dtype, s.wfmt, x, row_token, w_gate, w_up, (const float*)sc.gate,
+                               (const float*)sc.up, offsets, ts1, s.E, 0, max_m_tiles(R, s.E, s.capacity, bm1), s.d_e,
+                               s.d, at<void>(ws, L.h), st));
     MOE_MARK(MOE_STAGE_DOWN);
-    MOE_HIP(launch_gemm_down(kind, s.dtype, s.wfmt, at<void>(ws, L.h), w_down, sc.down, offsets, ts2, s.E, 0,
+    MOE_HIP(launch_gemm_down(kind, s.dtype, s.wfmt, at<void>(ws, L.h), w_down, (const float*)sc.down, offsets, ts2, s.E, 0,
                              max_m_tiles(R, s.E, s.capacity, bm2), s.d, s.d_e, at<float>(ws, L.o), st));
   }
   MOE_MARK(MOE_STAGE_SHARED_GATE_UP);
@@ -299,10 +300,12 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   if (s.d_e_shared > 0 && s.T > 0) {
     const GemmKind sk = choose_kind(s.T, 1, -1);
     const int sbm1 = gemm_block_m(sk, s.dtype, true, s.wfmt), sbm2 = gemm_block_m(sk, s.dtype, false, s.wfmt);
-    MOE_HIP(launch_gemm_gateup(sk, s.dtype, s.wfmt, x, nullptr, ws_gate, ws_up, ssc.gate, ssc.up, nullptr, nullptr, 1,
+    MOE_HIP(launch_gemm_gateup(sk, s.dtype, s.wfmt, x, nullptr, ws_gate, ws_up, (const float*)ssc.gate,
+                               (const float*)ssc.up, nullptr, nullptr, 1,
                                s.T, (s.T + sbm1 - 1) / sbm1, s.d_e_shared, s.d, at<void>(ws, L.sh_h), st));
     MOE_MARK(MOE_STAGE_SHARED_DOWN);
-    MOE_HIP(launch_gemm_down(sk, s.dtype, s.wfmt, at<void>(ws, L.sh_h), ws_down, ssc.down, nullptr, nullptr, 1, s.T,
+    MOE_HIP(launch_gemm_down(sk, s.dtype, s.wfmt, at<void>(ws, L.sh_h), ws_down, (const float*)ssc.down, nullptr,
+                             nullptr, 1, s.T,
                              (s.T + sbm2 - 1) / sbm2, s.d, s.d_e_shared, at<float>(ws, L.sh_o), st));
     shared_out = at<float>(ws, L.sh_o);
   }

@@ -89,7 +89,7 @@ def moe_permute(shape, x, idx, kept, offsets, row_token, row_of, x_perm, ws, str
 
 
 def moe_expert_ffn(shape, x_perm, offsets, w_gate, w_up, w_down, scales, o, ws, stream=None) -> None:
-    """scales: None, or the (gate, up, down) row-scale tensors of FP8 weights."""
+    """scales: None, or the (gate, up, down) scale tensors of quantised weights."""
     check("moe_expert_ffn", lib().moe_expert_ffn(C.byref(shape), _ptr(x_perm), _ptr(offsets), _ptr(w_gate),
                                                  _ptr(w_up), _ptr(w_down), _scales(scales), _ptr(o), _ptr(ws),
                                                  _nbytes(ws), _stream(stream)))

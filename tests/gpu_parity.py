@@ -38,7 +38,15 @@ def shape_of(w: wl.Workload, T=None):
     return moe.make_shape(w.T if T is None else T, w.d, w.d_e, w.E, w.k, capacity=cap, renormalize=w.renormalize,
                           d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32,
                           scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group,
-                          topk_group=w.topk_group, wfmt=moe.MOE_W_FP8_E4M3 if w.weights == "fp8_e4m3" else 0), cap
+                          topk_group=w.topk_group, wfmt=WFMT[w.weights]), cap
+
+
+WFMT = {"native": 0, "fp8_e4m3": 1, "mxfp4": 2}
+
+
+def dequant(q, sc, weights):
+    """Float64 weights from quantised storage, decoded by the oracle."""
+    return mo.dequantize_rows(q, sc) if weights == "fp8_e4m3" else mo.dequantize_mx_rows(q, sc)
 
 
 def router_kw(w: wl.Workload) -> dict:
@@ -54,17 +62,17 @@ def f64(a, w):
 
 
 def expert_f64(inp, e):
-    """Float64 weights of routed expert e as the GPU sees them (FP8 codes decoded by the
-    oracle and scaled per row)."""
-    if inp.wl.weights == "fp8_e4m3":
-        return tuple(mo.dequantize_rows(q, sc) for q, sc in inp.expert_q(e))
+    """Float64 weights of routed expert e as the GPU sees them (quantised codes decoded and
+    scaled by the oracle)."""
+    if inp.wl.weights != "native":
+        return tuple(dequant(q, sc, inp.wl.weights) for q, sc in inp.expert_q(e))
     return tuple(f64(m, inp.wl) for m in inp.expert(e))
 
 
 def shared_f64(inp):
-    if inp.wl.weights == "fp8_e4m3":
+    if inp.wl.weights != "native":
         sq = inp.shared_q()
-        return None if sq is None else tuple(mo.dequantize_rows(q, sc) for q, sc in sq)
+        return None if sq is None else tuple(dequant(q, sc, inp.wl.weights) for q, sc in sq)
     sh = inp.shared()
     return None if sh is None else tuple(f64(m, inp.wl) for m in sh)
 

@@ -54,7 +54,8 @@ def _shape(**kw):
     (dict(scoring=2), 3), (dict(scoring=-1), 3), (dict(n_group=0), 2), (dict(n_group=3), 2),
     (dict(n_group=4, topk_group=0), 2), (dict(n_group=4, topk_group=5), 2),
     (dict(n_group=8, topk_group=1, k=2), 2), (dict(E=256, n_group=128, topk_group=2), 3),
-    (dict(wfmt=2), 3), (dict(wfmt=-1), 3), (dict(wfmt=1, dtype=moe.MOE_F32), 3),
+    (dict(wfmt=3), 3), (dict(wfmt=-1), 3), (dict(wfmt=1, dtype=moe.MOE_F32), 3),
+    (dict(wfmt=2, dtype=moe.MOE_F32), 3),
 ])
 def test_shape_validation(kw, status):
     n = C.c_size_t()
@@ -154,10 +155,11 @@ def test_device_calls_reject_null_and_small_workspace():
     assert lib.moe_route(None, *_args(9), FAKE, 1 << 40, None) == 1
 
 
-def test_fp8_weights_need_scales():
-    """FP8 weights: every row-scale pointer is required; native weights ignore them."""
+@pytest.mark.parametrize("wfmt", [1, 2])
+def test_quantised_weights_need_scales(wfmt):
+    """FP8 / MXFP4 weights: every scale pointer is required; native weights ignore them."""
     lib = _lib.lib()
-    s = _shape(wfmt=moe.MOE_W_FP8_E4M3, dtype=moe.MOE_BF16)
+    s = _shape(wfmt=wfmt, dtype=moe.MOE_BF16)
     assert moe.moe_workspace_bytes(s) > 0
     ws_need = moe.moe_workspace_bytes(s)
     a = _args(7)
@@ -173,7 +175,7 @@ def test_fp8_weights_need_scales():
         f[i] = None
     assert _fwd(lib, s, f, ws_need) == 1
     assert _fwd(lib, s, f, 10, C.byref(full)) == 4
-    s2 = _shape(wfmt=moe.MOE_W_FP8_E4M3, dtype=moe.MOE_BF16, d_e_shared=256)
+    s2 = _shape(wfmt=wfmt, dtype=moe.MOE_BF16, d_e_shared=256)
     f2 = list(f)
     f2[6] = f2[7] = f2[8] = FAKE
     assert _fwd(lib, s2, f2, 10, C.byref(full)) == 1                      # shared scales missing

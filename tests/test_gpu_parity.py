@@ -57,6 +57,12 @@ SMALL = [
               d_e_shared=256),
     wl.scaled(BASE["deepseek_v3_fp8"], name="fp8_shared_large", T=1100, d=256, d_e=128, E=32, k=4, d_e_shared=384,
               capacity_factor=1.0),
+    # MXFP4 expert weights in every tile configuration
+    wl.scaled(BASE["mixtral_decode_mxfp4"], name="mxfp4_decode_tiles", T=16, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_decode_mxfp4"], name="mxfp4_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_large_d384", T=1600, d=384, d_e=256, E=4, k=2),
+    wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_shared", T=300, d=512, d_e=256, E=64, k=6, d_e_shared=256),
 ]
 
 
@@ -67,7 +73,7 @@ def test_forward_small(w):
 
 
 FULL = ["tiny_fp32", "switch_capacity", "mixtral_decode", "mixtral_prefill", "deepseek_v3", "deepseek_v3_grouped",
-        "mixtral_decode_fp8", "mixtral_prefill_fp8", "deepseek_v3_fp8"]
+        "mixtral_decode_fp8", "mixtral_prefill_fp8", "deepseek_v3_fp8", "mixtral_decode_mxfp4", "mixtral_prefill_mxfp4"]
 
 
 @needs_gpu
@@ -91,10 +97,10 @@ def _upload_i32(a):
 
 
 @needs_gpu
-@pytest.mark.parametrize("variant", ["softmax", "sigmoid_grouped", "fp8_weights"])
+@pytest.mark.parametrize("variant", ["softmax", "sigmoid_grouped", "fp8_weights", "mxfp4_weights"])
 def test_split_calls_compose(variant):
     """moe_route -> moe_permute -> moe_expert_ffn (+ shared) -> moe_combine equals moe_forward."""
-    extra = {"softmax": {}, "fp8_weights": dict(weights="fp8_e4m3"),
+    extra = {"softmax": {}, "fp8_weights": dict(weights="fp8_e4m3"), "mxfp4_weights": dict(weights="mxfp4"),
              "sigmoid_grouped": dict(scoring="sigmoid", n_group=4, topk_group=2, router_bias_var=1e-3)}[variant]
     w = wl.scaled(BASE["deepseek_v3"], name="split", T=211, d=256, d_e=128, E=16, k=3, d_e_shared=256,
                   capacity_factor=1.1, **extra)
@@ -171,6 +177,8 @@ def test_expert_ffn_given_rows():
                     (wl.scaled(BASE["mixtral_prefill"], name="ffnbf", T=1300, d=256, d_e=512, E=3, k=1),
                      [600, 0, 700]),
                     (wl.scaled(BASE["mixtral_prefill_fp8"], name="ffn_fp8", T=1300, d=256, d_e=512, E=3, k=1),
+                     [600, 0, 700]),
+                    (wl.scaled(BASE["mixtral_prefill_mxfp4"], name="ffn_mxfp4", T=1300, d=256, d_e=512, E=3, k=1),
                      [600, 0, 700])]:
         inp = wl.make_inputs(w)
         dev = upload(inp)

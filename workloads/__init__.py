@@ -59,7 +59,8 @@ class Workload:
     scoring: str = "softmax"   # "softmax", or "sigmoid" (the bias then only steers selection)
     n_group: int = 1           # expert groups for group-limited routing
     topk_group: int = 1        # groups a token may use
-    weights: str = "native"    # expert weights: "native" (dtype), or "fp8_e4m3" (codes + row scales)
+    weights: str = "native"    # expert weights: "native" (dtype), "fp8_e4m3" (codes + row scales) or
+                               # "mxfp4" (E2M1 codes + E8M0 scales per 32 along the row)
     note: str = ""
 
 
@@ -87,6 +88,10 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
     Workload("deepseek_v3_fp8", T=4096, d=7168, d_e=2048, E=256, k=8, dtype="bf16", d_e_shared=2048,
              weights="fp8_e4m3",
              note="DeepSeek-V3-shaped layer with FP8 E4M3 routed and shared expert weights"),
+    Workload("mixtral_decode_mxfp4", T=16, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="mxfp4",
+             note="Mixtral decode batch with MXFP4 expert weights (4-bit E2M1, E8M0 scale per 32)"),
+    Workload("mixtral_prefill_mxfp4", T=4096, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="mxfp4",
+             note="Mixtral prefill batch with MXFP4 expert weights"),
 ]}
 
 
@@ -135,6 +140,39 @@ def quantize_e4m3_rows(w: np.ndarray):
     return q.view(torch.uint8).numpy().copy(), scale.numpy().copy()
 
 
+def quantize_mxfp4_rows(w: np.ndarray, block: int = 32):
+    """MXFP4 storage of a float32 weight matrix [n, k] (k a multiple of `block`).
+
+    Checkpoint preparation, not part of the layer, following the OCP MX recipe: each block of
+    32 consecutive elements of a row shares the E8M0 scale 2^(floor(log2 amax) - 2) (2 is the
+    largest E2M1 exponent); elements divided by it go to the nearest E2M1 magnitude (ties to
+    the even code), saturating at 6.  Returns (packed [n, k/2] uint8: element 2j in the low
+    nibble of byte j; scales [k/block, n] uint8, block-major).
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    wb = w.reshape(n, k // block, block)
+    amax = np.abs(wb).max(axis=2)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.floor(np.log2(np.maximum(amax, 1e-38))) - 2, -127)
+    code = np.clip(ex + 127, 0, 254).astype(np.int64)
+    scale = np.exp2(code - 127.0).astype(np.float32)
+    x = np.abs(wb) / scale[:, :, None]
+    # nearest E2M1 code, ties to the even code: the grid is uniform on [0, 2) (step 0.5,
+    # codes 0-4), [2, 4) (step 1, codes 4-6) and [4, 6] (step 2, codes 6-7); rint rounds
+    # half to even, which is the even code on every piece
+    m = np.where(x < 2.0, np.rint(x * 2.0), np.where(x < 4.0, 4.0 + np.rint(x - 2.0), 6.0 + np.rint((x - 4.0) / 2.0)))
+    m = np.minimum(m, 7).astype(np.int64)
+    codes = (m | np.where(wb < 0, 8, 0)).astype(np.uint8).reshape(n, k)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, np.ascontiguousarray(code.T.astype(np.uint8))
+
+
+def quantize_rows(w: np.ndarray, weights: str):
+    """(codes, scales) of a float32 matrix in the workload's weight format."""
+    return quantize_e4m3_rows(w) if weights == "fp8_e4m3" else quantize_mxfp4_rows(w)
+
+
 # --------------------------------------------------------------------------- drawing
 
 def _draw(seed: int, key: tuple, shape, var: float, dtype: str) -> np.ndarray:
@@ -173,24 +211,24 @@ class Inputs:
         )
 
     def expert_q(self, e: int):
-        """FP8 workloads: ((codes, scale) of W_g, of W_u, of W_d) of routed expert e, from
-        the same float32 draws as ``expert``."""
+        """Quantised workloads: ((codes, scales) of W_g, of W_u, of W_d) of routed expert e,
+        from the same float32 draws as ``expert``."""
         wl = self.wl
         return (
-            quantize_e4m3_rows(_draw(self.seed, (3, e, 0), (wl.d_e, wl.d), 1.0 / wl.d, "f32")),
-            quantize_e4m3_rows(_draw(self.seed, (3, e, 1), (wl.d_e, wl.d), 1.0 / wl.d, "f32")),
-            quantize_e4m3_rows(_draw(self.seed, (3, e, 2), (wl.d, wl.d_e), 1.0 / wl.d_e, "f32")),
+            quantize_rows(_draw(self.seed, (3, e, 0), (wl.d_e, wl.d), 1.0 / wl.d, "f32"), wl.weights),
+            quantize_rows(_draw(self.seed, (3, e, 1), (wl.d_e, wl.d), 1.0 / wl.d, "f32"), wl.weights),
+            quantize_rows(_draw(self.seed, (3, e, 2), (wl.d, wl.d_e), 1.0 / wl.d_e, "f32"), wl.weights),
         )
 
     def shared_q(self):
-        """FP8 workloads: the shared expert's ((codes, scale) x 3), or None."""
+        """Quantised workloads: the shared expert's ((codes, scales) x 3), or None."""
         wl = self.wl
         if wl.d_e_shared <= 0:
             return None
         return (
-            quantize_e4m3_rows(_draw(self.seed, (4, 0), (wl.d_e_shared, wl.d), 1.0 / wl.d, "f32")),
-            quantize_e4m3_rows(_draw(self.seed, (4, 1), (wl.d_e_shared, wl.d), 1.0 / wl.d, "f32")),
-            quantize_e4m3_rows(_draw(self.seed, (4, 2), (wl.d, wl.d_e_shared), 1.0 / wl.d_e_shared, "f32")),
+            quantize_rows(_draw(self.seed, (4, 0), (wl.d_e_shared, wl.d), 1.0 / wl.d, "f32"), wl.weights),
+            quantize_rows(_draw(self.seed, (4, 1), (wl.d_e_shared, wl.d), 1.0 / wl.d, "f32"), wl.weights),
+            quantize_rows(_draw(self.seed, (4, 2), (wl.d, wl.d_e_shared), 1.0 / wl.d_e_shared, "f32"), wl.weights),
         )
 
     def shared(self):

@@ -32,19 +32,29 @@ class DeviceInputs:
     w_up: torch.Tensor       # [E, d_e, d]
     w_down: torch.Tensor     # [E, d, d_e]
     shared: tuple | None     # (W_g, W_u, W_d) or None
-    scales: tuple | None = None         # FP8 weights: (gate [E,d_e], up [E,d_e], down [E,d]) fp32
-    shared_scales: tuple | None = None  # FP8 shared expert: (gate [1,d_e_s], up, down [1,d])
+    scales: tuple | None = None         # FP8: (gate [E,d_e], up [E,d_e], down [E,d]) fp32;
+                                        # MXFP4: (gate [E,d/32,d_e], up, down [E,d_e/32,d]) uint8
+    shared_scales: tuple | None = None  # the shared expert's, with a leading 1
 
 
-def _upload_fp8(inp: Inputs, device, threads) -> DeviceInputs:
+def _upload_quant(inp: Inputs, device, threads) -> DeviceInputs:
+    """Quantised expert weights: codes and scales as the workload stores them."""
     wl = inp.wl
     u8, f32 = torch.uint8, torch.float32
-    wg = torch.empty((wl.E, wl.d_e, wl.d), dtype=u8, device=device)
-    wu = torch.empty((wl.E, wl.d_e, wl.d), dtype=u8, device=device)
-    wd = torch.empty((wl.E, wl.d, wl.d_e), dtype=u8, device=device)
-    sg = torch.empty((wl.E, wl.d_e), dtype=f32, device=device)
-    su = torch.empty((wl.E, wl.d_e), dtype=f32, device=device)
-    sd = torch.empty((wl.E, wl.d), dtype=f32, device=device)
+    if wl.weights == "fp8_e4m3":
+        wg = torch.empty((wl.E, wl.d_e, wl.d), dtype=u8, device=device)
+        wu = torch.empty((wl.E, wl.d_e, wl.d), dtype=u8, device=device)
+        wd = torch.empty((wl.E, wl.d, wl.d_e), dtype=u8, device=device)
+        sg = torch.empty((wl.E, wl.d_e), dtype=f32, device=device)
+        su = torch.empty((wl.E, wl.d_e), dtype=f32, device=device)
+        sd = torch.empty((wl.E, wl.d), dtype=f32, device=device)
+    else:                                    # mxfp4: two codes per byte, E8M0 scales block-major
+        wg = torch.empty((wl.E, wl.d_e, wl.d // 2), dtype=u8, device=device)
+        wu = torch.empty((wl.E, wl.d_e, wl.d // 2), dtype=u8, device=device)
+        wd = torch.empty((wl.E, wl.d, wl.d_e // 2), dtype=u8, device=device)
+        sg = torch.empty((wl.E, wl.d // 32, wl.d_e), dtype=u8, device=device)
+        su = torch.empty((wl.E, wl.d // 32, wl.d_e), dtype=u8, device=device)
+        sd = torch.empty((wl.E, wl.d_e // 32, wl.d), dtype=u8, device=device)
     with cf.ThreadPoolExecutor(max_workers=threads or _threads()) as ex:
         futs = [ex.submit(inp.expert_q, e) for e in range(wl.E)]
         for e, fu in enumerate(futs):
@@ -56,7 +66,7 @@ def _upload_fp8(inp: Inputs, device, threads) -> DeviceInputs:
     sq = inp.shared_q()
     if sq is not None:
         shared = tuple(torch.from_numpy(q).to(device) for q, _ in sq)
-        shared_scales = tuple(torch.from_numpy(sc).reshape(1, -1).to(device) for _, sc in sq)
+        shared_scales = tuple(torch.from_numpy(sc).unsqueeze(0).to(device) for _, sc in sq)
     b_r = None if inp.b_r is None else torch.from_numpy(inp.b_r).to(device)
     return DeviceInputs(_to_dev(inp.x, wl.dtype, device), _to_dev(inp.w_r, wl.dtype, device), b_r,
                         wg, wu, wd, shared, (sg, su, sd), shared_scales)
@@ -64,8 +74,8 @@ def _upload_fp8(inp: Inputs, device, threads) -> DeviceInputs:
 
 def upload(inp: Inputs, device="cuda", threads: int | None = None) -> DeviceInputs:
     wl = inp.wl
-    if wl.weights == "fp8_e4m3":
-        return _upload_fp8(inp, device, threads)
+    if wl.weights != "native":
+        return _upload_quant(inp, device, threads)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     wg = torch.empty((wl.E, wl.d_e, wl.d), dtype=tdt, device=device)
     wu = torch.empty((wl.E, wl.d_e, wl.d), dtype=tdt, device=device)
