@@ -48,30 +48,28 @@ struct GemmTile {
   static constexpr int BKE = 8 * EPP;                               // elements of K per stage
   static constexpr int PPR_B = WF == 1 ? 4 : (WF == 2 ? 2 : 8);    // 16-byte weight pieces per row per step
   static constexpr int ROWB_B = PPR_B * 16;
-  static constexpr int A_IT = (BM * 8 + NT - 1) / NT;
-  static constexpr int B_IT = (BROWS * PPR_B + NT - 1) / NT;
   // LDS: a ring of STAGES activation slots, then a ring of BSTAGES weight slots
   // MXFP4: each step's two E8M0 scale bytes per weight row follow the codes in the weight slot
-  // ([block][row], block-major like the global scale arrays); wave 0 loads them
+  // ([block][row], block-major like the global scale arrays)
   static constexpr int S_BYTES = WF == 2 ? 2 * BROWS : 0;
-  static constexpr int S_PIECES = S_BYTES / 16;
   static constexpr int A_SLOT = BM * ROWB, B_SLOT = BROWS * ROWB_B + S_BYTES;
   static constexpr int B_BASE = STAGES * A_SLOT;
   static constexpr int LDS = STAGES * A_SLOT + BSTAGES * B_SLOT;
   static constexpr int NW = WM * WN;
-  // buffer loads per K step issued by the wave with the fewest (the last one); waiting
-  // until at most LPS * n are outstanding leaves n newer steps in flight
-  static constexpr int LPS_A = [] {
-    int n = 0;
-    for (int it = 0; it < A_IT; ++it) n += (it * NT + (NW - 1) * kWave < BM * 8);
-    return n;
-  }();
-  static constexpr int LPS_B = [] {
-    int n = 0;
-    for (int it = 0; it < B_IT; ++it) n += (it * NT + (NW - 1) * kWave < BROWS * PPR_B);
-    return n;
-  }();
-  static constexpr int LPS = LPS_A + LPS_B;           // the last wave issues no scale loads
+  // 16-byte global -> LDS pieces per K step: activations, weights, MXFP4 scales.  Each wave
+  // loads a contiguous equal share of every kind (PW_* pieces, IT_* instructions of up to 64
+  // lanes), so every wave issues exactly LPS loads per step and "at most LPS * n outstanding"
+  // leaves exactly n newer steps in flight for every wave.
+  static constexpr int P_A = BM * 8, P_B = BROWS * PPR_B, P_S = S_BYTES / 16;
+  static constexpr int PW_A = P_A / NW, PW_B = P_B / NW, PW_S = P_S / NW;
+  static constexpr int IT_A = (PW_A + kWave - 1) / kWave, IT_B = (PW_B + kWave - 1) / kWave;
+  static constexpr int IT_S = P_S ? 1 : 0;
+  static constexpr int LPS_B = IT_B + IT_S;
+  static constexpr int LPS = IT_A + LPS_B;
+  static constexpr int A_IT = IT_A, B_IT = IT_B;
+  static_assert(P_A % NW == 0 && P_B % NW == 0 && P_S % NW == 0, "equal shares per wave");
+  static_assert(NW % 2 == 0, "gate and up halves of the weight pieces split on a wave boundary");
+  static_assert(P_S == 0 || (PW_S <= kWave && (BN / 16) % PW_S == 0), "a wave's scale share is one matrix");
   static_assert(LPS * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(BSTAGES == STAGES || (STAGES == 2 && BSTAGES == 3), "weight ring: same depth, or 3 with 2");
   static_assert(LDS <= 160 * 1024, "LDS per workgroup");
@@ -81,7 +79,7 @@ struct GemmTile {
   static constexpr bool SKIP_ROWS = BM != 256;
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
   static_assert(WF == 0 || sizeof(T) == 2, "quantised weights go with bf16 activations");
-  static_assert(S_PIECES <= kWave && NW > 1, "scale pieces: one instruction per matrix on wave 0");
+
 };
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
@@ -106,15 +104,16 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 }
 
 // Enqueue one K step of the A (activation) or B (weight) tile into an LDS slot
-// (asynchronous; completion is tracked by vmcnt).  Wave-uniform branches only.
+// (asynchronous; completion is tracked by vmcnt).  Wave w loads pieces [w PW, (w+1) PW) of
+// each kind, 64 per instruction (lane L writes LDS bytes 16 L .. 16 L + 15 past the
+// instruction's base); lanes past the share are masked off.
 template <typename Cfg>
 __device__ __forceinline__ void issue_a(char* As, uint32_t kb, __amdgpu_buffer_rsrc_t rsA, const uint32_t* voffA,
-                                        int wave) {
-  constexpr int NT = Cfg::NT;
+                                        int wave, int lane) {
 #pragma unroll
-  for (int it = 0; it < Cfg::A_IT; ++it) {
-    const int q0 = it * NT + wave * kWave;
-    if (Cfg::A_IT * NT == Cfg::BM_ * 8 || q0 < Cfg::BM_ * 8)
+  for (int it = 0; it < Cfg::IT_A; ++it) {
+    const int q0 = wave * Cfg::PW_A + it * kWave;
+    if (Cfg::PW_A % kWave == 0 || it * kWave + lane < Cfg::PW_A)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (__attribute__((address_space(3))) void*)(As + q0 * 16), 16,
                                                voffA[it], kb, 0, 0);
   }
@@ -122,16 +121,14 @@ __device__ __forceinline__ void issue_a(char* As, uint32_t kb, __amdgpu_buffer_r
 
 template <typename Cfg>
 __device__ __forceinline__ void issue_b(char* Bs, uint32_t kb, __amdgpu_buffer_rsrc_t rsB0,
-                                        __amdgpu_buffer_rsrc_t rsB1, const uint32_t* voffB, int wave) {
-  constexpr int NT = Cfg::NT, PPR = Cfg::PPR_B, RPI = NT / PPR;   // rows covered by one load of every wave
+                                        __amdgpu_buffer_rsrc_t rsB1, const uint32_t* voffB, int wave, int lane) {
+  // the up rows of the gated product are the second half of the pieces: whole waves
+  const bool up = Cfg::NB == 2 && wave >= Cfg::NW / 2;
 #pragma unroll
-  for (int it = 0; it < Cfg::B_IT; ++it) {
-    const int q0 = it * NT + wave * kWave;
-    if (Cfg::B_IT * NT == Cfg::BROWS * PPR || q0 < Cfg::BROWS * PPR) {
-      auto* dst = (__attribute__((address_space(3))) void*)(Bs + q0 * 16);
-      // up rows of the gated product: decided per unrolled step when the gate/up split
-      // falls on a step boundary
-      const bool up = Cfg::NB == 2 && (Cfg::BN_ % RPI == 0 ? it * RPI >= Cfg::BN_ : q0 / PPR >= Cfg::BN_);
+  for (int it = 0; it < Cfg::IT_B; ++it) {
+    const int q0 = wave * Cfg::PW_B + it * kWave;
+    auto* dst = (__attribute__((address_space(3))) void*)(Bs + q0 * 16);
+    if (Cfg::PW_B % kWave == 0 || it * kWave + lane < Cfg::PW_B) {
       if (up)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, voffB[it], kb, 0, 0);
       else
@@ -140,20 +137,21 @@ __device__ __forceinline__ void issue_b(char* Bs, uint32_t kb, __amdgpu_buffer_r
   }
 }
 
-// MXFP4 scale bytes of one K step (two blocks of 32) for the tile's weight rows, by wave 0:
-// lane q carries 16 rows' bytes of one block of one matrix (gate or up), so each matrix is
-// one instruction with the other matrix's lanes masked off.
+// MXFP4 scale bytes of one K step (two blocks of 32) for the tile's weight rows: the share
+// of wave w lies inside one (block, matrix) group of 16-row pieces.
 template <typename Cfg>
 __device__ __forceinline__ void issue_s(char* Ss, uint32_t kbs, __amdgpu_buffer_rsrc_t rsS0,
                                         __amdgpu_buffer_rsrc_t rsS1, uint32_t voffS, int wave, int lane) {
   if constexpr (Cfg::WF_ == 2) {
-    if (wave == 0) {
-      constexpr int PPM = Cfg::BN_ / 16;                          // pieces per matrix per block
-      const int m = (lane / PPM) % Cfg::NB;
-      auto* dst = (__attribute__((address_space(3))) void*)Ss;
-      if (lane < Cfg::S_PIECES && m == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS0, dst, 16, voffS, kbs, 0, 0);
-      if (Cfg::NB == 2 && lane < Cfg::S_PIECES && m == 1)
+    constexpr int PPM = Cfg::BN_ / 16;                            // pieces per matrix per block
+    const int q0 = wave * Cfg::PW_S;
+    const bool up = Cfg::NB == 2 && (q0 / PPM) % 2 == 1;
+    auto* dst = (__attribute__((address_space(3))) void*)(Ss + q0 * 16);
+    if (lane < Cfg::PW_S) {
+      if (up)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS1, dst, 16, voffS, kbs, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS0, dst, 16, voffS, kbs, 0, 0);
     }
   }
 }
@@ -168,7 +166,7 @@ __device__ __forceinline__ void tile_offsets(const GemmArgs& args, int wave, int
                                              uint32_t* voffB) {
 #pragma unroll
   for (int it = 0; it < Cfg::A_IT; ++it) {
-    const int q = it * Cfg::NT + wave * kWave + lane, r = q >> 3;
+    const int q = min(wave * Cfg::PW_A + it * kWave + lane, Cfg::P_A - 1), r = q >> 3;
     const int cl = (q & 7) ^ ((r >> 1) & 7);
     const int rr = min(r, rows - 1);
     const size_t arow = args.a_rows ? (size_t)args.a_rows[row0 + rr] : (size_t)rr;
@@ -176,7 +174,7 @@ __device__ __forceinline__ void tile_offsets(const GemmArgs& args, int wave, int
   }
 #pragma unroll
   for (int it = 0; it < Cfg::B_IT; ++it) {
-    const int q = it * Cfg::NT + wave * kWave + lane;
+    const int q = min(wave * Cfg::PW_B + it * kWave + lane, Cfg::P_B - 1);
     const int r = q / Cfg::PPR_B;
     const int cl = Cfg::WF_ == 1 ? (q & 3) ^ ((r >> 1) & 3)
                                  : (Cfg::WF_ == 2 ? (q & 1) ^ ((r >> 2) & 1) : (q & 7) ^ ((r >> 1) & 7));
@@ -254,12 +252,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       rsS1 = GATED ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S1 + gs), 0, 0x7fffffff, kBufFlags)
                    : rsS0;
       constexpr int PPM = BN / 16;
-      const int c = lane / (NB * PPM), p = lane % PPM;
+      const int qs = wave * Cfg::PW_S + min(lane, Cfg::PW_S - 1);   // [block c][matrix][piece p]
+      const int c = qs / (NB * PPM), p = qs % PPM;
       voffS = (uint32_t)(c * N + nt * BN + 16 * p);
     }
     // one K step of weights (codes, and MXFP4 scales) into weight slot s
     auto issue_w = [&](int s, int ks) {
-      issue_b<Cfg>(b_slot(s), (uint32_t)ks * KB_B, rsB0, rsB1, voffB, wave);
+      issue_b<Cfg>(b_slot(s), (uint32_t)ks * KB_B, rsB0, rsB1, voffB, wave, lane);
       issue_s<Cfg>(b_slot(s) + Cfg::BROWS * Cfg::ROWB_B, (uint32_t)ks * 2 * N, rsS0, rsS1, voffS, wave, lane);
     };
 
@@ -384,7 +383,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
       for (int p = 0; p < STAGES - 1; ++p)
         if (p < nks) {
-          issue_a<Cfg>(a_slot(p), (uint32_t)p * 128, rsA, voffA, wave);
+          issue_a<Cfg>(a_slot(p), (uint32_t)p * 128, rsA, voffA, wave, lane);
           issue_w(p, p);
         }
       int slot = 0;
@@ -393,7 +392,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         block_barrier();                                // ... for every wave; slot ks-1 is free
         if (ks + STAGES - 1 < nks) {
           const int fs = slot == 0 ? STAGES - 1 : slot - 1;
-          issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsA, voffA, wave);
+          issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsA, voffA, wave, lane);
           issue_w(fs, ks + STAGES - 1);
         }
         compute(a_slot(slot), b_slot(slot));
@@ -403,7 +402,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       // Weights two K steps ahead, activations one.  Issue order A(0) B(0) B(1), then per
       // step A(ks+1) B(ks+2): when step ks is consumed the only newer loads than A(ks) are
       // those of B(ks+1), so waiting until at most LPS_B are outstanding lands A(ks), B(ks).
-      issue_a<Cfg>(a_slot(0), 0, rsA, voffA, wave);
+      issue_a<Cfg>(a_slot(0), 0, rsA, voffA, wave, lane);
       issue_w(0, 0);
       if (nks > 1) issue_w(1, 1);
       int bs = 0;                                       // weight slot of step ks
@@ -411,7 +410,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         if (ks + 1 < nks) wait_vmcnt<Cfg::LPS_B>();
         else wait_vmcnt<0>();
         block_barrier();                                // step ks visible; slots of ks-1 free
-        if (ks + 1 < nks) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * 128, rsA, voffA, wave);
+        if (ks + 1 < nks) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * 128, rsA, voffA, wave, lane);
         if (ks + 2 < nks)
           issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
         compute(a_slot(ks & 1), b_slot(bs));
@@ -442,6 +441,10 @@ int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt) {
 // keep more steps in flight.
 template <int WF>
 constexpr int kDecodeStages = 4;
+// weight rows per decode tile (gate/up: per matrix): 4-bit weights carry a quarter of the
+// bytes per K step, so their tiles are wider to keep the bytes per step up
+template <int WF, bool GATED>
+constexpr int kDecodeBN = GATED ? (WF == 2 ? 64 : 64) : (WF == 2 ? 32 : 32);
 
 template <typename T, bool GATED, int WF>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
@@ -467,9 +470,14 @@ static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipS
     default:
       // decode: a few rows per expert, 4-deep ring; the down product has half the weight
       // rows of gate/up, so narrower tiles give it as many blocks streaming in parallel
-      if constexpr (GATED) return launch_cfg<T, 16, 64, 1, 4, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(
-          a, max_tiles_m, s);
-      else return launch_cfg<T, 16, 32, 1, 2, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(a, max_tiles_m, s);
+      if constexpr (GATED) {
+        return launch_cfg<T, 16, kDecodeBN<WF, true>, 1, 4, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(
+            a, max_tiles_m, s);
+      } else {
+        if (a.N % kDecodeBN<WF, false> != 0) return launch_cfg<T, 16, 32, 1, 2, GATED, 4, 4, WF>(a, max_tiles_m, s);
+        return launch_cfg<T, 16, kDecodeBN<WF, false>, 1, 2, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(
+            a, max_tiles_m, s);
+      }
   }
 }
 
