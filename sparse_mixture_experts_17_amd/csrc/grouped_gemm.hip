@@ -90,15 +90,19 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   if constexpr (STAGES <= 2) {
     wait_vmcnt<0>();
   } else {
-    static_assert(STAGES <= 8, "deeper rings need more cases");
-    switch (ahead) {
+    static_assert(STAGES <= 12, "deeper rings need more cases");
+    switch (ahead) {      // ahead <= STAGES - 2; each case's count is only used when reachable
       case 0: wait_vmcnt<0>(); break;
       case 1: wait_vmcnt<LPS>(); break;
       case 2: wait_vmcnt<2 * LPS>(); break;
-      case 3: wait_vmcnt<(STAGES > 4 ? 3 : 2) * LPS>(); break;
-      case 4: wait_vmcnt<(STAGES > 5 ? 4 : 2) * LPS>(); break;
-      case 5: wait_vmcnt<(STAGES > 6 ? 5 : 2) * LPS>(); break;
-      default: wait_vmcnt<(STAGES > 7 ? 6 : 2) * LPS>(); break;
+      case 3: wait_vmcnt<(STAGES > 4 ? 3 : 0) * LPS>(); break;
+      case 4: wait_vmcnt<(STAGES > 5 ? 4 : 0) * LPS>(); break;
+      case 5: wait_vmcnt<(STAGES > 6 ? 5 : 0) * LPS>(); break;
+      case 6: wait_vmcnt<(STAGES > 7 ? 6 : 0) * LPS>(); break;
+      case 7: wait_vmcnt<(STAGES > 8 ? 7 : 0) * LPS>(); break;
+      case 8: wait_vmcnt<(STAGES > 9 ? 8 : 0) * LPS>(); break;
+      case 9: wait_vmcnt<(STAGES > 10 ? 9 : 0) * LPS>(); break;
+      default: wait_vmcnt<(STAGES > 11 ? 10 : 0) * LPS>(); break;
     }
   }
 }
