@@ -19,6 +19,9 @@ struct GemmArgs {
   const int32_t* tstart;    // [G+1] first m-tile of each group (unused when dense)
   int G, dense_rows, N, K;
   void* C;                  // [rows, N]  (dtype for gated, fp32 for down)
+  int ksplit = 1;           // K chunks (plain product only): chunk c covers K steps
+                            // [c K/ksplit, (c+1) K/ksplit) and writes C + c * split_stride
+  size_t split_stride = 0;  // floats between the partial outputs of consecutive chunks
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
@@ -99,7 +102,7 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& args, int L, int
 // product stores SiLU(a) * b in the activation type, the plain one fp32.
 template <typename Cfg, typename Acc>
 __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0, const Acc& acc1, int wm, int wn,
-                                           int lane, int g, int nt, int row0, int rows) {
+                                           int lane, int g, int nt, int row0, int rows, size_t c_off = 0) {
   using T = typename Cfg::Elem;
   const int N = args.N;
 #pragma unroll
@@ -119,7 +122,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
               const float h = __fdividef(a, 1.f + __expf(-a)) * b;
               ((T*)args.C)[o] = ElemOut<T>::from_f32(h);
             } else {
-              ((float*)args.C)[o] = acc0[i][j][q] * args.S0[sc];
+              ((float*)args.C)[c_off + o] = acc0[i][j][q] * args.S0[sc];
             }
           } else if constexpr (Cfg::NB == 2) {
             const float a = acc0[i][j][q], b = acc1[i][j][q];
@@ -127,7 +130,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
                                                                     // result is rounded to bf16)
             ((T*)args.C)[o] = ElemOut<T>::from_f32(h);
           } else {
-            ((float*)args.C)[o] = acc0[i][j][q];
+            ((float*)args.C)[c_off + o] = acc0[i][j][q];
           }
         }
       }
@@ -146,7 +149,7 @@ static hipError_t launch_kernel(const GemmArgs& a, int max_tiles_m, hipStream_t 
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     return hipErrorInvalidDevice;
-  const long long max_live = (long long)max_tiles_m * (a.N / Cfg::BN_);
+  const long long max_live = (long long)max_tiles_m * (a.N / Cfg::BN_) * std::max(1, a.ksplit);
   long long grid = std::min<long long>(max_live, (long long)cus * occ);
   grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid < kNumXcd) grid = kNumXcd;

@@ -221,23 +221,28 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int N = args.N, K = args.K;
   const int ntn = N / BN;
   const int mt_live = args.offsets ? args.tstart[args.G] : (args.dense_rows + BM - 1) / BM;
-  const int live = mt_live * ntn;
+  const int ksp = GATED ? 1 : args.ksplit;            // K chunks per output tile
+  const int live = mt_live * ntn * ksp;
   const int xcd = blockIdx.x % kNumXcd, j0 = blockIdx.x / kNumXcd, bpx = gridDim.x / kNumXcd;
   const int lo = (int)((long long)live * xcd / kNumXcd);
   const int hi = (int)((long long)live * (xcd + 1) / kNumXcd);
-  const int nks = K / BKE;
+  const int nks = K / BKE / ksp;                      // K steps per chunk
   const size_t row_stride = (size_t)K * sizeof(T);   // bytes per row of A
   const size_t row_stride_b = WF == 1 ? (size_t)K : (WF == 2 ? (size_t)K / 2 : row_stride);   // per weight row
   constexpr uint32_t KB_B = Cfg::ROWB_B;              // weight bytes per row per K step
 
   for (int L = lo + j0; L < hi; L += bpx) {
-    const TileCoord tc = tile_coord(args, L, ntn, mt_live, bpx, BM);
+    // consecutive work items are the K chunks of one output tile
+    const int chunk = ksp > 1 ? L % ksp : 0;
+    const TileCoord tc = tile_coord(args, ksp > 1 ? L / ksp : L, ntn, mt_live, max(1, bpx / ksp), BM);
     const int g = tc.g, nt = tc.nt, row0 = tc.row0, rows = tc.rows;
-    // Buffer resources over this tile's A rows and B rows; per-lane 32-bit offsets are fixed
-    // for the tile and the K step rides in the scalar offset.
-    const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride);
-    const char* B0b = (const char*)args.B0 + ((size_t)g * N + (size_t)nt * BN) * row_stride_b;
-    const char* B1b = GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride_b : B0b;
+    const size_t ks0 = (size_t)chunk * nks;             // first K step of the chunk
+    // Buffer resources over this tile's A rows and B rows (from the chunk's first K step);
+    // per-lane 32-bit offsets are fixed for the tile and the K step rides in the scalar offset.
+    const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride) + ks0 * BKE * sizeof(T);
+    const char* B0b = (const char*)args.B0 + ((size_t)g * N + (size_t)nt * BN) * row_stride_b + ks0 * KB_B;
+    const char* B1b =
+        GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride_b + ks0 * KB_B : B0b;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, 0x7fffffff, kBufFlags);
     const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, 0x7fffffff, kBufFlags);
     const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, 0x7fffffff, kBufFlags);
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     __amdgpu_buffer_rsrc_t rsS0 = rsB0, rsS1 = rsB1;
     uint32_t voffS = 0;
     if constexpr (WF == 2) {
-      const size_t gs = (size_t)g * (K / 32) * N;
+      const size_t gs = (size_t)g * (K / 32) * N + ks0 * 2 * N;   // two blocks per K step
       rsS0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S0 + gs), 0, 0x7fffffff, kBufFlags);
       rsS1 = GATED ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S1 + gs), 0, 0x7fffffff, kBufFlags)
                    : rsS0;
@@ -423,7 +428,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     }
     __syncthreads();                                    // LDS free for the next tile
 
-    store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, g, nt, row0, rows);
+    store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, g, nt, row0, rows, (size_t)chunk * args.split_stride);
   }
 }
 
@@ -500,8 +505,11 @@ hipError_t launch_gemm_gateup(GemmKind kind, int dtype, int wfmt, const void* A,
 
 hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, const void* Wd, const float* Sd,
                             const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
-                            int N, int K, float* O, hipStream_t stream) {
-  GemmArgs a{H, nullptr, Wd, nullptr, Sd, nullptr, offsets, tstart, G, dense_rows, N, K, O};
+                            int N, int K, float* O, int ksplit, size_t split_stride, hipStream_t stream) {
+  GemmArgs a{H, nullptr, Wd, nullptr, Sd, nullptr, offsets, tstart, G, dense_rows, N, K, O, ksplit, split_stride};
+  // K chunks: decode tiles only, each chunk a whole number of K steps (64 elements; 32 in fp32)
+  if (ksplit < 1 || (ksplit > 1 && (kind != kGemmDecode || K % (ksplit * (dtype == 1 ? 64 : 32)) != 0)))
+    return hipErrorInvalidValue;
   if (dtype == 1) {
     if (wfmt == 1) return dispatch_kind<uint16_t, false, 1>(kind, a, max_tiles_m, stream);
     if (wfmt == 2) return dispatch_kind<uint16_t, false, 2>(kind, a, max_tiles_m, stream);

@@ -40,9 +40,10 @@ hipError_t launch_rank_gather(int dtype, const void* x, const int32_t* idx, int 
                               int cap, const int32_t* chunk_base, const int32_t* offsets,
                               int32_t* row_token, int32_t* row_of, void* x_perm, hipStream_t stream);
 
-// y[t] = shared[t] (or 0) + sum_j gate[t,j] * o[row_of[t,j]] over kept slots.
+// y[t] = shared[t] (or 0) + sum_j gate[t,j] * o[row_of[t,j]] over kept slots, where a row of o
+// is the sum of nsplit partials o + p * split_stride (floats; a multiple of 4), p = 0 .. nsplit-1.
 hipError_t launch_combine(const float* o, const int32_t* row_of, const float* gate, const float* shared,
-                          float* y, int T, int d, int k, hipStream_t stream);
+                          float* y, int T, int d, int k, int nsplit, size_t split_stride, hipStream_t stream);
 
 // Grouped GEMM tile configurations (one kernel template; see grouped_gemm.hip).
 enum GemmKind { kGemmLarge = 0, kGemmStream = 1, kGemmDecode = 2 };
@@ -62,6 +63,6 @@ hipError_t launch_gemm_gateup(GemmKind kind, int dtype, int wfmt, const void* A,
 // Down projection:  o[r, n] = H_e W_d[e]^T, fp32 out (times Sd[e, n] for FP8 weights).
 hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, const void* Wd, const float* Sd,
                             const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
-                            int N, int K, float* O, hipStream_t stream);
+                            int N, int K, float* O, int ksplit, size_t split_stride, hipStream_t stream);
 
 }  // namespace moe

@@ -16,9 +16,31 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Tile configuration from the expected rows per expert (host-known bounds only).
+GemmKind choose_kind(long long rows_total, int groups, int cap) {
+  const double mean = (double)rows_total / (double)groups;
+  double mx = mean + 4.0 * sqrt(mean) + 2.0;
+  if (cap >= 0) mx = std::min(mx, (double)cap);
+  if (mx <= 16.0) return kGemmDecode;
+  if (mean >= 384.0) return kGemmLarge;
+  return kGemmStream;
+}
+
+// K chunks of the routed down product.  At decode sizes each expert has one m-tile, so the
+// product has only E * d / 32 output tiles, each a long run of d_e / 64 K steps.  With 4-bit
+// weights a decode tile takes so little LDS that several times more blocks fit on a CU than
+// there are tiles; cutting K in two doubles the blocks streaming weights at once.  (With
+// 8- and 16-bit weights the tiles already fill the CUs, and the extra partial sums only cost
+// time.)  The combine sums the chunks' partial outputs.
+int down_ksplit(const moe_shape& s, GemmKind kind) {
+  if (kind != kGemmDecode || s.wfmt != MOE_W_MXFP4) return 1;
+  return s.d_e % 128 == 0 && s.d_e / 128 >= 16 ? 2 : 1;
+}
+
 struct Layout {
   size_t p_part, hist, chunk_base, counts, kept, offsets, row_token, row_of, tstart1, tstart2;
   size_t x_perm, h, o, sh_h, sh_o, total;
+  int ksplit;   // K chunks of the routed down product in the forward (partials at o + c * T*k*d)
 };
 
 size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
@@ -42,7 +64,8 @@ Layout layout(const moe_shape& s) {
   L.tstart2 = take((E + 1) * sizeof(int32_t));
   L.x_perm = take(R * (size_t)s.d * es);
   L.h = take(R * (size_t)s.d_e * es);
-  L.o = take(R * (size_t)s.d * sizeof(float));
+  L.ksplit = down_ksplit(s, choose_kind(std::max<long long>((long long)R, 1), s.E, s.capacity));
+  L.o = take(R * (size_t)s.d * sizeof(float) * (size_t)L.ksplit);
   L.sh_h = take((size_t)s.T * (size_t)s.d_e_shared * es);
   L.sh_o = take(s.d_e_shared > 0 ? (size_t)s.T * (size_t)s.d * sizeof(float) : 0);
   L.total = off;
@@ -70,16 +93,6 @@ moe_status check_shape(const moe_shape* s) {
   if ((long long)s->T * s->k * (long long)s->d * (s->dtype == MOE_BF16 ? 2 : 4) >= (1LL << 35))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
-}
-
-// Tile configuration from the expected rows per expert (host-known bounds only).
-GemmKind choose_kind(long long rows_total, int groups, int cap) {
-  const double mean = (double)rows_total / (double)groups;
-  double mx = mean + 4.0 * sqrt(mean) + 2.0;
-  if (cap >= 0) mx = std::min(mx, (double)cap);
-  if (mx <= 16.0) return kGemmDecode;
-  if (mean >= 384.0) return kGemmLarge;
-  return kGemmStream;
 }
 
 // Upper bound on the number of m-tiles over all groups.
@@ -128,7 +141,7 @@ moe_status run_ffn(const moe_shape& s, int G, const void* A, const int32_t* offs
   MOE_HIP(launch_gemm_gateup(kind, s.dtype, s.wfmt, A, nullptr, wg, wu, (const float*)sc.gate, (const float*)sc.up,
                              offsets, tstart1, G, dense_rows, tiles1, d_e, s.d, h, st));
   MOE_HIP(launch_gemm_down(kind, s.dtype, s.wfmt, h, wd, (const float*)sc.down, offsets, tstart2, G, dense_rows,
-                           tiles2, s.d, d_e, o, st));
+                           tiles2, s.d, d_e, o, 1, 0, st));
   return MOE_OK;
 }
 
@@ -228,7 +241,7 @@ moe_status moe_combine(const moe_shape* shape, const float* o, const int32_t* ro
   const moe_shape& s = *shape;
   if (s.T == 0) return MOE_OK;
   if (!o || !row_of || !gate || !y) return MOE_ERR_NULL;
-  MOE_HIP(launch_combine(o, row_of, gate, shared_out, y, s.T, s.d, s.k, (hipStream_t)stream));
+  MOE_HIP(launch_combine(o, row_of, gate, shared_out, y, s.T, s.d, s.k, 1, 0, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -293,7 +306,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
                                s.d, at<void>(ws, L.h), st));
     MOE_MARK(MOE_STAGE_DOWN);
     MOE_HIP(launch_gemm_down(kind, s.dtype, s.wfmt, at<void>(ws, L.h), w_down, (const float*)sc.down, offsets, ts2, s.E, 0,
-                             max_m_tiles(R, s.E, s.capacity, bm2), s.d, s.d_e, at<float>(ws, L.o), st));
+                             max_m_tiles(R, s.E, s.capacity, bm2), s.d, s.d_e, at<float>(ws, L.o), L.ksplit,
+                             (size_t)R * s.d, st));
   }
   MOE_MARK(MOE_STAGE_SHARED_GATE_UP);
   const float* shared_out = nullptr;
@@ -306,11 +320,13 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
     MOE_MARK(MOE_STAGE_SHARED_DOWN);
     MOE_HIP(launch_gemm_down(sk, s.dtype, s.wfmt, at<void>(ws, L.sh_h), ws_down, (const float*)ssc.down, nullptr,
                              nullptr, 1, s.T,
-                             (s.T + sbm2 - 1) / sbm2, s.d, s.d_e_shared, at<float>(ws, L.sh_o), st));
+                             (s.T + sbm2 - 1) / sbm2, s.d, s.d_e_shared, at<float>(ws, L.sh_o), 1, 0, st));
     shared_out = at<float>(ws, L.sh_o);
   }
   MOE_MARK(MOE_STAGE_COMBINE);
-  if (s.T > 0) MOE_HIP(launch_combine(at<float>(ws, L.o), row_of, gate, shared_out, y, s.T, s.d, s.k, st));
+  if (s.T > 0)
+    MOE_HIP(launch_combine(at<float>(ws, L.o), row_of, gate, shared_out, y, s.T, s.d, s.k, L.ksplit, (size_t)R * s.d,
+                           st));
   MOE_MARK(MOE_NUM_STAGES);
 #undef MOE_MARK
   return MOE_OK;

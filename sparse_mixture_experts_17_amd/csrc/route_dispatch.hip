@@ -482,26 +482,38 @@ hipError_t launch_rank_gather(int dtype, const void* x, const int32_t* idx, int 
 //
 // The layer's gate-weighted sum back in token order (Zero to Frontier §13.1, "The MoE
 // layer" equation), accumulated as: shared (or 0), then slot 0, 1, ..., k-1 with one
-// fused multiply-add each.  A dropped slot (row -1) adds nothing.
+// fused multiply-add each.  A dropped slot (row -1) adds nothing.  When the down product
+// ran in nsplit K chunks, a row's output is the sum of its partials, taken in chunk order
+// (fixed, so the result does not depend on scheduling).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
                                                       const float* __restrict__ shared, float* __restrict__ y,
-                                                      int T, int d, int k) {
+                                                      int T, int d, int k, int nsplit, size_t split_stride) {
   __shared__ int s_row[16];
   __shared__ float s_g[16];
-  const int t = blockIdx.x;
+  const int d4 = d / 4, nch = (d4 + 255) / 256;   // blocks per token: 1024 columns each
+  const int t = blockIdx.x / nch;
   if (threadIdx.x < k) {
     s_row[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
     s_g[threadIdx.x] = gate[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  const int d4 = d / 4;
-  for (int c = threadIdx.x; c < d4; c += 256) {
+  const size_t ss4 = split_stride / 4;
+  const int c = (blockIdx.x % nch) * 256 + threadIdx.x;
+  if (c < d4) {
     f32x4_t acc = shared ? ((const f32x4_t*)shared)[(size_t)t * d4 + c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int row = s_row[j];
       if (row >= 0) {
-        const f32x4_t v = ((const f32x4_t*)o)[(size_t)row * d4 + c];
+        const f32x4_t* src = (const f32x4_t*)o + (size_t)row * d4 + c;
+        f32x4_t v = src[0];
+        for (int p = 1; p < nsplit; ++p) {
+          const f32x4_t w = src[p * ss4];
+          v[0] += w[0];
+          v[1] += w[1];
+          v[2] += w[2];
+          v[3] += w[3];
+        }
         const float g = s_g[j];
         acc[0] = fmaf(g, v[0], acc[0]);
         acc[1] = fmaf(g, v[1], acc[1]);
@@ -514,8 +526,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_combine(const float* o, const int32_t* row_of, const float* gate, const float* shared, float* y,
-                          int T, int d, int k, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, o, row_of, gate, shared, y, T, d, k);
+                          int T, int d, int k, int nsplit, size_t split_stride, hipStream_t stream) {
+  if (nsplit < 1 || (nsplit > 1 && split_stride % 4 != 0)) return hipErrorInvalidValue;
+  const long long blocks = (long long)T * ((d / 4 + 255) / 256);
+  if (blocks >= (1LL << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, row_of, gate, shared, y, T, d,
+                     k, nsplit, split_stride);
   return hipGetLastError();
 }
 

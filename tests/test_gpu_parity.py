@@ -59,6 +59,8 @@ SMALL = [
               capacity_factor=1.0),
     # MXFP4 expert weights in every tile configuration
     wl.scaled(BASE["mixtral_decode_mxfp4"], name="mxfp4_decode_tiles", T=16, d=512, d_e=1024, E=8, k=2),
+    # d_e / 128 >= 16: the down product runs in two K chunks summed by the combine
+    wl.scaled(BASE["mixtral_decode_mxfp4"], name="mxfp4_decode_ksplit", T=16, d=384, d_e=2048, E=8, k=2),
     wl.scaled(BASE["mixtral_decode_mxfp4"], name="mxfp4_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_large_d384", T=1600, d=384, d_e=256, E=4, k=2),
