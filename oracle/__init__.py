@@ -1,4 +1,4 @@
-"""Plain, slow CPU oracle for one sparse mixture-of-experts FFN layer (forward).
+"""Plain, slow CPU oracle for one sparse mixture-of-experts FFN layer (forward and backward).
 
 TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import, call or execute anything in this package.  It
@@ -11,7 +11,8 @@ stored element type, so the oracle sees the same values the GPU receives.
 Modules
   moe_oracle   the layer: router, softmax, top-k, gates, aux statistics,
                capacity dispatch, SwiGLU experts, combine, near-tie report,
-               and the FP8 (E4M3) weight decode
+               the FP8 (E4M3) and MXFP4 weight decodes, and the backward pass
+               (gradients with the routing held fixed)
   bruteforce   pure-Python evaluation of the dense "every expert, unchosen
                gates zero" form, for tiny inputs
   param_count  parameter and FLOP arithmetic of whole MoE models

@@ -1,4 +1,4 @@
-"""Float64 oracle of the forward pass of one sparse MoE FFN layer.
+"""Float64 oracle of the forward and backward passes of one sparse MoE FFN layer.
 
 TEST INFRASTRUCTURE (see the package docstring): only tests, the smoke check and
 the benchmark's CPU-baseline leg use this module.
@@ -35,6 +35,9 @@ in the design notes of the repository):
   * SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)) (the pages name it, not define it).
   * a shared expert is added with weight one, outside routing, capacity and
     the statistics.
+  * backward: the routing (expert choice and capacity drops) and f are constants;
+    gradients reach the router only through the chosen gates and through P in
+    aux (AI Engineering Illustrated, "Inside the Router").
 """
 from __future__ import annotations
 
@@ -442,3 +445,141 @@ def rel_err(y, y_ref) -> float:
     if rms == 0.0:
         return float(np.max(np.abs(y - y_ref)))
     return float(np.max(np.abs(y - y_ref)) / rms)
+
+
+# --------------------------------------------------------------------------- backward
+
+@dataclass
+class Grads:
+    dx: np.ndarray             # [T, d]
+    dw_r: np.ndarray           # [E, d]
+    db_r: np.ndarray | None    # [E], or None when the layer has no router bias
+    dw_gate: np.ndarray        # [E, d_e, d]
+    dw_up: np.ndarray          # [E, d_e, d]
+    dw_down: np.ndarray        # [E, d, d_e]
+    dshared: tuple | None      # (dW_g, dW_u, dW_d) of the shared expert, or None
+    dgate: np.ndarray          # [T, k] dL/dg of each slot (0 for a dropped slot)
+    dlogits: np.ndarray        # [T, E] dL/dr
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d SiLU(z) / dz = sigma(z) (1 + z (1 - sigma(z))), the derivative of z * sigma(z)."""
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def swiglu_backward(X, w_g, w_u, w_d, dO):
+    """(dX, dW_g, dW_u, dW_d) of O = (SiLU(X W_g^T) * (X W_u^T)) W_d^T for rows X [m, d].
+
+    The chain rule through the SwiGLU expert of Zero to Frontier §13.1, "The MoE layer",
+    with h = SiLU(a) * b, a = X W_g^T, b = X W_u^T:
+      dW_d = dO^T h,   dh = dO W_d,
+      da = dh * b * SiLU'(a),   db = dh * SiLU(a),
+      dW_g = da^T X,   dW_u = db^T X,   dX = da W_g + db W_u.
+    """
+    X = np.asarray(X, np.float64)
+    wg, wu, wd = (np.asarray(w, np.float64) for w in (w_g, w_u, w_d))
+    a = X @ wg.T
+    b = X @ wu.T
+    h = silu(a) * b
+    dh = dO @ wd
+    da = dh * b * silu_grad(a)
+    db = dh * silu(a)
+    return da @ wg + db @ wu, da.T @ X, db.T @ X, dO.T @ h
+
+
+def router_backward(p: np.ndarray, idx: np.ndarray, g: np.ndarray, dgate: np.ndarray, f: np.ndarray,
+                    d_aux: float, renormalize: bool = True, scoring: str = "softmax") -> np.ndarray:
+    """dL/dr [T, E] from the gate gradients and the auxiliary term, with the choice of
+    experts held fixed.
+
+    The top-k choice is a hard selection with no gradient; the gradient reaches the router
+    only through the weights of the chosen experts (AI Engineering Illustrated, "Inside
+    the Router").  Steps:
+      * renormalised gates g_j = p_{K_j} / S, S = sum_{i in K} p_i, give
+        dp_{K_i} = (dg_i - sum_j dg_j g_j) / S; raw gates give dp_{K_i} = dg_i;
+      * aux = E sum_e f_e P_e with P_e the mean of p over the T tokens and f_e fixed
+        by the counts, so it adds d_aux * E * f_e / T to every dp[t, e];
+      * softmax scoring: dr = p * (dp - sum_e p_e dp_e); sigmoid scoring (p is the
+        affinity sigma(r)): dr = dp * p * (1 - p).
+    """
+    T, E = p.shape
+    dp = np.zeros((T, E))
+    if renormalize:
+        S = np.take_along_axis(p, idx.astype(np.int64), axis=1).sum(axis=1, keepdims=True)
+        dpk = (dgate - np.sum(dgate * g, axis=1, keepdims=True)) / S
+    else:
+        dpk = dgate
+    rows = np.arange(T)
+    for j in range(idx.shape[1]):
+        dp[rows, idx[:, j]] += dpk[:, j]
+    if T > 0:
+        dp += d_aux * E * np.asarray(f, np.float64)[None, :] / T
+    if scoring == "softmax":
+        return p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    if scoring == "sigmoid":
+        return dp * p * (1.0 - p)
+    raise ValueError(scoring)
+
+
+def moe_backward(x, w_r, experts, k: int, dy, d_aux: float = 0.0, cap: int = -1, b_r=None,
+                 renormalize: bool = True, shared=None, idx=None, scoring: str = "softmax",
+                 n_group: int = 1, topk_group: int = 1) -> Grads:
+    """Gradients of L = sum(dy * y) + d_aux * aux for the layer of ``moe_forward``.
+
+    The routing -- which experts each token picked and which assignments capacity
+    dropped -- is a constant of the backward pass (AI Engineering Illustrated, "Inside the
+    Router"); f, being counts, is constant too.  A kept slot (t, j) with expert e and row
+    r passes g_tj dy_t into expert e's rows (dO_r) and gets dL/dg_tj = dy_t . O_r; a
+    dropped slot passes nothing.  Expert gradients follow ``swiglu_backward`` and the
+    router's ``router_backward``; dx sums every kept slot's dX row, the router's dr W_r
+    and the shared expert's dX.  The router bias is part of the logits under softmax
+    scoring (db_r = sum_t dr_t); under sigmoid scoring it only picks experts and gets a
+    zero gradient.
+    """
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    T, d = x.shape
+    E = len(experts)
+    fwd = moe_forward(x, w_r, experts, k, cap, b_r, renormalize, None, idx, scoring, n_group, topk_group)
+    disp, g = fwd.disp, fwd.gate
+    dx = np.zeros((T, d))
+    dgate = np.zeros((T, k))
+    dwg, dwu, dwd = [], [], []
+    slot = np.full(int(disp.offsets[-1]), -1, dtype=np.int64)        # slot j of each kept row
+    for j in range(k):
+        rows = disp.row_of[:, j]
+        slot[rows[rows >= 0]] = j
+    for e in range(E):
+        wg, wu, wd = (np.asarray(w, np.float64) for w in experts[e])
+        lo, hi = int(disp.offsets[e]), int(disp.offsets[e + 1])
+        if hi == lo:                                 # an expert with no rows gets zero gradients
+            dwg.append(np.zeros_like(wg))
+            dwu.append(np.zeros_like(wu))
+            dwd.append(np.zeros_like(wd))
+            continue
+        toks, js = disp.row_token[lo:hi], slot[lo:hi]
+        X = x[toks]
+        O = swiglu_ffn(X, wg, wu, wd)
+        dgate[toks, js] = np.sum(dy[toks] * O, axis=1)
+        dO = g[toks, js][:, None] * dy[toks]
+        dX, gg, gu, gd = swiglu_backward(X, wg, wu, wd, dO)
+        dwg.append(gg)
+        dwu.append(gu)
+        dwd.append(gd)
+        np.add.at(dx, toks, dX)
+    dr = router_backward(fwd.p, fwd.idx, g, dgate, fwd.f, d_aux, renormalize, scoring)
+    w_r64 = np.asarray(w_r, np.float64)
+    dx += dr @ w_r64
+    dw_r = dr.T @ x
+    db_r = None
+    if b_r is not None:
+        db_r = dr.sum(axis=0) if scoring == "softmax" else np.zeros(E)
+    dshared = None
+    if shared is not None:
+        sX, sg, su, sd = swiglu_backward(x, *shared, dy)
+        dx += sX
+        dshared = (sg, su, sd)
+    return Grads(dx=dx, dw_r=dw_r, db_r=db_r, dw_gate=np.stack(dwg) if E else np.zeros((0,)),
+                 dw_up=np.stack(dwu) if E else np.zeros((0,)), dw_down=np.stack(dwd) if E else np.zeros((0,)),
+                 dshared=dshared, dgate=dgate, dlogits=dr)

@@ -505,4 +505,119 @@ def pin_mx_dequantize():
             assert w[r, j] == mo.e2m1_decode(codes[r, j:j + 1])[0] * 2.0 ** (int(sc[j // 32, r]) - 127)
 
 
+# --------------------------------------------------------------------------- backward
+
+def _loss(x, w_r, experts, k, dy, d_aux, cap, b_r, renorm, sh, idx, scoring, ng, tg):
+    """L = sum(dy * y) + d_aux * aux from the (pinned) forward, routing forced to idx."""
+    res = mo.moe_forward(x, w_r, experts, k, cap, b_r, renorm, sh, idx, scoring, ng, tg)
+    return float(np.sum(dy * res.y) + d_aux * res.aux)
+
+
+def _fd_check(seed, T, d, de, E, k, cap, renorm, scoring="softmax", ng=1, tg=1, bias=True, shared=True,
+              d_aux=0.7, step=1e-6):
+    """Central differences of the forward loss, every input element, against moe_backward.
+
+    The routing (idx) is taken from the unperturbed forward and held fixed, which is the
+    definition of the backward pass (selection carries no gradient); capacity then drops
+    the same assignments at every perturbed point.
+    """
+    x, w_r, experts, b_r, sh = _tiny_layer(seed, T=T, d=d, d_e=de, E=E, bias=bias, shared=shared)
+    if b_r is not None and scoring == "sigmoid":
+        b_r = b_r * 0.2
+    dy = _rng(seed + 1000).standard_normal((T, d))
+    idx = mo.moe_forward(x, w_r, experts, k, cap, b_r, renorm, sh, None, scoring, ng, tg).idx
+    G = mo.moe_backward(x, w_r, experts, k, dy, d_aux, cap, b_r, renorm, sh, idx, scoring, ng, tg)
+    experts = [list(ex) for ex in experts]
+    sh = None if sh is None else list(sh)
+
+    def L():
+        return _loss(x, w_r, experts, k, dy, d_aux, cap, b_r, renorm, sh, idx, scoring, ng, tg)
+
+    def fd(arr):
+        out = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            v = arr[i]
+            arr[i] = v + step
+            lp = L()
+            arr[i] = v - step
+            lm = L()
+            arr[i] = v
+            out[i] = (lp - lm) / (2 * step)
+        return out
+
+    checks = [("dx", fd(x), G.dx), ("dw_r", fd(w_r), G.dw_r)]
+    if b_r is not None:
+        checks.append(("db_r", fd(b_r), G.db_r))
+    for e in range(E):
+        for m, name, got in ((0, "dw_gate", G.dw_gate[e]), (1, "dw_up", G.dw_up[e]), (2, "dw_down", G.dw_down[e])):
+            experts[e][m] = experts[e][m].copy()
+            checks.append((f"{name}[{e}]", fd(experts[e][m]), got))
+    if sh is not None:
+        for m in range(3):
+            sh[m] = sh[m].copy()
+            checks.append((f"dshared[{m}]", fd(sh[m]), G.dshared[m]))
+    for name, want, got in checks:
+        assert got is not None and np.shape(got) == np.shape(want), name
+        scale = max(1.0, float(np.max(np.abs(want))))
+        assert np.max(np.abs(np.asarray(got) - want)) <= 1e-6 * scale, (name, np.max(np.abs(got - want)))
+    return G, idx
+
+
+def pin_backward_fd_softmax():
+    """Softmax router with bias, renormalised gates, capacity drops, shared expert, aux term."""
+    G, idx = _fd_check(41, T=6, d=5, de=4, E=4, k=2, cap=2, renorm=True)
+    # the softmax is unchanged by a common shift of the logits: each dr row sums to zero
+    assert np.allclose(G.dlogits.sum(axis=1), 0.0, atol=1e-12)
+
+
+def pin_backward_fd_raw_gates():
+    """Switch-style raw gates at k = 1 with drops, and k = 3 without a bias or shared expert."""
+    _fd_check(42, T=7, d=4, de=3, E=3, k=1, cap=2, renorm=False)
+    _fd_check(43, T=5, d=4, de=3, E=5, k=3, cap=-1, renorm=True, bias=False, shared=False, d_aux=0.0)
+
+
+def pin_backward_fd_sigmoid():
+    """Sigmoid affinities with a selection-only bias and the group limit."""
+    G, _ = _fd_check(44, T=6, d=4, de=3, E=8, k=2, cap=-1, renorm=True, scoring="sigmoid", ng=4, tg=2)
+    assert np.array_equal(G.db_r, np.zeros(8))       # the bias only picks experts
+    _fd_check(45, T=5, d=4, de=3, E=6, k=3, cap=3, renorm=False, scoring="sigmoid", ng=3, tg=2, shared=False)
+
+
+def pin_backward_dropped_slots():
+    """A dropped slot gets dL/dg = 0 and sends nothing to its expert; a token whose every
+    slot is dropped still gets the router's and the shared expert's dx."""
+    x, w_r, experts, b_r, sh = _tiny_layer(46, T=6, d=5, d_e=4, E=3, bias=False, shared=True)
+    idx = np.zeros((6, 1), dtype=np.int32)               # all on expert 0, capacity 2
+    dy = _rng(47).standard_normal((6, 5))
+    G = mo.moe_backward(x, w_r, experts, 1, dy, 0.0, 2, None, True, sh, idx)
+    assert np.all(G.dgate[2:] == 0.0) and np.all(G.dgate[:2] != 0.0)
+    assert np.all(G.dw_gate[1:] == 0.0) and np.all(G.dw_down[1:] == 0.0)
+    # k = 1 renormalised: g = 1 whatever p is, so the router gets no gradient from y
+    assert np.allclose(G.dlogits, 0.0, atol=1e-15) and np.allclose(G.dw_r, 0.0, atol=1e-15)
+    sX = mo.swiglu_backward(x, *sh, dy)[0]
+    assert np.allclose(G.dx[2:], sX[2:], rtol=1e-13, atol=1e-13)
+    # expert 0 saw tokens 0 and 1 only
+    xe = mo.swiglu_backward(x[:2], *experts[0], dy[:2])
+    assert np.allclose(G.dw_gate[0], xe[1], rtol=1e-13, atol=1e-13)
+
+
+def pin_backward_single_expert_autograd():
+    """E = 1, k = 1 reduces the layer to one SwiGLU network (g = 1, aux = 1 at any logits):
+    the gradients are torch.autograd's of that network, and the router gets none."""
+    import torch
+    g = _rng(48)
+    T, d, de = 7, 6, 5
+    x, w_r = g.standard_normal((T, d)), g.standard_normal((1, d))
+    wg, wu, wd = g.standard_normal((de, d)), g.standard_normal((de, d)), g.standard_normal((d, de))
+    dy = g.standard_normal((T, d))
+    G = mo.moe_backward(x, w_r, [(wg, wu, wd)], 1, dy, d_aux=0.9)
+    tx, tg, tu, td = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, wg, wu, wd))
+    y = torch.nn.functional.linear(torch.nn.functional.silu(torch.nn.functional.linear(tx, tg))
+                                   * torch.nn.functional.linear(tx, tu), td)
+    y.backward(torch.tensor(dy))
+    for got, want in ((G.dx, tx.grad), (G.dw_gate[0], tg.grad), (G.dw_up[0], tu.grad), (G.dw_down[0], td.grad)):
+        assert np.allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(G.dw_r, 0.0, atol=1e-15)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -14,7 +14,8 @@ from oracle import moe_oracle as mo
 _orig = {name: getattr(mo, name) for name in
          ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
           "capacity", "dispatch", "near_ties", "sigmoid", "group_limited_top_k", "route", "e4m3_decode",
-          "dequantize_rows", "e2m1_decode", "e8m0_decode", "dequantize_mx_rows"]}
+          "dequantize_rows", "e2m1_decode", "e8m0_decode", "dequantize_mx_rows", "silu_grad",
+          "swiglu_backward", "router_backward", "moe_backward"]}
 
 
 def _softmax_no_shift(r):
@@ -196,6 +197,88 @@ def _mx_scales_transposed(packed, scales, block=32):
     return _orig["dequantize_mx_rows"](packed, np.resize(sc.T, sc.shape), block)
 
 
+def _silu_grad_sigmoid(z):
+    return mo.sigmoid(z)
+
+
+def _silu_grad_sign(z):
+    s = mo.sigmoid(z)
+    return s * (1.0 - z * (1.0 - s))
+
+
+def _swb_no_b(X, w_g, w_u, w_d, dO):
+    X = np.asarray(X, np.float64)
+    a, b = X @ np.asarray(w_g).T, X @ np.asarray(w_u).T
+    dh = dO @ np.asarray(w_d)
+    da, db = dh * mo.silu_grad(a), dh * mo.silu(a)
+    return da @ w_g + db @ w_u, da.T @ X, db.T @ X, dO.T @ (mo.silu(a) * b)
+
+
+def _swb_dx_no_up(X, w_g, w_u, w_d, dO):
+    dX, gg, gu, gd = _orig["swiglu_backward"](X, w_g, w_u, w_d, dO)
+    X = np.asarray(X, np.float64)
+    a = X @ np.asarray(w_g).T
+    db = (dO @ np.asarray(w_d)) * mo.silu(a)
+    return dX - db @ np.asarray(w_u), gg, gu, gd
+
+
+def _swb_swapped(X, w_g, w_u, w_d, dO):
+    dX, gg, gu, gd = _orig["swiglu_backward"](X, w_g, w_u, w_d, dO)
+    return dX, gu, gg, gd
+
+
+def _swb_down_transposed(X, w_g, w_u, w_d, dO):
+    dX, gg, gu, gd = _orig["swiglu_backward"](X, w_g, w_u, w_d, dO)
+    return dX, gg, gu, np.resize(gd.T, gd.shape)
+
+
+def _rb_no_renorm_term(p, idx, g, dgate, f, d_aux, renormalize=True, scoring="softmax"):
+    if renormalize:
+        S = np.take_along_axis(p, idx.astype(np.int64), axis=1).sum(axis=1, keepdims=True)
+        return _orig["router_backward"](p, idx, g, dgate / S, f, d_aux, False, scoring)
+    return _orig["router_backward"](p, idx, g, dgate, f, d_aux, renormalize, scoring)
+
+
+def _rb_no_aux(p, idx, g, dgate, f, d_aux, renormalize=True, scoring="softmax"):
+    return _orig["router_backward"](p, idx, g, dgate, f, 0.0, renormalize, scoring)
+
+
+def _rb_aux_without_E(p, idx, g, dgate, f, d_aux, renormalize=True, scoring="softmax"):
+    return _orig["router_backward"](p, idx, g, dgate, f, d_aux / p.shape[1], renormalize, scoring)
+
+
+def _rb_softmax_sign(p, idx, g, dgate, f, d_aux, renormalize=True, scoring="softmax"):
+    dr = _orig["router_backward"](p, idx, g, dgate, f, d_aux, renormalize, scoring)
+    if scoring != "softmax":
+        return dr
+    # p * (dp + sum p dp) instead of p * (dp - sum p dp)
+    dp = dr / p + 0.0
+    c = np.sum(p * dp, axis=1, keepdims=True) / (1.0 - np.sum(p * p, axis=1, keepdims=True))
+    return dr + 2.0 * p * c
+
+
+def _rb_sigmoid_no_1mp(p, idx, g, dgate, f, d_aux, renormalize=True, scoring="softmax"):
+    dr = _orig["router_backward"](p, idx, g, dgate, f, d_aux, renormalize, scoring)
+    return dr / (1.0 - p) if scoring == "sigmoid" else dr
+
+
+def _bwd_dropped_slots_count(x, w_r, experts, k, dy, d_aux=0.0, cap=-1, *a, **kw):
+    return _orig["moe_backward"](x, w_r, experts, k, dy, d_aux, -1, *a, **kw)
+
+
+def _bwd_no_router_dx(x, w_r, experts, k, dy, *a, **kw):
+    G = _orig["moe_backward"](x, w_r, experts, k, dy, *a, **kw)
+    G.dx = G.dx - G.dlogits @ np.asarray(w_r, np.float64)
+    return G
+
+
+def _bwd_sigmoid_bias_grad(x, w_r, experts, k, dy, *a, **kw):
+    G = _orig["moe_backward"](x, w_r, experts, k, dy, *a, **kw)
+    if G.db_r is not None:
+        G.db_r = G.dlogits.sum(axis=0)
+    return G
+
+
 MUTANTS = [
     ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
     ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
@@ -214,6 +297,14 @@ MUTANTS = [
     ("dequantize_rows", _dequant_columns),
     ("e2m1_decode", _e2m1_bias2), ("e2m1_decode", _e2m1_no_subnormal), ("e8m0_decode", _e8m0_bias128),
     ("dequantize_mx_rows", _mx_nibbles_swapped), ("dequantize_mx_rows", _mx_scales_transposed),
+    ("silu_grad", _silu_grad_sigmoid), ("silu_grad", _silu_grad_sign),
+    ("swiglu_backward", _swb_no_b), ("swiglu_backward", _swb_dx_no_up), ("swiglu_backward", _swb_swapped),
+    ("swiglu_backward", _swb_down_transposed),
+    ("router_backward", _rb_no_renorm_term), ("router_backward", _rb_no_aux),
+    ("router_backward", _rb_aux_without_E), ("router_backward", _rb_softmax_sign),
+    ("router_backward", _rb_sigmoid_no_1mp),
+    ("moe_backward", _bwd_dropped_slots_count), ("moe_backward", _bwd_no_router_dx),
+    ("moe_backward", _bwd_sigmoid_bias_grad),
 ]
 
 
