@@ -1,5 +1,5 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts FFN layer, forward pass.
+ * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts FFN layer, forward and backward.
  *
  * The layer (Zero to Frontier §13.1 "Why MoE", section "The MoE layer"; the routing
  * paragraph of the kevinluzbetak.com "Mixture-Of-Experts" page): for each token row x,
@@ -229,6 +229,57 @@ moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_r, c
                        float *f, float *P, float *aux,
                        int32_t *offsets, int32_t *row_token, int32_t *row_of,
                        void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
+
+/* ---------------------------------------------------------------- backward pass */
+
+/* Workspace bytes needed by moe_backward for this shape (validates it; native weights only). */
+moe_status moe_backward_workspace_bytes(const moe_shape *shape, size_t *bytes);
+
+/* Gradients of L = sum(dy * y) + d_aux * aux for the layer of moe_forward, with that forward's
+ * routing held fixed.  The choice of experts is a hard selection and carries no gradient: the
+ * router learns only through the weights of the experts it chose (AI Engineering Illustrated,
+ * "Inside the Router"); aux = E * sum_e f_e P_e adds d_aux * E * f_e / T to dL/dp[t, e] (f_e
+ * are counts).  Capacity drops are part of the routing: a dropped assignment passes no
+ * gradient, and a kept gate is not renormalised over the survivors.
+ *   x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down   as given to moe_forward
+ *   idx, gate, counts, offsets, row_token, row_of                moe_forward's outputs for them
+ *   dy      [T, d]        fp32   dL/dy
+ *   d_aux                 host   dL/daux (e.g. the auxiliary-loss weight)
+ * Outputs (fp32, overwritten; layouts of the corresponding inputs):
+ *   dx [T, d]; dw_r [E, d]; db_r [E] or NULL (the logit bias under softmax scoring gets
+ *   sum_t dL/dr_t; under sigmoid scoring the bias only picks experts and gets 0);
+ *   dw_gate, dw_up [E, d_e, d]; dw_down [E, d, d_e] (an expert with no rows gets zeros);
+ *   dws_gate, dws_up [d_e_shared, d], dws_down [d, d_e_shared] (required iff d_e_shared > 0);
+ *   dgate [T, k] or NULL: dL/dg per slot (0 for a dropped slot).
+ * Precision: the gate/up products are recomputed (bit-identical to the forward's); every
+ * product takes dtype operands with fp32 accumulation, so with MOE_BF16 dy, g * dy, dA and dB
+ * are rounded to bf16 before the products that consume them (as h is in the forward); router
+ * gradients, dW_r and the sums into dx are fp32.  Deterministic (fixed summation orders).
+ * Only wfmt = MOE_W_NATIVE (else MOE_ERR_UNSUPPORTED).
+ * stage_events: NULL or a host array of MOE_NUM_BSTAGES + 1 hipEvent_t, recorded as for
+ * moe_forward at the boundaries of the stages of moe_bstage.  For timing only. */
+typedef enum {
+  MOE_BSTAGE_PREP = 0,           /* padded layouts, transposed weights, dy to dtype */
+  MOE_BSTAGE_RECOMPUTE = 1,      /* gate/up products again: a, b, and h transposed */
+  MOE_BSTAGE_DOWN_BWD = 2,       /* u = dy W_d, dA, dB, dL/dg partial dots */
+  MOE_BSTAGE_ROUTER_BWD = 3,     /* dL/dg, dL/dr */
+  MOE_BSTAGE_DX_EXPERT = 4,      /* dX = dA W_g + dB W_u per row */
+  MOE_BSTAGE_WGRAD_DOWN = 5,     /* dW_d = (g dy)^T h per expert */
+  MOE_BSTAGE_WGRAD_GATE_UP = 6,  /* dW_g = dA^T x, dW_u = dB^T x per expert */
+  MOE_BSTAGE_SHARED = 7,         /* the shared expert's backward */
+  MOE_BSTAGE_DX = 8,             /* dx = dr W_r + sum of rows + shared; dW_r, db_r */
+  MOE_NUM_BSTAGES = 9
+} moe_bstage;
+
+moe_status moe_backward(const moe_shape *shape, const void *x, const void *w_r, const float *b_r,
+                        const void *w_gate, const void *w_up, const void *w_down,
+                        const void *ws_gate, const void *ws_up, const void *ws_down,
+                        const int32_t *idx, const float *gate, const int32_t *counts,
+                        const int32_t *offsets, const int32_t *row_token, const int32_t *row_of,
+                        const float *dy, float d_aux,
+                        float *dx, float *dw_r, float *db_r, float *dw_gate, float *dw_up, float *dw_down,
+                        float *dws_gate, float *dws_up, float *dws_down, float *dgate,
+                        void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,9 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_W_NATIVE, MOE_W_FP8_E4M3, MOE_W_MXFP4 = 0, 1, 2
 MOE_NUM_STAGES = 8
 STAGE_NAMES = ["router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
+MOE_NUM_BSTAGES = 9
+BSTAGE_NAMES = ["prep", "recompute", "down_bwd", "router_bwd", "dx_expert", "wgrad_down", "wgrad_gate_up",
+                "shared", "dx"]
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
 
@@ -45,6 +48,9 @@ SIGNATURES = {
     "moe_combine": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P]),
     "moe_forward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 9 + [C.POINTER(MoeWScales)] * 2 + [_P] * 11
                     + [_P, C.c_size_t, _P, _P]),
+    "moe_backward_workspace_bytes": (C.c_int, [C.POINTER(MoeShape), C.POINTER(C.c_size_t)]),
+    "moe_backward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 16 + [C.c_float] + [_P] * 10
+                     + [_P, C.c_size_t, _P, _P]),
 }
 
 _lib = None

@@ -28,9 +28,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 template <typename T> struct ElemOut;
 template <> struct ElemOut<uint16_t> {
   __device__ __forceinline__ static uint16_t from_f32(float v) { return (uint16_t)f32_to_bf16_bits(v); }
+  __device__ __forceinline__ static float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 };
 template <> struct ElemOut<float> {
   __device__ __forceinline__ static float from_f32(float v) { return v; }
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
 };
 
 // One 16x16 output tile step over 64 bytes of the contraction dimension.

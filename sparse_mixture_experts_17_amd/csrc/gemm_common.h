@@ -22,6 +22,17 @@ struct GemmArgs {
   int ksplit = 1;           // K chunks (plain product only): chunk c covers K steps
                             // [c K/ksplit, (c+1) K/ksplit) and writes C + c * split_stride
   size_t split_stride = 0;  // floats between the partial outputs of consecutive chunks
+  // K-grouped products: group g covers K columns [koffsets[g], koffsets[g+1]) of A
+  // [dense_rows, K] and B0 [N, K] and writes C + g * dense_rows * N
+  const int32_t* koffsets = nullptr;
+  // backward epilogues (see store_save_ab / store_dgrad)
+  float* ep_a = nullptr;             // [rows, N] fp32 gate pre-activations (written, or read)
+  float* ep_b = nullptr;             // [rows, N] fp32 up pre-activations
+  const float* ep_g = nullptr;       // [rows] gate of each row (NULL: 1)
+  void* ep_t = nullptr;              // transposed output, leading dimension ep_ldt
+  float* ep_part = nullptr;          // [rows, ep_npart] partial row dots (or NULL)
+  const int32_t* ep_poff = nullptr;  // [G+1] column of each group's first row in ep_t (NULL: row)
+  int ep_ldt = 0, ep_npart = 0;
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
@@ -134,6 +145,104 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
           }
         }
       }
+}
+
+// Column of row `row` (of group g) in a transposed backward operand: groups start on
+// 64-aligned columns so each group's K range is whole K steps; the gaps hold zeros.
+__device__ __forceinline__ int tcol(const GemmArgs& args, int g, int row) {
+  return args.ep_poff ? args.ep_poff[g] + (row - args.offsets[g]) : row;
+}
+
+// Backward recompute of the gate/up product: stores the pre-activations a, b (fp32,
+// row-major) and h = SiLU(a) * b -- rounded exactly as the forward rounds it -- transposed
+// into ep_t [N, ldt].  A lane's 4 rows are consecutive columns of ep_t.
+template <typename Cfg, typename Acc>
+__device__ __forceinline__ void store_save_ab(const GemmArgs& args, const Acc& acc0, const Acc& acc1, int wm,
+                                              int wn, int lane, int g, int nt, int row0, int rows) {
+  using T = typename Cfg::Elem;
+  const int N = args.N;
+  const size_t ldt = (size_t)args.ep_ldt;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+    const int rl = wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;     // first of the lane's 4 rows
+    if (rl >= rows) continue;
+    const int p0 = tcol(args, g, row0 + rl);
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) {
+      const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
+      T* ht = (T*)args.ep_t + (size_t)col * ldt + p0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (rl + q < rows) {
+          const size_t o = (size_t)(row0 + rl + q) * N + col;
+          const float a = acc0[i][j][q], b = acc1[i][j][q];
+          args.ep_a[o] = a;
+          args.ep_b[o] = b;
+          ht[q] = ElemOut<T>::from_f32(__fdividef(a, 1.f + __expf(-a)) * b);
+        }
+      }
+    }
+  }
+}
+
+// Backward of the down product, per element of u = dy_row W_d (the accumulator): with the
+// row's gate gr, dh = gr u; h = SiLU(a) b as the forward rounded it; s = sigmoid(a);
+// dA = dh b s (1 + a (1 - s)), dB = dh SiLU(a).  dA, dB go to C [rows, 2N] (dA in columns
+// [0, N), dB in [N, 2N)) and transposed to ep_t [2N, ldt]; the row dot sum_n h u over the
+// wave's columns goes to ep_part (dL/dg of the row is the sum over the row's parts).
+template <typename Cfg, typename Acc>
+__device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc0, int wm, int wn, int lane, int g,
+                                            int nt, int row0, int rows) {
+  using T = typename Cfg::Elem;
+  const int N = args.N;
+  const size_t ldt = (size_t)args.ep_ldt;
+  T* dab = (T*)args.C;
+  T* dabt = (T*)args.ep_t;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+    const int rl = wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    if (rl < rows) {
+      const int p0 = tcol(args, g, row0 + rl);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (rl + q < rows) {
+          const int row = row0 + rl + q;
+          const float gr = args.ep_g ? args.ep_g[row] : 1.f;
+#pragma unroll
+          for (int j = 0; j < Cfg::TN; ++j) {
+            const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
+            const size_t o = (size_t)row * N + col;
+            const float a = args.ep_a[o], b = args.ep_b[o], u = acc0[i][j][q];
+            const float silu = __fdividef(a, 1.f + __expf(-a));
+            const float h = ElemOut<T>::to_f32(ElemOut<T>::from_f32(silu * b));
+            part[q] = fmaf(h, u, part[q]);
+            const float sg = __fdividef(1.f, 1.f + __expf(-a));
+            const float dh = gr * u;
+            const T da = ElemOut<T>::from_f32(dh * b * sg * (1.f + a * (1.f - sg)));
+            const T db = ElemOut<T>::from_f32(dh * silu);
+            dab[(size_t)row * 2 * N + col] = da;
+            dab[(size_t)row * 2 * N + N + col] = db;
+            dabt[(size_t)col * ldt + p0 + q] = da;
+            dabt[(size_t)(N + col) * ldt + p0 + q] = db;
+          }
+        }
+      }
+    }
+    if (args.ep_part) {
+      // sum over the 16 columns held by lanes of one lane group (lane & 15)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) part[q] += __shfl_xor(part[q], o, kWave);
+      if ((lane & 15) == 0) {
+        const int slot = (nt * Cfg::BN_ + wn * Cfg::WTN) / Cfg::WTN;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (rl + q < rows) args.ep_part[(size_t)(row0 + rl + q) * args.ep_npart + slot] = part[q];
+      }
+    }
+  }
 }
 
 // Persistent grid: #CUs x occupancy blocks (at most one per tile), a multiple of the XCD count.

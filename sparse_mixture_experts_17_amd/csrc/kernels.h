@@ -65,4 +65,56 @@ hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, c
                             const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
                             int N, int K, float* O, int ksplit, size_t split_stride, hipStream_t stream);
 
+// ---- backward products (grouped_gemm_bwd.hip)
+// Gate/up product again with the gate/up tiles of `kind`: a_out, b_out [rows, N] fp32 (the
+// pre-activations) and hT [N, ldt] = h^T in dtype, row r of group g at column
+// poff[g] + r - offsets[g] (poff == NULL: column r).
+hipError_t launch_gemm_save_ab(GemmKind kind, int dtype, const void* A, const int32_t* a_rows, const void* Wg,
+                               const void* Wu, const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
+                               int max_tiles_m, int N, int K, float* a_out, float* b_out, void* hT,
+                               const int32_t* poff, int ldt, hipStream_t stream);
+// u = A_r WdT[e]^T (N = d_e, K = d; WdT = W_d transposed, [G, d_e, d]) with the SwiGLU
+// backward in the epilogue: dAB [rows, 2N] and dABT [2N, ldt] (dA then dB, dtype), and
+// part [rows, N / gemm_dgrad_part_cols] the partial dots sum_n h u (part may be NULL).
+// g_row [rows] scales u (NULL: 1).  Tile heights are the gate/up ones of `kind`.
+hipError_t launch_gemm_dgrad(GemmKind kind, int dtype, const void* A, const int32_t* a_rows, const void* WdT,
+                             const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
+                             int N, int K, const float* a_in, const float* b_in, const float* g_row, void* dAB,
+                             void* dABT, const int32_t* poff, int ldt, float* part, hipStream_t stream);
+int gemm_dgrad_part_cols(GemmKind kind, int N);
+// C[g] = A[:, K_g] B[:, K_g]^T for groups g < G, K_g = [koffsets[g], koffsets[g+1]) (multiples
+// of 64 in bf16, 32 in fp32); A [M, ld], B [N, ld] in dtype; C [G, M, N] fp32.
+hipError_t launch_gemm_kgrouped(int dtype, const void* A, const void* B, const int32_t* koffsets, int G, int M,
+                                int N, int ld, float* C, hipStream_t stream);
+
+// ---- backward, non-GEMM kernels (backward.hip)
+// poff [E+1]: padded column of each expert's first row (whole 64-column steps); g_row [R]:
+// gate of each kept row; koff_dense {0, dense_pad} when not NULL.
+hipError_t launch_bwd_layout(const int32_t* offsets, int E, const int32_t* row_of, const float* gate, int R,
+                             int32_t* poff, float* g_row, int dense_pad, int32_t* koff_dense, hipStream_t stream);
+// dst[b][c][coff + r] = src[b][r][c]  (src [B, Rn, C], dst [B, C, ldd]; Rn, C multiples of 64)
+hipError_t launch_transpose(int dtype, const void* src, int B, int Rn, int C, void* dst, int ldd, int coff,
+                            size_t dst_batch, hipStream_t stream);
+// dst [C, ldt] (dst_dtype): column p of expert e = source row rows[r] (or r) times scale[r]
+// (or 1) for r = offsets[e] + p - poff[e] < offsets[e+1], else 0; offsets == NULL: one group
+// of n_dense rows.  Columns [0, p_bound) are visited (p_bound <= ldt, multiples of 64).
+hipError_t launch_gather_t(int src_dtype, int dst_dtype, const void* src, int C, const int32_t* rows,
+                           const float* scale, const int32_t* offsets, const int32_t* poff, int E, int n_dense,
+                           int p_bound, void* dst, int ldt, hipStream_t stream);
+// zero columns [poff[e] + kept_e, poff[e+1]) (dense: [n_dense, pad_dense)) of dst [nrows, ldt]
+hipError_t launch_zero_gaps(int dtype, void* dst, int nrows, int ldt, const int32_t* offsets, const int32_t* poff,
+                            int E, int n_dense, int pad_dense, hipStream_t stream);
+hipError_t launch_to_bf16(const float* src, size_t n, void* dst, hipStream_t stream);
+// dr [T, E] = dL/dlogits; dgate [T, k] (may be NULL) = sum of each kept row's partial dots
+hipError_t launch_router_bwd(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E, int k,
+                             int renorm, int scoring, const int32_t* idx, const float* gate, const int32_t* row_of,
+                             const int32_t* counts, const float* part, int npart, float d_aux, float* dr,
+                             float* dgate, hipStream_t stream);
+// dw_r [E, d] = dr^T x; db_r [E] = sum_t dr (zeros when zero_bias), skipped when NULL
+hipError_t launch_dwr(int dtype, const float* dr, const void* x, int T, int d, int E, float* dw_r, float* db_r,
+                      int zero_bias, hipStream_t stream);
+// dx [T, d] = dr W_r + sum_j dX[row_of[t, j]] + dXs[t] (dXs may be NULL)
+hipError_t launch_dx(int dtype, const float* dr, const void* w_r, int T, int d, int E, int k, const float* dX,
+                     const int32_t* row_of, const float* dXs, float* dx, hipStream_t stream);
+
 }  // namespace moe

@@ -72,6 +72,60 @@ Layout layout(const moe_shape& s) {
   return L;
 }
 
+// Workspace of moe_backward.  Transposed operands of the weight-gradient products hold each
+// expert's rows from a 64-aligned column (ldt bounds the padded total).
+struct BwdLayout {
+  size_t poff, koff_dense, ts1, ts2, g_row, wdT, wguT, dyb, a, b, hT, dab, dabT, part, dr, dX, xT, doT;
+  size_t swdT, swguT, sa, sb, shT, sdab, sdabT, sdX, sdyT, sxT, total;
+  int ldt, ldts, npart;
+  GemmKind kind, skind;
+};
+
+BwdLayout bwd_layout(const moe_shape& s) {
+  BwdLayout L{};
+  const size_t es = elem_size(s.dtype);
+  const size_t E = (size_t)s.E, R = (size_t)s.T * (size_t)s.k, d = (size_t)s.d, de = (size_t)s.d_e;
+  const size_t des = (size_t)s.d_e_shared, T = (size_t)s.T;
+  L.kind = choose_kind(std::max<long long>((long long)R, 1), s.E, s.capacity);
+  L.skind = choose_kind(std::max<long long>((long long)T, 1), 1, -1);
+  L.ldt = (int)((R + 63 * E + 63) / 64 * 64);
+  L.ldts = (int)((T + 63) / 64 * 64);
+  L.npart = s.d_e / gemm_dgrad_part_cols(L.kind, s.d_e);
+  const size_t ldt = (size_t)L.ldt, ldts = (size_t)L.ldts;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  L.poff = take((E + 1) * sizeof(int32_t));
+  L.koff_dense = take(2 * sizeof(int32_t));
+  L.ts1 = take((E + 1) * sizeof(int32_t));
+  L.ts2 = take((E + 1) * sizeof(int32_t));
+  L.g_row = take(R * sizeof(float));
+  L.wdT = take(E * de * d * es);
+  L.wguT = take(E * d * 2 * de * es);
+  L.dyb = take(s.dtype == MOE_BF16 ? T * d * es : 0);
+  L.a = take(R * de * sizeof(float));
+  L.b = take(R * de * sizeof(float));
+  L.hT = take(de * ldt * es);
+  L.dab = take(R * 2 * de * es);
+  L.dabT = take(2 * de * ldt * es);
+  L.part = take(R * (size_t)L.npart * sizeof(float));
+  L.dr = take(T * E * sizeof(float));
+  L.dX = take(R * d * sizeof(float));
+  L.xT = take(d * ldt * es);
+  L.doT = take(d * ldt * es);
+  L.swdT = take(des * d * es);
+  L.swguT = take(d * 2 * des * es);
+  L.sa = take(T * des * sizeof(float));
+  L.sb = take(T * des * sizeof(float));
+  L.shT = take(des * ldts * es);
+  L.sdab = take(T * 2 * des * es);
+  L.sdabT = take(2 * des * ldts * es);
+  L.sdX = take(des > 0 ? T * d * sizeof(float) : 0);
+  L.sdyT = take(des > 0 ? d * ldts * es : 0);
+  L.sxT = take(des > 0 ? d * ldts * es : 0);
+  L.total = off;
+  return L;
+}
+
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_NULL;
   if (s->T < 0 || s->d < 1 || s->d_e < 1 || s->E < 1 || s->k < 1 || s->k > s->E || s->d_e_shared < 0)
@@ -328,6 +382,147 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
     MOE_HIP(launch_combine(at<float>(ws, L.o), row_of, gate, shared_out, y, s.T, s.d, s.k, L.ksplit, (size_t)R * s.d,
                            st));
   MOE_MARK(MOE_NUM_STAGES);
+#undef MOE_MARK
+  return MOE_OK;
+}
+
+moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->wfmt != MOE_W_NATIVE) return MOE_ERR_UNSUPPORTED;
+  *bytes = bwd_layout(*shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_shape* shape, const void* x, const void* w_r, const float* b_r, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                        const void* ws_down, const int32_t* idx, const float* gate, const int32_t* counts,
+                        const int32_t* offsets, const int32_t* row_token, const int32_t* row_of, const float* dy,
+                        float d_aux, float* dx, float* dw_r, float* db_r, float* dw_gate, float* dw_up,
+                        float* dw_down, float* dws_gate, float* dws_up, float* dws_down, float* dgate, void* ws,
+                        size_t ws_bytes, void* stream, void* const* stage_events) {
+  moe_status v = check_shape(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.wfmt != MOE_W_NATIVE) return MOE_ERR_UNSUPPORTED;
+  if (!w_r || !w_gate || !w_up || !w_down || !counts || !offsets || !dw_r || !dw_gate || !dw_up || !dw_down || !ws)
+    return MOE_ERR_NULL;
+  if (s.T > 0 && (!x || !idx || !gate || !row_token || !row_of || !dy || !dx)) return MOE_ERR_NULL;
+  if (s.d_e_shared > 0 && (!ws_gate || !ws_up || !ws_down || !dws_gate || !dws_up || !dws_down)) return MOE_ERR_NULL;
+  if (!isfinite(d_aux)) return MOE_ERR_SHAPE;
+  const BwdLayout L = bwd_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int next_stage = 0;
+  auto mark = [&](int upto) -> bool {
+    if (!stage_events) return true;
+    for (; next_stage <= upto; ++next_stage)
+      if (stage_events[next_stage] && hipEventRecord((hipEvent_t)stage_events[next_stage], st) != hipSuccess)
+        return false;
+    return true;
+  };
+#define MOE_MARK(i) \
+  if (!mark(i)) return MOE_ERR_HIP
+
+  const int T = s.T, d = s.d, de = s.d_e, des = s.d_e_shared, E = s.E;
+  const long long R = (long long)T * s.k;
+  const size_t es = elem_size(s.dtype);
+  const GemmKind kind = L.kind;
+  const int bm1 = gemm_block_m(kind, s.dtype, true, 0), bm2 = gemm_block_m(kind, s.dtype, false, 0);
+  const int tiles1 = max_m_tiles(R, E, s.capacity, bm1), tiles2 = max_m_tiles(R, E, s.capacity, bm2);
+  int32_t* poff = at<int32_t>(ws, L.poff);
+  int32_t* koff_dense = at<int32_t>(ws, L.koff_dense);
+  float* g_row = at<float>(ws, L.g_row);
+  int32_t* ts1 = at<int32_t>(ws, L.ts1);   // tile starts of the gate/up-height tiles
+  int32_t* ts2 = at<int32_t>(ws, L.ts2);   // ... and of the down-height tiles
+  const void* dyb = s.dtype == MOE_BF16 ? at<void>(ws, L.dyb) : (const void*)dy;
+  void* wdT = at<void>(ws, L.wdT);
+  void* wguT = at<void>(ws, L.wguT);
+  float* a = at<float>(ws, L.a);
+  float* b = at<float>(ws, L.b);
+  void* hT = at<void>(ws, L.hT);
+  void* dab = at<void>(ws, L.dab);
+  char* dabT = at<char>(ws, L.dabT);
+  float* part = at<float>(ws, L.part);
+  float* dr = at<float>(ws, L.dr);
+  float* dX = at<float>(ws, L.dX);
+
+  MOE_MARK(MOE_BSTAGE_PREP);
+  MOE_HIP(launch_bwd_layout(offsets, E, row_of, gate, (int)R, poff, g_row, L.ldts, koff_dense, st));
+  MOE_HIP(launch_transpose(s.dtype, w_down, E, d, de, wdT, d, 0, (size_t)de * d, st));
+  MOE_HIP(launch_transpose(s.dtype, w_gate, E, de, d, wguT, 2 * de, 0, (size_t)d * 2 * de, st));
+  MOE_HIP(launch_transpose(s.dtype, w_up, E, de, d, wguT, 2 * de, de, (size_t)d * 2 * de, st));
+  if (s.dtype == MOE_BF16) MOE_HIP(launch_to_bf16(dy, (size_t)T * d, at<void>(ws, L.dyb), st));
+  MOE_MARK(MOE_BSTAGE_RECOMPUTE);
+  if (T > 0) {
+    MOE_HIP(launch_tile_sched(offsets, E, bm1, ts1, bm2, ts2, st));
+    MOE_HIP(launch_gemm_save_ab(kind, s.dtype, x, row_token, w_gate, w_up, offsets, ts1, E, 0, tiles1, de, d, a, b,
+                                hT, poff, L.ldt, st));
+    MOE_HIP(launch_zero_gaps(s.dtype, hT, de, L.ldt, offsets, poff, E, 0, 0, st));
+  }
+  MOE_MARK(MOE_BSTAGE_DOWN_BWD);
+  if (T > 0) {
+    MOE_HIP(launch_gemm_dgrad(kind, s.dtype, dyb, row_token, wdT, offsets, ts1, E, 0, tiles1, de, d, a, b, g_row, dab,
+                              dabT, poff, L.ldt, part, st));
+    MOE_HIP(launch_zero_gaps(s.dtype, dabT, 2 * de, L.ldt, offsets, poff, E, 0, 0, st));
+  }
+  MOE_MARK(MOE_BSTAGE_ROUTER_BWD);
+  MOE_HIP(launch_router_bwd(s.dtype, x, w_r, b_r, T, d, E, s.k, s.renormalize, s.scoring, idx, gate, row_of, counts,
+                            part, L.npart, d_aux, dr, dgate, st));
+  MOE_MARK(MOE_BSTAGE_DX_EXPERT);
+  if (T > 0)
+    MOE_HIP(launch_gemm_down(kind, s.dtype, 0, dab, wguT, nullptr, offsets, ts2, E, 0, tiles2, d, 2 * de, dX, 1, 0,
+                             st));
+  MOE_MARK(MOE_BSTAGE_WGRAD_DOWN);
+  MOE_HIP(launch_gather_t(0, s.dtype, dy, d, row_token, g_row, offsets, poff, E, 0, L.ldt, at<void>(ws, L.doT), L.ldt,
+                          st));
+  MOE_HIP(launch_gemm_kgrouped(s.dtype, at<void>(ws, L.doT), hT, poff, E, d, de, L.ldt, dw_down, st));
+  MOE_MARK(MOE_BSTAGE_WGRAD_GATE_UP);
+  MOE_HIP(launch_gather_t(s.dtype, s.dtype, x, d, row_token, nullptr, offsets, poff, E, 0, L.ldt, at<void>(ws, L.xT),
+                          L.ldt, st));
+  MOE_HIP(launch_gemm_kgrouped(s.dtype, dabT, at<void>(ws, L.xT), poff, E, de, d, L.ldt, dw_gate, st));
+  MOE_HIP(launch_gemm_kgrouped(s.dtype, dabT + (size_t)de * L.ldt * es, at<void>(ws, L.xT), poff, E, de, d, L.ldt,
+                               dw_up, st));
+  MOE_MARK(MOE_BSTAGE_SHARED);
+  const float* sdX = nullptr;
+  if (des > 0) {
+    const GemmKind sk = L.skind;
+    const int sbm1 = gemm_block_m(sk, s.dtype, true, 0), sbm2 = gemm_block_m(sk, s.dtype, false, 0);
+    void* swdT = at<void>(ws, L.swdT);
+    void* swguT = at<void>(ws, L.swguT);
+    float* sa = at<float>(ws, L.sa);
+    float* sb = at<float>(ws, L.sb);
+    void* shT = at<void>(ws, L.shT);
+    void* sdab = at<void>(ws, L.sdab);
+    char* sdabT = at<char>(ws, L.sdabT);
+    MOE_HIP(launch_transpose(s.dtype, ws_down, 1, d, des, swdT, d, 0, 0, st));
+    MOE_HIP(launch_transpose(s.dtype, ws_gate, 1, des, d, swguT, 2 * des, 0, 0, st));
+    MOE_HIP(launch_transpose(s.dtype, ws_up, 1, des, d, swguT, 2 * des, des, 0, st));
+    if (T > 0) {
+      MOE_HIP(launch_gemm_save_ab(sk, s.dtype, x, nullptr, ws_gate, ws_up, nullptr, nullptr, 1, T, (T + sbm1 - 1) / sbm1,
+                                  des, d, sa, sb, shT, nullptr, L.ldts, st));
+      MOE_HIP(launch_gemm_dgrad(sk, s.dtype, dyb, nullptr, swdT, nullptr, nullptr, 1, T, (T + sbm1 - 1) / sbm1, des, d,
+                                sa, sb, nullptr, sdab, sdabT, nullptr, L.ldts, nullptr, st));
+      MOE_HIP(launch_gemm_down(sk, s.dtype, 0, sdab, swguT, nullptr, nullptr, nullptr, 1, T, (T + sbm2 - 1) / sbm2, d,
+                               2 * des, at<float>(ws, L.sdX), 1, 0, st));
+      sdX = at<float>(ws, L.sdX);
+    }
+    MOE_HIP(launch_zero_gaps(s.dtype, shT, des, L.ldts, nullptr, nullptr, 1, T, L.ldts, st));
+    MOE_HIP(launch_zero_gaps(s.dtype, sdabT, 2 * des, L.ldts, nullptr, nullptr, 1, T, L.ldts, st));
+    MOE_HIP(launch_gather_t(0, s.dtype, dy, d, nullptr, nullptr, nullptr, nullptr, 1, T, L.ldts, at<void>(ws, L.sdyT),
+                            L.ldts, st));
+    MOE_HIP(launch_gather_t(s.dtype, s.dtype, x, d, nullptr, nullptr, nullptr, nullptr, 1, T, L.ldts,
+                            at<void>(ws, L.sxT), L.ldts, st));
+    MOE_HIP(launch_gemm_kgrouped(s.dtype, at<void>(ws, L.sdyT), shT, koff_dense, 1, d, des, L.ldts, dws_down, st));
+    MOE_HIP(launch_gemm_kgrouped(s.dtype, sdabT, at<void>(ws, L.sxT), koff_dense, 1, des, d, L.ldts, dws_gate, st));
+    MOE_HIP(launch_gemm_kgrouped(s.dtype, sdabT + (size_t)des * L.ldts * es, at<void>(ws, L.sxT), koff_dense, 1, des,
+                                 d, L.ldts, dws_up, st));
+  }
+  MOE_MARK(MOE_BSTAGE_DX);
+  MOE_HIP(launch_dx(s.dtype, dr, w_r, T, d, E, s.k, dX, row_of, sdX, dx, st));
+  MOE_HIP(launch_dwr(s.dtype, dr, x, T, d, E, dw_r, db_r, s.scoring == MOE_SCORE_SIGMOID, st));
+  MOE_MARK(MOE_NUM_BSTAGES);
 #undef MOE_MARK
   return MOE_OK;
 }

@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "router_logits.h"
 
 namespace moe {
 
@@ -28,27 +29,6 @@ namespace moe {
 // Phase 2: each wave takes 4 tokens: softmax over E (lane l holds experts l + 64 q),
 //          k rounds of wave arg-max (ties -> lower index), gates, LDS histogram.
 // Phase 3: per-block partial sums of p (fixed order over waves) and histogram to global.
-
-// Contraction split of the router for E experts: 4 waves share the work.
-__host__ __device__ inline int router_ksplit(int E) {
-  const int groups = ((E + 15) / 16 + 3) / 4;
-  return groups == 1 ? 4 : (groups == 2 ? 2 : 1);
-}
-
-// Partial logits of NTL consecutive expert tiles over chunks [c0, c1) of 64 bytes.
-template <typename T, int NTL>
-__device__ __forceinline__ void router_tiles(const char* xrow, const char* const* wrow, int c0, int c1,
-                                             f32x4_t* acc) {
-#pragma unroll 8
-  for (int c = c0; c < c1; ++c) {
-    const u32x4_t a = *(const u32x4_t*)(xrow + (size_t)c * 64);
-#pragma unroll
-    for (int j = 0; j < NTL; ++j) {
-      const u32x4_t b = *(const u32x4_t*)(wrow[j] + (size_t)c * 64);
-      Mfma<T>::step(acc[j], a, b);
-    }
-  }
-}
 
 template <typename T>
 __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
@@ -72,48 +52,7 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
   for (int i = tid; i < E; i += 256) lhist[i] = 0;
 
   // ---- phase 1: logits
-  const int r16 = lane & 15, grp = lane >> 4;
-  const int tok = min(t0 + r16, T_ - 1);            // rows past T repeat row T-1; never used
-  const size_t row_bytes = (size_t)d * sizeof(T);
-  const char* xrow = (const char*)x + (size_t)tok * row_bytes + grp * 16;
-  const int nchunks = (int)(row_bytes / 64);
-  const int n_et = (E + 15) / 16;
-  const int kpart = wave % ksplit;
-  const int c0 = kpart * nchunks / ksplit, c1 = (kpart + 1) * nchunks / ksplit;
-  float* part = logits + kpart * TB * E;
-  for (int tb = (wave / ksplit) * 4; tb < n_et; tb += 4 * (4 / ksplit)) {
-    const int ntl = min(4, n_et - tb);
-    const char* wrow[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = min((tb + j) * 16 + r16, E - 1);
-      wrow[j] = (const char*)w_r + (size_t)e * row_bytes + grp * 16;
-    }
-    f32x4_t acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    switch (ntl) {
-      case 4: router_tiles<T, 4>(xrow, wrow, c0, c1, acc); break;
-      case 3: router_tiles<T, 3>(xrow, wrow, c0, c1, acc); break;
-      case 2: router_tiles<T, 2>(xrow, wrow, c0, c1, acc); break;
-      default: router_tiles<T, 1>(xrow, wrow, c0, c1, acc); break;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = (tb + j) * 16 + r16;
-      if (j < ntl && e < E) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[(grp * 4 + i) * E + e] = acc[j][i];
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < TB * E; i += 256) {          // fixed-order sum of the K parts, then bias
-    float v = logits[i];
-    for (int p = 1; p < ksplit; ++p) v += logits[p * TB * E + i];
-    logits[i] = v + ((b_r && !sigm) ? b_r[i % E] : 0.f);   // softmax: the bias is part of the logit
-  }
-  __syncthreads();
+  router_block_logits<T>(x, w_r, sigm ? nullptr : b_r, T_, d, E, t0, logits, wave, lane, tid);
 
   // ---- phase 2: scores and top-k, one token per wave at a time
   // Lane l holds experts e = 64 q + l.  sel = the selection score (logit for softmax, affinity

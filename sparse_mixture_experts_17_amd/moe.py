@@ -160,3 +160,69 @@ def forward(shape: MoeShape, x, w_r, b_r, w_gate, w_up, w_down, shared=None, out
                 out.gate, out.counts, out.kept, out.f, out.P, out.aux, out.offsets, out.row_token, out.row_of, out.ws,
                 stream, stage_events)
     return out
+
+
+# ------------------------------------------------------------------ backward
+
+def moe_backward_workspace_bytes(shape: MoeShape) -> int:
+    n = C.c_size_t(0)
+    check("moe_backward_workspace_bytes", lib().moe_backward_workspace_bytes(C.byref(shape), C.byref(n)))
+    return int(n.value)
+
+
+def moe_backward(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, idx, gate, counts, offsets,
+                 row_token, row_of, dy, d_aux, dx, dw_r, db_r, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down,
+                 dgate, ws, stream=None, stage_events=None) -> None:
+    """stage_events: None, or a ctypes array of MOE_NUM_BSTAGES + 1 hipEvent_t handles."""
+    check("moe_backward", lib().moe_backward(
+        C.byref(shape), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
+        _ptr(ws_up), _ptr(ws_down), _ptr(idx), _ptr(gate), _ptr(counts), _ptr(offsets), _ptr(row_token),
+        _ptr(row_of), _ptr(dy), C.c_float(d_aux), _ptr(dx), _ptr(dw_r), _ptr(db_r), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(dws_gate), _ptr(dws_up), _ptr(dws_down), _ptr(dgate), _ptr(ws), _nbytes(ws),
+        _stream(stream), stage_events))
+
+
+@dataclass
+class BackwardOutputs:
+    dx: torch.Tensor
+    dw_r: torch.Tensor
+    db_r: torch.Tensor | None
+    dw_gate: torch.Tensor
+    dw_up: torch.Tensor
+    dw_down: torch.Tensor
+    dshared: tuple | None
+    dgate: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_backward(shape: MoeShape, bias: bool, device="cuda") -> BackwardOutputs:
+    """Gradient tensors (fp32) and workspace for moe_backward (allocated by torch)."""
+    T, d, de, E, k, des = shape.T, shape.d, shape.d_e, shape.E, shape.k, shape.d_e_shared
+    f32 = torch.float32
+    dshared = None
+    if des > 0:
+        dshared = (torch.empty((des, d), dtype=f32, device=device), torch.empty((des, d), dtype=f32, device=device),
+                   torch.empty((d, des), dtype=f32, device=device))
+    return BackwardOutputs(
+        dx=torch.empty((T, d), dtype=f32, device=device),
+        dw_r=torch.empty((E, d), dtype=f32, device=device),
+        db_r=torch.empty(E, dtype=f32, device=device) if bias else None,
+        dw_gate=torch.empty((E, de, d), dtype=f32, device=device),
+        dw_up=torch.empty((E, de, d), dtype=f32, device=device),
+        dw_down=torch.empty((E, d, de), dtype=f32, device=device),
+        dshared=dshared,
+        dgate=torch.empty((T, k), dtype=f32, device=device),
+        ws=torch.empty(max(moe_backward_workspace_bytes(shape), 1), dtype=torch.uint8, device=device),
+    )
+
+
+def backward(shape: MoeShape, x, w_r, b_r, w_gate, w_up, w_down, fwd: ForwardOutputs, dy, d_aux: float = 0.0,
+             shared=None, out: BackwardOutputs | None = None, stream=None, stage_events=None) -> BackwardOutputs:
+    """Gradients of sum(dy * y) + d_aux * aux for the layer call that produced `fwd`."""
+    out = out or alloc_backward(shape, b_r is not None, x.device)
+    sg, su, sd = shared if shared is not None else (None, None, None)
+    dsg, dsu, dsd = out.dshared if out.dshared is not None else (None, None, None)
+    moe_backward(shape, x, w_r, b_r, w_gate, w_up, w_down, sg, su, sd, fwd.idx, fwd.gate, fwd.counts, fwd.offsets,
+                 fwd.row_token, fwd.row_of, dy, d_aux, out.dx, out.dw_r, out.db_r, out.dw_gate, out.dw_up,
+                 out.dw_down, dsg, dsu, dsd, out.dgate, out.ws, stream, stage_events)
+    return out

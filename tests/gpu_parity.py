@@ -10,6 +10,10 @@ Protocol
      oracle's dispatch of the GPU's idx; x_perm rows bit-identical to x rows.
   4. Output: max|y - y_oracle| / rms(y_oracle) <= 1e-4 (fp32) or 2e-2 (bf16), the
      oracle run with the GPU's routing; at full size on sampled tokens.
+  5. Backward: every gradient (dx, dW_r, db_r, dW_g, dW_u, dW_d, the shared expert's, dL/dg)
+     against the oracle's backward with the GPU's routing: ||G - G_oracle|| / ||G_oracle||
+     <= BWD_FROB and max|G - G_oracle| / max|G_oracle| <= BWD_PEAK per tensor and per expert
+     slice of the weight gradients.
 """
 from __future__ import annotations
 
@@ -26,6 +30,23 @@ from oracle import moe_oracle as mo
 from workloads.device import upload
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Backward bars, per gradient tensor and per expert slice of the weight gradients (an
+# expert's gradient is a sum over its rows, few for a small expert, so an element can be a
+# sum of a handful of products of heavy-tailed factors and a bar relative to the rms would
+# be set by the tail):
+#   frob: ||G - G_ref|| / ||G_ref||;   peak: max|G - G_ref| / max|G_ref|.
+# In bf16 a gradient's operands carry at most two roundings to bf16 each (2^-9 relative:
+# dy, then dA or dB; g dy; h), summed in fp32.  Over many terms the errors add like
+# 2^-9 x sqrt(#terms) x (typical term) against a largest element of several times
+# sqrt(#terms) x (typical term): a few 1e-3 for both measures, the rms one bar 1e-2.  For a
+# one-row expert the slice is an outer product and its largest element carries the
+# roundings of both factors in full, up to 4 x 2^-9 ~ 8e-3: the peak bar is 2e-2.  fp32
+# (fp32 operands, fp32 accumulation): 1e-5.
+BWD_FROB = {"f32": 1e-5, "bf16": 1e-2}
+BWD_PEAK = {"f32": 1e-5, "bf16": 2e-2}
+
+# dL/daux of the backward tests: the Switch auxiliary-loss weight (0.01)
+D_AUX = 0.01
 
 
 def log(msg):
@@ -165,3 +186,63 @@ def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
         f"near_ties={len(nt)} flipped={len(flipped)} dropped={dropped} ({time.time() - t0:.1f}s)")
     assert err <= TOL[w.dtype], err
     return dict(err=err, near_ties=len(nt), flipped=len(flipped), dropped=dropped, host=h)
+
+
+def run_backward(w: wl.Workload, seed=0, d_aux=D_AUX, repeat_check=False):
+    """Forward + backward on the GPU; every gradient against the oracle's backward with the
+    GPU's routing (after the forward's routing and dispatch checks)."""
+    t0 = time.time()
+    inp = wl.make_inputs(w, seed)
+    dev = upload(inp)
+    shape, cap = shape_of(w)
+    out = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+    dy_h = inp.dy()
+    dy = torch.from_numpy(dy_h).to(dev.x.device)
+    g = moe.backward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, out, dy, d_aux, dev.shared)
+    torch.cuda.synchronize()
+    names = ["dx", "dw_r", "dw_gate", "dw_up", "dw_down", "dgate"] + (["db_r"] if g.db_r is not None else [])
+    hg = {k: getattr(g, k).cpu().numpy() for k in names}
+    if g.dshared is not None:
+        for i, k in enumerate(["dws_gate", "dws_up", "dws_down"]):
+            hg[k] = g.dshared[i].cpu().numpy()
+    hf = {k: getattr(out, k).cpu().numpy() for k in
+          ["idx", "gate", "counts", "f", "P", "aux", "kept", "offsets", "row_token", "row_of"]}
+    if repeat_check:
+        g2 = moe.backward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, out, dy, d_aux,
+                          dev.shared)
+        torch.cuda.synchronize()
+        for k in names:
+            assert np.array_equal(getattr(g2, k).cpu().numpy().view(np.uint8), hg[k].view(np.uint8)), \
+                f"second backward differs in {k}"
+    del dev, out, g
+    torch.cuda.empty_cache()
+    check_routing(w, inp, hf["idx"], hf["gate"], hf["counts"], hf["f"], hf["P"], hf["aux"][0])
+    check_dispatch(w, hf["idx"], cap, hf["kept"], hf["offsets"], hf["row_token"], hf["row_of"])
+    ex = experts_f64(inp, range(w.E))
+    ref = mo.moe_backward(f64(inp.x, w), f64(inp.w_r, w), [ex[e] for e in range(w.E)], w.k, dy_h.astype(np.float64),
+                          d_aux, cap, inp.b_r, w.renormalize, shared_f64(inp), idx=hf["idx"], **router_kw(w))
+    want = {"dx": ref.dx, "dw_r": ref.dw_r, "dw_gate": ref.dw_gate, "dw_up": ref.dw_up, "dw_down": ref.dw_down,
+            "dgate": ref.dgate}
+    if "db_r" in hg:
+        want["db_r"] = ref.db_r
+    if ref.dshared is not None:
+        want.update(dws_gate=ref.dshared[0], dws_up=ref.dshared[1], dws_down=ref.dshared[2])
+    errs = {}
+    for k, v in want.items():
+        got = hg[k]
+        assert got.shape == v.shape, (k, got.shape, v.shape)
+        slices = list(range(v.shape[0])) if k in ("dw_gate", "dw_up", "dw_down") else [None]
+        frob = peak = 0.0
+        for e in slices:
+            a, b = (got, v) if e is None else (got[e], v[e])
+            if not np.any(b):                   # e.g. an expert with no rows: exactly zero
+                assert not np.any(a), (k, e)
+                continue
+            frob = max(frob, float(np.linalg.norm(a - b)) / float(np.linalg.norm(b)))
+            peak = max(peak, float(np.max(np.abs(a - b))) / float(np.max(np.abs(b))))
+        errs[k] = (frob, peak)
+    log(f"[{w.name} backward] T={w.T} d={w.d} d_e={w.d_e} E={w.E} k={w.k} cap={cap}: "
+        + " ".join(f"{k}={f:.1e}/{m:.1e}" for k, (f, m) in errs.items()) + f" ({time.time() - t0:.1f}s)")
+    for k, (f, m) in errs.items():
+        assert f <= BWD_FROB[w.dtype] and m <= BWD_PEAK[w.dtype], (k, f, m)
+    return errs

@@ -21,7 +21,8 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
     assert names == sorted(["moe_capacity", "moe_workspace_bytes", "moe_status_str", "moe_route", "moe_permute",
-                            "moe_expert_ffn", "moe_combine", "moe_forward"])
+                            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_backward_workspace_bytes",
+                            "moe_backward"])
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -182,3 +183,51 @@ def test_quantised_weights_need_scales(wfmt):
     assert _fwd(lib, s2, f2, 10, C.byref(full), C.byref(full)) == 4
     native = _shape()
     assert _ffn(lib, native, a, 0) == 4                                   # native: scales not needed
+
+
+def _bwd(lib, s, a, ws_bytes, d_aux=0.0):
+    """moe_backward with pointers a = x w_r b_r w_gate w_up w_down ws_gate ws_up ws_down idx gate counts
+    offsets row_token row_of dy | dx dw_r db_r dw_gate dw_up dw_down dws_gate dws_up dws_down dgate ws."""
+    return lib.moe_backward(C.byref(s), *a[:16], C.c_float(d_aux), *a[16:26], a[26], ws_bytes, None, None)
+
+
+def test_backward_rejects_null_small_workspace_and_quantised_weights():
+    lib = _lib.lib()
+    s = _shape()
+    need = moe.moe_backward_workspace_bytes(s)
+    assert need > moe.moe_workspace_bytes(s)
+    a = _args(27)
+    optional = (2, 6, 7, 8, 18, 22, 23, 24, 25)          # b_r, shared weights, db_r, shared grads, dgate
+    for i in optional:
+        a[i] = None
+    assert _bwd(lib, s, a, need - 1) == 4
+    for i in range(27):
+        if i in optional:
+            continue
+        b = list(a)
+        b[i] = None
+        assert _bwd(lib, s, b, need) == 1, i
+    # the shared expert's weights and gradients are required when d_e_shared > 0
+    s2 = _shape(d_e_shared=256)
+    need2 = moe.moe_backward_workspace_bytes(s2)
+    assert _bwd(lib, s2, a, need2) == 1
+    full = [FAKE] * 27
+    assert _bwd(lib, s2, full, need2 - 1) == 4
+    for i in (6, 7, 8, 22, 23, 24):
+        b = list(full)
+        b[i] = None
+        assert _bwd(lib, s2, b, need2) == 1, i
+    assert _bwd(lib, s, a, need, d_aux=float("nan")) == 2
+    # training runs on native weights only
+    for wfmt in (1, 2):
+        q = _shape(wfmt=wfmt, dtype=moe.MOE_BF16)
+        n = C.c_size_t(0)
+        assert lib.moe_backward_workspace_bytes(C.byref(q), C.byref(n)) == 3
+        assert _bwd(lib, q, full, 1 << 40) == 3
+    assert _bwd(lib, _shape(k=9), full, 1 << 40) == 2
+
+
+def test_backward_workspace_grows_with_shape():
+    small = moe.moe_backward_workspace_bytes(_shape())
+    assert moe.moe_backward_workspace_bytes(_shape(d_e_shared=256)) > small
+    assert moe.moe_backward_workspace_bytes(_shape(T=2 * _shape().T)) > small

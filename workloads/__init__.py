@@ -242,6 +242,10 @@ class Inputs:
             _draw(self.seed, (4, 2), (wl.d, wl.d_e_shared), 1.0 / wl.d_e_shared, wl.dtype),
         )
 
+    def dy(self) -> np.ndarray:
+        """Upstream gradient dL/dy [T, d] for the backward pass: float32 N(0, 1)."""
+        return _draw(self.seed, (5,), (self.wl.T, self.wl.d), 1.0, "f32")
+
     def experts_stacked(self, threads: int | None = None):
         """All routed experts stacked: W_g [E,d_e,d], W_u [E,d_e,d], W_d [E,d,d_e].
 
