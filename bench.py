@@ -5,7 +5,8 @@ One step = one moe_forward call (router, dispatch, grouped SwiGLU experts, combi
 over one batch of synthetic tokens already resident in device memory.  Default
 workload: the Mixtral 8x7B layer shape at a prefill batch of 4096 tokens (bf16
 weights and activations, fp32 accumulate).  A decode-batch line (16 tokens, same
-weights) rides along as "secondary".
+weights) rides along as "secondary", and the backward pass of the prefill call as
+"secondary_backward".
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize(); per-stage durations come from HIP events that the library
@@ -233,6 +234,75 @@ def secondary_line(dec, fmt):
     }
 
 
+def run_backward(info, steps, warmup, kernel_stage="dx_expert"):
+    """Time moe_backward on the forward's inputs and routing (same weights, dy ~ N(0, 1)).
+
+    As run_gpu: the timed region records HIP events only around `kernel_stage`; a second,
+    untimed pass marks every stage boundary.
+    """
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_17_amd as moe
+
+    w, shape, dev = info["w"], info["shape"], info["dev"]
+    fwd = moe.forward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, dev.shared)
+    dy = torch.from_numpy(info["inp"].dy()).to("cuda")
+    out = moe.alloc_backward(shape, dev.b_r is not None)
+    ev = HipEvents()
+    nst = moe._lib.MOE_NUM_BSTAGES
+    names = moe._lib.BSTAGE_NAMES
+    ks = names.index(kernel_stage)
+
+    def call(events=None):
+        moe.backward(shape, dev.x, dev.w_r, dev.b_r, dev.w_gate, dev.w_up, dev.w_down, fwd, dy, 0.01, dev.shared,
+                     out=out, stage_events=events)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(steps):
+        arr = (C.c_void_p * (nst + 1))()
+        pair = ev.create(2)
+        arr[ks], arr[ks + 1] = pair[0], pair[1]
+        marks.append((arr, pair))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s_ in range(steps):
+        call(marks[s_][0])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    kernel_ms = float(np.mean([ev.elapsed_ms(p[0], p[1]) for _, p in marks]))
+    for _, p in marks:
+        ev.destroy(p)
+    full = [ev.create(nst + 1) for _ in range(steps)]
+    for s_ in range(steps):
+        call(full[s_])
+    torch.cuda.synchronize()
+    stage_ms = np.array([[ev.elapsed_ms(e[i], e[i + 1]) for i in range(nst)] for e in full])
+    for e in full:
+        ev.destroy(e)
+    R = info["R_kept"]
+    ms = total_ms / steps
+    # products of the backward: gate/up recompute 4, u = dy W_d 2, dX 4, dW_d 2, dW_g + dW_u 4
+    # (x d x d_e FLOPs per kept row); the shared expert adds 16 x d x d_e_shared per token
+    flops = 16 * w.d * w.d_e * R + 16 * w.d * w.d_e_shared * w.T
+    k_flops = 4 * w.d * w.d_e * R                     # dX = dA W_g + dB W_u (one launch)
+    achieved = k_flops / (kernel_ms / 1e3) / 1e12
+    return {
+        "workload": w.name + " (backward)", "value": w.T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+        "stages_ms": {n: float(v) for n, v in zip(names, stage_ms.mean(axis=0))},
+        "tflops": flops / (ms / 1e3) / 1e12, "frac_mfma": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": "grouped_gemm dX = [dA|dB] [W_g;W_u] (large tiles)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w.name, "dx_expert"),
+                     "avg_ms": kernel_ms,
+                     "algorithmic": f"4*d*d_e FLOPs per kept row x {R} rows"},
+    }
+
+
 def cpu_baseline(info, target_s):
     """The CPU oracle, unchanged, on the first n tokens of the same workload."""
     import numpy as np
@@ -338,6 +408,10 @@ def main():
                          "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
             "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
         }
+    if not a.no_secondary and w.name == "mixtral_prefill":
+        print("[bench] secondary: backward pass on the same inputs", file=sys.stderr, flush=True)
+        line["secondary_backward"] = run_backward(info, a.steps, a.warmup)
+        torch.cuda.empty_cache()
     if not a.no_secondary and w.name == "mixtral_prefill":
         print("[bench] secondary: mixtral_decode_fp8 (FP8 E4M3 expert weights)", file=sys.stderr, flush=True)
         del info["dev"]
