@@ -370,28 +370,31 @@ hipError_t launch_router_bwd(int dtype, const void* x, const void* w_r, const fl
 
 // ------------------------------------------------------------------------------ dW_r, dx
 
-// dW_r [E, d] = dr^T x (fp32, tokens summed in ascending order), and for blocks of the first
-// column tile db_r[e] = sum_t dr[t, e] when db_r != NULL (zeros when zero_bias).
+// dW_r [E, d] = dr^T x and db_r[e] = sum_t dr[t, e] (fp32).  Tokens come in chunks of
+// kDwrChunk: block (c-tile, e-tile, chunk) sums its chunk's tokens in ascending order into
+// part [chunks, E, d] (and bpart [chunks, E]); dwr_reduce_kernel adds the chunks in order.
 // 64 x 64 output tile per block, 16 tokens per LDS step, 4 x 4 outputs per thread.
+constexpr int kDwrChunk = 256;
+
 template <typename T>
 __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dr, const T* __restrict__ x, int T_, int d,
-                                                  int E, float* __restrict__ dw_r, float* __restrict__ db_r,
-                                                  int zero_bias) {
+                                                  int E, float* __restrict__ part, float* __restrict__ bpart) {
   __shared__ float sA[16][64], sB[16][64];
   const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-  const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64, ch = blockIdx.z;
+  const int tbeg = ch * kDwrChunk, tend = min(T_, tbeg + kDwrChunk);
   float acc[4][4] = {};
   float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = 0; t0 < T_; t0 += 16) {
+  for (int t0 = tbeg; t0 < tend; t0 += 16) {
     {
       const int kk = tid / 16, cc = 4 * (tid % 16), t = t0 + kk;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = e0 + cc + q;
-        sA[kk][cc + q] = (t < T_ && e < E) ? dr[(size_t)t * E + e] : 0.f;
+        sA[kk][cc + q] = (t < tend && e < E) ? dr[(size_t)t * E + e] : 0.f;
       }
       float f[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < T_ && c0 + cc < d) Elem4<T>::to_f32(*(const typename Elem4<T>::V*)(x + (size_t)t * d + c0 + cc), f);
+      if (t < tend && c0 + cc < d) Elem4<T>::to_f32(*(const typename Elem4<T>::V*)(x + (size_t)t * d + c0 + cc), f);
 #pragma unroll
       for (int q = 0; q < 4; ++q) sB[kk][cc + q] = f[q];
     }
@@ -408,28 +411,57 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dr, 
     }
     __syncthreads();
   }
+  float* out = part + (size_t)ch * E * d;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = e0 + ty * 4 + i;
     if (e >= E) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + tx * 4 + j;
-      if (c < d) dw_r[(size_t)e * d + c] = acc[i][j];
-    }
-    if (db_r && blockIdx.x == 0 && tx == 0) db_r[e] = zero_bias ? 0.f : bsum[i];
+    const int c = c0 + tx * 4;
+    if (c < d) *(float4*)(out + (size_t)e * d + c) = float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+    if (blockIdx.x == 0 && tx == 0) bpart[(size_t)ch * E + e] = bsum[i];
   }
 }
 
+// dw_r[i] = sum over chunks of part[ch][i] (i < E*d), db_r[e] likewise (zeros when zero_bias).
+__global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* __restrict__ part,
+                                                         const float* __restrict__ bpart, int nch, size_t n, int E,
+                                                         float* __restrict__ dw_r, float* __restrict__ db_r,
+                                                         int zero_bias) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n + (size_t)E; i += (size_t)gridDim.x * 256) {
+    if (i < n) {
+      float v = 0.f;
+      for (int ch = 0; ch < nch; ++ch) v += part[(size_t)ch * n + i];
+      dw_r[i] = v;
+    } else if (db_r) {
+      const size_t e = i - n;
+      float v = 0.f;
+      for (int ch = 0; ch < nch; ++ch) v += bpart[(size_t)ch * E + e];
+      db_r[e] = zero_bias ? 0.f : v;
+    }
+  }
+}
+
+size_t dwr_workspace_bytes(int T, int d, int E) {
+  const size_t nch = (size_t)(T + kDwrChunk - 1) / kDwrChunk;
+  return nch * (size_t)E * ((size_t)d + 1) * sizeof(float);
+}
+
 hipError_t launch_dwr(int dtype, const float* dr, const void* x, int T, int d, int E, float* dw_r, float* db_r,
-                      int zero_bias, hipStream_t stream) {
-  dim3 grid((d + 63) / 64, (E + 63) / 64);
-  if (dtype == 1)
-    hipLaunchKernelGGL(dwr_kernel<uint16_t>, grid, dim3(256), 0, stream, dr, (const uint16_t*)x, T, d, E, dw_r, db_r,
-                       zero_bias);
-  else
-    hipLaunchKernelGGL(dwr_kernel<float>, grid, dim3(256), 0, stream, dr, (const float*)x, T, d, E, dw_r, db_r,
-                       zero_bias);
+                      int zero_bias, float* part, hipStream_t stream) {
+  const int nch = (T + kDwrChunk - 1) / kDwrChunk;
+  float* bpart = part + (size_t)nch * E * d;
+  if (nch > 0) {
+    dim3 grid((d + 63) / 64, (E + 63) / 64, nch);
+    if (dtype == 1)
+      hipLaunchKernelGGL(dwr_kernel<uint16_t>, grid, dim3(256), 0, stream, dr, (const uint16_t*)x, T, d, E, part,
+                         bpart);
+    else
+      hipLaunchKernelGGL(dwr_kernel<float>, grid, dim3(256), 0, stream, dr, (const float*)x, T, d, E, part, bpart);
+  }
+  const size_t n = (size_t)E * d;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + E + 255) / 256, 4096);
+  hipLaunchKernelGGL(dwr_reduce_kernel, dim3(blocks), dim3(256), 0, stream, part, bpart, nch, n, E, dw_r, db_r,
+                     zero_bias);
   return hipGetLastError();
 }
 

@@ -147,6 +147,17 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
       }
 }
 
+// Four consecutive values of T as one 8-byte (bf16) or 16-byte (fp32) store.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    *(uint2*)p = uint2{(uint32_t)ElemOut<T>::from_f32(v[0]) | ((uint32_t)ElemOut<T>::from_f32(v[1]) << 16),
+                       (uint32_t)ElemOut<T>::from_f32(v[2]) | ((uint32_t)ElemOut<T>::from_f32(v[3]) << 16)};
+  } else {
+    *(float4*)p = float4{v[0], v[1], v[2], v[3]};
+  }
+}
+
 // Column of row `row` (of group g) in a transposed backward operand: groups start on
 // 64-aligned columns so each group's K range is whole K steps; the gaps hold zeros.
 __device__ __forceinline__ int tcol(const GemmArgs& args, int g, int row) {
@@ -155,7 +166,8 @@ __device__ __forceinline__ int tcol(const GemmArgs& args, int g, int row) {
 
 // Backward recompute of the gate/up product: stores the pre-activations a, b (fp32,
 // row-major) and h = SiLU(a) * b -- rounded exactly as the forward rounds it -- transposed
-// into ep_t [N, ldt].  A lane's 4 rows are consecutive columns of ep_t.
+// into ep_t [N, ldt].  A lane's 4 rows are 4 consecutive columns of ep_t (one store; the
+// first is a multiple of 4 because tiles and groups start on multiples of 4 rows).
 template <typename Cfg, typename Acc>
 __device__ __forceinline__ void store_save_ab(const GemmArgs& args, const Acc& acc0, const Acc& acc1, int wm,
                                               int wn, int lane, int g, int nt, int row0, int rows) {
@@ -171,15 +183,23 @@ __device__ __forceinline__ void store_save_ab(const GemmArgs& args, const Acc& a
     for (int j = 0; j < Cfg::TN; ++j) {
       const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
       T* ht = (T*)args.ep_t + (size_t)col * ldt + p0;
+      float h[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        const float a = acc0[i][j][q], b = acc1[i][j][q];
+        h[q] = __fdividef(a, 1.f + __expf(-a)) * b;
         if (rl + q < rows) {
           const size_t o = (size_t)(row0 + rl + q) * N + col;
-          const float a = acc0[i][j][q], b = acc1[i][j][q];
           args.ep_a[o] = a;
           args.ep_b[o] = b;
-          ht[q] = ElemOut<T>::from_f32(__fdividef(a, 1.f + __expf(-a)) * b);
         }
+      }
+      if (rl + 3 < rows) {
+        store4<T>(ht, h);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (rl + q < rows) ht[q] = ElemOut<T>::from_f32(h[q]);
       }
     }
   }
@@ -204,33 +224,48 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
     float part[4] = {0.f, 0.f, 0.f, 0.f};
     if (rl < rows) {
       const int p0 = tcol(args, g, row0 + rl);
+      float gr[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (rl + q < rows) {
-          const int row = row0 + rl + q;
-          const float gr = args.ep_g ? args.ep_g[row] : 1.f;
+      for (int q = 0; q < 4; ++q) gr[q] = rl + q < rows && args.ep_g ? args.ep_g[row0 + rl + q] : 1.f;
 #pragma unroll
-          for (int j = 0; j < Cfg::TN; ++j) {
-            const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
+      for (int j = 0; j < Cfg::TN; ++j) {
+        const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
+        float da[4] = {0.f, 0.f, 0.f, 0.f}, db[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (rl + q < rows) {
+            const int row = row0 + rl + q;
             const size_t o = (size_t)row * N + col;
             const float a = args.ep_a[o], b = args.ep_b[o], u = acc0[i][j][q];
             const float silu = __fdividef(a, 1.f + __expf(-a));
             const float h = ElemOut<T>::to_f32(ElemOut<T>::from_f32(silu * b));
             part[q] = fmaf(h, u, part[q]);
             const float sg = __fdividef(1.f, 1.f + __expf(-a));
-            const float dh = gr * u;
-            const T da = ElemOut<T>::from_f32(dh * b * sg * (1.f + a * (1.f - sg)));
-            const T db = ElemOut<T>::from_f32(dh * silu);
-            dab[(size_t)row * 2 * N + col] = da;
-            dab[(size_t)row * 2 * N + N + col] = db;
-            dabt[(size_t)col * ldt + p0 + q] = da;
-            dabt[(size_t)(N + col) * ldt + p0 + q] = db;
+            const float dh = gr[q] * u;
+            da[q] = dh * b * sg * (1.f + a * (1.f - sg));
+            db[q] = dh * silu;
+            dab[(size_t)row * 2 * N + col] = ElemOut<T>::from_f32(da[q]);
+            dab[(size_t)row * 2 * N + N + col] = ElemOut<T>::from_f32(db[q]);
           }
+        }
+        T* ta = dabt + (size_t)col * ldt + p0;
+        T* tb = dabt + (size_t)(N + col) * ldt + p0;
+        if (rl + 3 < rows) {
+          store4<T>(ta, da);
+          store4<T>(tb, db);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (rl + q < rows) {
+              ta[q] = ElemOut<T>::from_f32(da[q]);
+              tb[q] = ElemOut<T>::from_f32(db[q]);
+            }
         }
       }
     }
     if (args.ep_part) {
-      // sum over the 16 columns held by lanes of one lane group (lane & 15)
+      // sum over the 16 columns held by one lane group (the group's 16 lanes share rl, so
+      // they are active or inactive together)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll

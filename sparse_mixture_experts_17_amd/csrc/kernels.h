@@ -110,9 +110,11 @@ hipError_t launch_router_bwd(int dtype, const void* x, const void* w_r, const fl
                              int renorm, int scoring, const int32_t* idx, const float* gate, const int32_t* row_of,
                              const int32_t* counts, const float* part, int npart, float d_aux, float* dr,
                              float* dgate, hipStream_t stream);
-// dw_r [E, d] = dr^T x; db_r [E] = sum_t dr (zeros when zero_bias), skipped when NULL
+// dw_r [E, d] = dr^T x; db_r [E] = sum_t dr (zeros when zero_bias), skipped when NULL;
+// part: scratch of dwr_workspace_bytes(T, d, E)
+size_t dwr_workspace_bytes(int T, int d, int E);
 hipError_t launch_dwr(int dtype, const float* dr, const void* x, int T, int d, int E, float* dw_r, float* db_r,
-                      int zero_bias, hipStream_t stream);
+                      int zero_bias, float* part, hipStream_t stream);
 // dx [T, d] = dr W_r + sum_j dX[row_of[t, j]] + dXs[t] (dXs may be NULL)
 hipError_t launch_dx(int dtype, const float* dr, const void* w_r, int T, int d, int E, int k, const float* dX,
                      const int32_t* row_of, const float* dXs, float* dx, hipStream_t stream);

@@ -76,7 +76,7 @@ Layout layout(const moe_shape& s) {
 // expert's rows from a 64-aligned column (ldt bounds the padded total).
 struct BwdLayout {
   size_t poff, koff_dense, ts1, ts2, g_row, wdT, wguT, dyb, a, b, hT, dab, dabT, part, dr, dX, xT, doT;
-  size_t swdT, swguT, sa, sb, shT, sdab, sdabT, sdX, sdyT, sxT, total;
+  size_t swdT, swguT, sa, sb, shT, sdab, sdabT, sdX, sdyT, sxT, dwr_part, total;
   int ldt, ldts, npart;
   GemmKind kind, skind;
 };
@@ -122,6 +122,7 @@ BwdLayout bwd_layout(const moe_shape& s) {
   L.sdX = take(des > 0 ? T * d * sizeof(float) : 0);
   L.sdyT = take(des > 0 ? d * ldts * es : 0);
   L.sxT = take(des > 0 ? d * ldts * es : 0);
+  L.dwr_part = take(dwr_workspace_bytes(s.T, s.d, s.E));
   L.total = off;
   return L;
 }
@@ -521,7 +522,8 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const void* w_r, 
   }
   MOE_MARK(MOE_BSTAGE_DX);
   MOE_HIP(launch_dx(s.dtype, dr, w_r, T, d, E, s.k, dX, row_of, sdX, dx, st));
-  MOE_HIP(launch_dwr(s.dtype, dr, x, T, d, E, dw_r, db_r, s.scoring == MOE_SCORE_SIGMOID, st));
+  MOE_HIP(launch_dwr(s.dtype, dr, x, T, d, E, dw_r, db_r, s.scoring == MOE_SCORE_SIGMOID, at<float>(ws, L.dwr_part),
+                     st));
   MOE_MARK(MOE_NUM_BSTAGES);
 #undef MOE_MARK
   return MOE_OK;
