@@ -237,7 +237,7 @@ moe_status moe_backward_workspace_bytes(const moe_shape *shape, size_t *bytes);
 
 /* Gradients of L = sum(dy * y) + d_aux * aux for the layer of moe_forward, with that forward's
  * routing held fixed.  The choice of experts is a hard selection and carries no gradient: the
- * router learns only through the weights of the experts it chose (AI Engineering Illustrated,
+ * router learns only through the weights of the experts it chose (Moatlab AI-064,
  * "Inside the Router"); aux = E * sum_e f_e P_e adds d_aux * E * f_e / T to dL/dp[t, e] (f_e
  * are counts).  Capacity drops are part of the routing: a dropped assignment passes no
  * gradient, and a kept gate is not renormalised over the survivors.

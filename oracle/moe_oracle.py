@@ -37,7 +37,7 @@ in the design notes of the repository):
     the statistics.
   * backward: the routing (expert choice and capacity drops) and f are constants;
     gradients reach the router only through the chosen gates and through P in
-    aux (AI Engineering Illustrated, "Inside the Router").
+    aux (Moatlab AI-064, "Inside the Router").
 """
 from __future__ import annotations
 
@@ -494,8 +494,8 @@ def router_backward(p: np.ndarray, idx: np.ndarray, g: np.ndarray, dgate: np.nda
     experts held fixed.
 
     The top-k choice is a hard selection with no gradient; the gradient reaches the router
-    only through the weights of the chosen experts (AI Engineering Illustrated, "Inside
-    the Router").  Steps:
+    only through the weights of the chosen experts (Moatlab AI-064, "Inside the
+    Router").  Steps:
       * renormalised gates g_j = p_{K_j} / S, S = sum_{i in K} p_i, give
         dp_{K_i} = (dg_i - sum_j dg_j g_j) / S; raw gates give dp_{K_i} = dg_i;
       * aux = E sum_e f_e P_e with P_e the mean of p over the T tokens and f_e fixed
@@ -528,7 +528,7 @@ def moe_backward(x, w_r, experts, k: int, dy, d_aux: float = 0.0, cap: int = -1,
     """Gradients of L = sum(dy * y) + d_aux * aux for the layer of ``moe_forward``.
 
     The routing -- which experts each token picked and which assignments capacity
-    dropped -- is a constant of the backward pass (AI Engineering Illustrated, "Inside the
+    dropped -- is a constant of the backward pass (Moatlab AI-064, "Inside the
     Router"); f, being counts, is constant too.  A kept slot (t, j) with expert e and row
     r passes g_tj dy_t into expert e's rows (dO_r) and gets dL/dg_tj = dy_t . O_r; a
     dropped slot passes nothing.  Expert gradients follow ``swiglu_backward`` and the

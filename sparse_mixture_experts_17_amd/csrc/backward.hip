@@ -2,7 +2,7 @@
 // weight-gradient products, transposes, the router backward, dW_r and the assembly of dx.
 //
 // The routing is held fixed: the top-k choice is a hard selection with no gradient, and the
-// router learns only through the weights of the chosen experts (AI Engineering Illustrated,
+// router learns only through the weights of the chosen experts (Moatlab AI-064,
 // "Inside the Router"); aux = E sum_e f_e P_e adds its P_e term (f_e are counts).
 #include <algorithm>
 

@@ -3,9 +3,9 @@
 //
 // The backward of an expert o = (SiLU(X W_g^T) * (X W_u^T)) W_d^T (Zero to Frontier §13.1
 // "Why MoE", section "The MoE layer") needs, besides plain products:
-//   * the gate/up product again, keeping a and b (recomputing them is cheaper than storing
-//     them in the forward pass, the trade that AI Engineering Illustrated's FlashAttention
-//     section calls recomputation);
+//   * the gate/up product again, keeping a and b (recomputing instead of storing in the
+//     forward pass, the trade of the FlashAttention backward in AI Engineering Illustrated's
+//     FlashAttention issue, "The trick that makes tiling legal");
 //   * u = dy W_d with the SwiGLU derivative applied in the epilogue;
 //   * K-grouped products for the weight gradients, whose contraction runs over each
 //     expert's rows.
