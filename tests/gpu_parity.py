@@ -218,6 +218,7 @@ def run_backward(w: wl.Workload, seed=0, d_aux=D_AUX, repeat_check=False):
     torch.cuda.empty_cache()
     check_routing(w, inp, hf["idx"], hf["gate"], hf["counts"], hf["f"], hf["P"], hf["aux"][0])
     check_dispatch(w, hf["idx"], cap, hf["kept"], hf["offsets"], hf["row_token"], hf["row_of"])
+    log(f"[{w.name} backward] GPU done ({time.time() - t0:.1f}s); oracle backward")
     ex = experts_f64(inp, range(w.E))
     ref = mo.moe_backward(f64(inp.x, w), f64(inp.w_r, w), [ex[e] for e in range(w.E)], w.k, dy_h.astype(np.float64),
                           d_aux, cap, inp.b_r, w.renormalize, shared_f64(inp), idx=hf["idx"], **router_kw(w))

@@ -79,3 +79,14 @@ def test_backward_zero_tokens(dtype):
     torch.cuda.synchronize()
     for t in [g.dw_r, g.dw_gate, g.dw_up, g.dw_down, *g.dshared]:
         assert torch.count_nonzero(t).item() == 0
+
+
+# Full sizes of the workloads whose backward the oracle finishes in about a minute: every
+# element of every gradient is compared (the oracle's backward runs whole, in float64).
+FULL = ["switch_capacity", "mixtral_decode", "mixtral_prefill"]
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", FULL)
+def test_backward_full_size(name):
+    gp.run_backward(wl.get(name))
