@@ -218,8 +218,8 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
   const size_t ldt = (size_t)args.ep_ldt;
   T* dab = (T*)args.C;
   T* dabt = (T*)args.ep_t;
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
+  static_for<0, Cfg::TM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
     const int rl = wm * Cfg::WTM + i * 16 + (lane >> 4) * 4;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
     if (rl < rows) {
@@ -227,8 +227,8 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
       float gr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) gr[q] = rl + q < rows && args.ep_g ? args.ep_g[row0 + rl + q] : 1.f;
-#pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j) {
+      static_for<0, Cfg::TN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
         const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
         float da[4] = {0.f, 0.f, 0.f, 0.f}, db[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -261,7 +261,7 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
               tb[q] = ElemOut<T>::from_f32(db[q]);
             }
         }
-      }
+      });
     }
     if (args.ep_part) {
       // sum over the 16 columns held by one lane group (the group's 16 lanes share rl, so
@@ -277,7 +277,7 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
           if (rl + q < rows) args.ep_part[(size_t)(row0 + rl + q) * args.ep_npart + slot] = part[q];
       }
     }
-  }
+  });
 }
 
 // Persistent grid: #CUs x occupancy blocks (at most one per tile), a multiple of the XCD count.

@@ -32,11 +32,12 @@ static hipError_t save_ab_kind(GemmKind kind, const GemmArgs& a, int max_tiles_m
 }
 
 // The down-product backward has the gate/up tile heights, so it shares their tile starts.
-// Its epilogue holds a, b, dA, dB per accumulator: 128-column tiles keep it in registers.
 template <typename T>
 static hipError_t dgrad_kind(GemmKind kind, const GemmArgs& a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
-    case kGemmLarge: return launch_bwd<T, 256, 128, 4, 2, false, 2, 3, 2>(a, max_tiles_m, s);
+    case kGemmLarge:
+      if (a.N % 256 == 0) return launch_bwd<T, 256, 256, 4, 2, false, 2, 3, 2>(a, max_tiles_m, s);
+      return launch_bwd<T, 256, 128, 4, 2, false, 2, 3, 2>(a, max_tiles_m, s);
     case kGemmStream: return launch_bwd<T, 160, 128, 2, 4, false, 3, 3, 2>(a, max_tiles_m, s);
     default: return launch_bwd<T, 16, 32, 1, 2, false, 4, 4, 2>(a, max_tiles_m, s);
   }
@@ -44,9 +45,8 @@ static hipError_t dgrad_kind(GemmKind kind, const GemmArgs& a, int max_tiles_m, 
 
 // columns per partial dot of the down-product backward (the wave tile width BN / WN)
 int gemm_dgrad_part_cols(GemmKind kind, int N) {
-  (void)N;
   switch (kind) {
-    case kGemmLarge: return 64;
+    case kGemmLarge: return N % 256 == 0 ? 128 : 64;
     case kGemmStream: return 32;
     default: return 16;
   }
