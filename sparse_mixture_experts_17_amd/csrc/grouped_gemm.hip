@@ -6,10 +6,11 @@ namespace moe {
 // ------------------------------------------------------------------------------ launch
 
 template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES,
-          int WF = 0>
+          int WF = 0, int KSUB = 1>
 static hipError_t launch_cfg(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
-  return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF>,
-                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF, 0>>(a, max_tiles_m, stream);
+  return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF, 0, KSUB>,
+                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF, 0, KSUB>>(a, max_tiles_m,
+                                                                                                  stream);
 }
 
 int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt) {
@@ -17,10 +18,14 @@ int gemm_block_m(GemmKind kind, int dtype, bool gated, int wfmt) {
   return kind == kGemmStream ? 160 : 16;
 }
 
-// LDS ring depth of the decode tiles: FP8 weights carry half the bytes per K step, so they
-// keep more steps in flight.
+// Decode tiles with quantised weights take KSUB 64-element sub-steps per LDS stage, so that a
+// weight row gives 128 contiguous bytes per stage (FP8: 2 x 64 bytes, MXFP4: 4 x 32 bytes).
 template <int WF>
-constexpr int kDecodeStages = 4;
+constexpr int kDecodeKsub = WF == 1 ? 2 : (WF == 2 ? 4 : 1);
+// LDS ring depth of the decode tiles.  With 4-bit weights more blocks per CU beat a deeper
+// ring (measured: 2 stages, 3 blocks per CU, best).
+template <int WF>
+constexpr int kDecodeStages = WF == 0 ? 4 : (WF == 2 ? 2 : 3);
 // weight rows per decode tile (gate/up: per matrix): 4-bit weights carry a quarter of the
 // bytes per K step, so their tiles are wider to keep the bytes per step up
 template <int WF, bool GATED>
@@ -50,14 +55,19 @@ static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipS
     default:
       // decode: a few rows per expert, 4-deep ring; the down product has half the weight
       // rows of gate/up, so narrower tiles give it as many blocks streaming in parallel
-      if constexpr (GATED) {
-        return launch_cfg<T, 16, kDecodeBN<WF, true>, 1, 4, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(
-            a, max_tiles_m, s);
-      } else {
-        if (a.N % kDecodeBN<WF, false> != 0) return launch_cfg<T, 16, 32, 1, 2, GATED, 4, 4, WF>(a, max_tiles_m, s);
-        return launch_cfg<T, 16, kDecodeBN<WF, false>, 1, 2, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF>(
-            a, max_tiles_m, s);
+      // (sub-steps need K, per K chunk, to be a whole number of stages; else one per stage)
+      if (a.K % (64 * kDecodeKsub<WF> * a.ksplit) != 0) {
+        if constexpr (GATED)
+          return launch_cfg<T, 16, kDecodeBN<WF, true>, 1, 4, GATED, 4, 4, WF, 1>(a, max_tiles_m, s);
+        else
+          return launch_cfg<T, 16, kDecodeBN<WF, false>, 1, 2, GATED, 4, 4, WF, 1>(a, max_tiles_m, s);
       }
+      if constexpr (GATED)
+        return launch_cfg<T, 16, kDecodeBN<WF, true>, 1, 4, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF,
+                          kDecodeKsub<WF>>(a, max_tiles_m, s);
+      else
+        return launch_cfg<T, 16, kDecodeBN<WF, false>, 1, 2, GATED, kDecodeStages<WF>, kDecodeStages<WF>, WF,
+                          kDecodeKsub<WF>>(a, max_tiles_m, s);
   }
 }
 

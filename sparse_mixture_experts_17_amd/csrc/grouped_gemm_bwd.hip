@@ -16,8 +16,8 @@ namespace moe {
 template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES, int EPI>
 static hipError_t launch_bwd(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
   return launch_kernel<GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, 0, EPI>,
-                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, 0, EPI>>(a, max_tiles_m,
-                                                                                                stream);
+                       grouped_gemm_kernel<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, 0, EPI, 1>>(a, max_tiles_m,
+                                                                                                   stream);
 }
 
 // The gate/up recompute uses the forward's gate/up tiles (same rows per tile, so the same

@@ -39,13 +39,18 @@ namespace moe {
 //   2  plain, backward of the down product: dA, dB from a, b and per-row partial dots (gemm_bwd.h)
 //   3  plain, K-grouped: group g contracts K columns [koffsets[g], koffsets[g+1]) of one A and
 //      one B into its own fp32 output (the weight gradients)
+// KSUB: 64-element K sub-steps per LDS stage.  Quantised decode tiles take several, so that
+// each weight row contributes 128 contiguous bytes per stage (a 64-element step of 4-bit
+// codes is only 32 bytes; the memory system serves few enough requests per second that
+// 32-byte requests cannot stream weights at HBM speed).
 template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES = STAGES,
-          int WF = 0, int EPI = 0>
+          int WF = 0, int EPI = 0, int KSUB = 1>
 struct GemmTile {
   using Elem = T;
   // weight format: 0 native (dtype), 1 FP8 E4M3 with row scales, 2 MXFP4 (E2M1, E8M0 per 32)
   static constexpr int WF_ = WF;
   static constexpr int EPI_ = EPI;
+  static constexpr int KSUB_ = KSUB;
   static constexpr int NT = WM * WN * kWave;
   static constexpr int BM_ = BM, BN_ = BN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -55,21 +60,22 @@ struct GemmTile {
   static constexpr int ROWB = 128;                                  // bytes of K per row per stage
   static constexpr int EPP = Mfma<T>::kElemsPerPiece;               // elements per 16-byte piece
   static constexpr int BKE = 8 * EPP;                               // elements of K per stage
-  static constexpr int PPR_B = WF == 1 ? 4 : (WF == 2 ? 2 : 8);    // 16-byte weight pieces per row per step
+  // 16-byte weight pieces per row per stage
+  static constexpr int PPR_B = (WF == 1 ? 4 : (WF == 2 ? 2 : 8)) * KSUB;
   static constexpr int ROWB_B = PPR_B * 16;
-  // LDS: a ring of STAGES activation slots, then a ring of BSTAGES weight slots
-  // MXFP4: each step's two E8M0 scale bytes per weight row follow the codes in the weight slot
-  // ([block][row], block-major like the global scale arrays)
-  static constexpr int S_BYTES = WF == 2 ? 2 * BROWS : 0;
-  static constexpr int A_SLOT = BM * ROWB, B_SLOT = BROWS * ROWB_B + S_BYTES;
-  static constexpr int B_BASE = STAGES * A_SLOT;
-  static constexpr int LDS = STAGES * A_SLOT + BSTAGES * B_SLOT;
+  // LDS: a ring of STAGES activation stages (KSUB slots of one 64-element sub-step each), then a
+  // ring of BSTAGES weight slots.  MXFP4: the stage's 2 KSUB E8M0 scale bytes per weight row
+  // follow the codes in the weight slot, [matrix][block][row of the matrix]
+  static constexpr int S_BYTES = WF == 2 ? 2 * KSUB * BROWS : 0;
+  static constexpr int A_SLOT = BM * ROWB, A_STAGE = KSUB * A_SLOT, B_SLOT = BROWS * ROWB_B + S_BYTES;
+  static constexpr int B_BASE = STAGES * A_STAGE;
+  static constexpr int LDS = STAGES * A_STAGE + BSTAGES * B_SLOT;
   static constexpr int NW = WM * WN;
   // 16-byte global -> LDS pieces per K step: activations, weights, MXFP4 scales.  Each wave
   // loads a contiguous equal share of every kind (PW_* pieces, IT_* instructions of up to 64
   // lanes), so every wave issues exactly LPS loads per step and "at most LPS * n outstanding"
   // leaves exactly n newer steps in flight for every wave.
-  static constexpr int P_A = BM * 8, P_B = BROWS * PPR_B, P_S = S_BYTES / 16;
+  static constexpr int P_A = BM * 8 * KSUB, P_B = BROWS * PPR_B, P_S = S_BYTES / 16;
   static constexpr int PW_A = P_A / NW, PW_B = P_B / NW, PW_S = P_S / NW;
   static constexpr int IT_A = (PW_A + kWave - 1) / kWave, IT_B = (PW_B + kWave - 1) / kWave;
   static constexpr int IT_S = P_S ? 1 : 0;
@@ -78,7 +84,9 @@ struct GemmTile {
   static constexpr int A_IT = IT_A, B_IT = IT_B;
   static_assert(P_A % NW == 0 && P_B % NW == 0 && P_S % NW == 0, "equal shares per wave");
   static_assert(NW % 2 == 0, "gate and up halves of the weight pieces split on a wave boundary");
-  static_assert(P_S == 0 || (PW_S <= kWave && (BN / 16) % PW_S == 0), "a wave's scale share is one matrix");
+  static_assert(P_S == 0 || (PW_S <= kWave && (2 * KSUB * (BN / 16)) % PW_S == 0),
+                "a wave's scale share is one matrix");
+  static_assert(KSUB == 1 || (WF != 0 && ROWB_B == 128 && EPI == 0), "sub-steps: 128-byte weight rows");
   static_assert(LPS * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(BSTAGES == STAGES || (STAGES == 2 && BSTAGES == 3), "weight ring: same depth, or 3 with 2");
   static_assert(LDS <= 160 * 1024, "LDS per workgroup");
@@ -151,15 +159,15 @@ __device__ __forceinline__ void issue_b(char* Bs, uint32_t kb, __amdgpu_buffer_r
   }
 }
 
-// MXFP4 scale bytes of one K step (two blocks of 32) for the tile's weight rows: the share
-// of wave w lies inside one (block, matrix) group of 16-row pieces.
+// MXFP4 scale bytes of one stage (2 KSUB blocks of 32) for the tile's weight rows, matrix
+// by matrix: the share of wave w lies inside one matrix.
 template <typename Cfg>
 __device__ __forceinline__ void issue_s(char* Ss, uint32_t kbs, __amdgpu_buffer_rsrc_t rsS0,
                                         __amdgpu_buffer_rsrc_t rsS1, uint32_t voffS, int wave, int lane) {
   if constexpr (Cfg::WF_ == 2) {
-    constexpr int PPM = Cfg::BN_ / 16;                            // pieces per matrix per block
+    constexpr int PPMS = 2 * Cfg::KSUB_ * (Cfg::BN_ / 16);         // pieces per matrix per stage
     const int q0 = wave * Cfg::PW_S;
-    const bool up = Cfg::NB == 2 && (q0 / PPM) % 2 == 1;
+    const bool up = Cfg::NB == 2 && q0 >= PPMS;
     auto* dst = (__attribute__((address_space(3))) void*)(Ss + q0 * 16);
     if (lane < Cfg::PW_S) {
       if (up)
@@ -168,6 +176,15 @@ __device__ __forceinline__ void issue_s(char* Ss, uint32_t kbs, __amdgpu_buffer_
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS0, dst, 16, voffS, kbs, 0, 0);
     }
   }
+}
+
+// LDS byte offset of 16-byte piece `c` of weight row r in a weight slot (rows of PPR_B pieces,
+// swizzled as tile_offsets places them).
+template <typename Cfg>
+__device__ __forceinline__ int b_piece(int r, int c) {
+  if constexpr (Cfg::PPR_B == 8) return swz(r, c);
+  else if constexpr (Cfg::PPR_B == 4) return swz64(r, c);
+  else return r * 32 + ((c ^ ((r >> 2) & 1)) << 4);
 }
 
 // Per-lane 32-bit buffer offsets of one tile's global -> LDS pieces.  Lane L of a wave's
@@ -180,18 +197,19 @@ __device__ __forceinline__ void tile_offsets(const GemmArgs& args, int wave, int
                                              uint32_t* voffB) {
 #pragma unroll
   for (int it = 0; it < Cfg::A_IT; ++it) {
-    const int q = min(wave * Cfg::PW_A + it * kWave + lane, Cfg::P_A - 1), r = q >> 3;
-    const int cl = (q & 7) ^ ((r >> 1) & 7);
+    const int q = min(wave * Cfg::PW_A + it * kWave + lane, Cfg::P_A - 1);
+    const int u = q / (Cfg::BM_ * 8), qa = q - u * (Cfg::BM_ * 8), r = qa >> 3;   // sub-step, row
+    const int cl = (qa & 7) ^ ((r >> 1) & 7);
     const int rr = min(r, rows - 1);
     const size_t arow = args.a_rows ? (size_t)args.a_rows[row0 + rr] : (size_t)rr;
-    voffA[it] = (uint32_t)(arow * row_stride + cl * 16);
+    voffA[it] = (uint32_t)(arow * row_stride + u * 128 + cl * 16);
   }
 #pragma unroll
   for (int it = 0; it < Cfg::B_IT; ++it) {
     const int q = min(wave * Cfg::PW_B + it * kWave + lane, Cfg::P_B - 1);
     const int r = q / Cfg::PPR_B;
-    const int cl = Cfg::WF_ == 1 ? (q & 3) ^ ((r >> 1) & 3)
-                                 : (Cfg::WF_ == 2 ? (q & 1) ^ ((r >> 2) & 1) : (q & 7) ^ ((r >> 1) & 7));
+    const int cl = Cfg::PPR_B == 8 ? (q & 7) ^ ((r >> 1) & 7)
+                                   : (Cfg::PPR_B == 4 ? (q & 3) ^ ((r >> 1) & 3) : (q & 1) ^ ((r >> 2) & 1));
     voffB[it] = (uint32_t)((Cfg::NB == 2 && r >= Cfg::BN_ ? r - Cfg::BN_ : r) * row_stride_b + cl * 16);
   }
 }
@@ -218,9 +236,10 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES, int WF, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, bool GATED, int STAGES, int BSTAGES, int WF, int EPI,
+          int KSUB>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF, EPI>;
+  using Cfg = GemmTile<T, BM, BN, WM, WN, GATED, STAGES, BSTAGES, WF, EPI, KSUB>;
   constexpr bool KGRP = EPI == 3;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, NB = Cfg::NB;
   constexpr int A_IT = Cfg::A_IT, B_IT = Cfg::B_IT, BKE = Cfg::BKE;
@@ -237,16 +256,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int xcd = blockIdx.x % kNumXcd, j0 = blockIdx.x / kNumXcd, bpx = gridDim.x / kNumXcd;
   const int lo = (int)((long long)live * xcd / kNumXcd);
   const int hi = (int)((long long)live * (xcd + 1) / kNumXcd);
-  const int nks = K / BKE / ksp;                      // K steps per chunk
+  const int nks = K / (BKE * KSUB) / ksp;             // LDS stages (K steps of BKE * KSUB) per chunk
   const size_t row_stride = (size_t)K * sizeof(T);   // bytes per row of A
   const size_t row_stride_b = WF == 1 ? (size_t)K : (WF == 2 ? (size_t)K / 2 : row_stride);   // per weight row
-  constexpr uint32_t KB_B = Cfg::ROWB_B;              // weight bytes per row per K step
+  constexpr uint32_t KB_B = Cfg::ROWB_B;              // weight bytes per row per stage
+  constexpr uint32_t KB_A = 128 * KSUB;               // activation bytes per row per stage
 
   for (int L = lo + j0; L < hi; L += bpx) {
     // consecutive work items are the K chunks of one output tile
     const int chunk = ksp > 1 ? L % ksp : 0;
     int g, nt, row0, rows, nk = nks;
-    size_t ks0 = (size_t)chunk * nks;                   // first K step of the chunk
+    size_t ks0 = (size_t)chunk * nks;                   // first stage of the chunk
     size_t c_off = (size_t)chunk * args.split_stride;   // output offset (elements)
     if constexpr (KGRP) {
       // group-major; inside a group n-tile-major, so consecutive tiles share the B tile
@@ -271,7 +291,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     // per-lane 32-bit offsets are fixed for the tile and the K step rides in the scalar offset.
     // (K-grouped: one B for every group.)
     const size_t brow0 = (KGRP ? 0 : (size_t)g * N) + (size_t)nt * BN;
-    const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride) + ks0 * BKE * sizeof(T);
+    const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride) + ks0 * KB_A;
     const char* B0b = (const char*)args.B0 + brow0 * row_stride_b + ks0 * KB_B;
     const char* B1b = GATED ? (const char*)args.B1 + brow0 * row_stride_b + ks0 * KB_B : B0b;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, 0x7fffffff, kBufFlags);
@@ -280,26 +300,27 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 
     uint32_t voffA[A_IT], voffB[B_IT];
     tile_offsets<Cfg>(args, wave, lane, row0, rows, row_stride, row_stride_b, voffA, voffB);
-    auto a_slot = [&](int s) { return lds + s * Cfg::A_SLOT; };
+    auto a_slot = [&](int s) { return lds + s * Cfg::A_STAGE; };
     auto b_slot = [&](int s) { return lds + Cfg::B_BASE + s * Cfg::B_SLOT; };
-    // MXFP4 block scales: [G, K/32, N] bytes per matrix; lane q of wave 0 loads 16 rows of one
-    // block of one matrix (see issue_s), each step advancing two blocks
+    // MXFP4 block scales: [G, K/32, N] bytes per matrix; each lane loads 16 rows of one block
+    // of one matrix (see issue_s), each stage advancing 2 KSUB blocks
     __amdgpu_buffer_rsrc_t rsS0 = rsB0, rsS1 = rsB1;
     uint32_t voffS = 0;
     if constexpr (WF == 2) {
-      const size_t gs = (size_t)g * (K / 32) * N + ks0 * 2 * N;   // two blocks per K step
+      const size_t gs = (size_t)g * (K / 32) * N + ks0 * 2 * KSUB * N;
       rsS0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S0 + gs), 0, 0x7fffffff, kBufFlags);
       rsS1 = GATED ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S1 + gs), 0, 0x7fffffff, kBufFlags)
                    : rsS0;
-      constexpr int PPM = BN / 16;
-      const int qs = wave * Cfg::PW_S + min(lane, Cfg::PW_S - 1);   // [block c][matrix][piece p]
-      const int c = qs / (NB * PPM), p = qs % PPM;
+      constexpr int PPM = BN / 16, PPMS = 2 * KSUB * PPM;
+      const int qs = wave * Cfg::PW_S + min(lane, Cfg::PW_S - 1);   // [matrix][block c][piece p]
+      const int c = (qs % PPMS) / PPM, p = qs % PPM;
       voffS = (uint32_t)(c * N + nt * BN + 16 * p);
     }
-    // one K step of weights (codes, and MXFP4 scales) into weight slot s
+    // one stage of weights (codes, and MXFP4 scales) into weight slot s
     auto issue_w = [&](int s, int ks) {
       issue_b<Cfg>(b_slot(s), (uint32_t)ks * KB_B, rsB0, rsB1, voffB, wave, lane);
-      issue_s<Cfg>(b_slot(s) + Cfg::BROWS * Cfg::ROWB_B, (uint32_t)ks * 2 * N, rsS0, rsS1, voffS, wave, lane);
+      issue_s<Cfg>(b_slot(s) + Cfg::BROWS * Cfg::ROWB_B, (uint32_t)ks * 2 * KSUB * N, rsS0, rsS1, voffS, wave,
+                   lane);
     };
 
     f32x4_t acc0[TM][TN], acc1[TM][TN];
@@ -318,65 +339,76 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       const int ra = wm * Cfg::WTM + (lane & 15);
       const int rb = wn * Cfg::WTN + (lane & 15);
       if constexpr (WF == 2) {
-        // MXFP4 weights: an 8-byte LDS read per weight subtile gives lane group q = lane >> 4
-        // the codes of K elements 16q .. 16q+15 of the step (rows of 32 bytes, 16-byte pieces
-        // swizzled by row quad), and one byte the scale of their block (q >> 1); the same K
-        // permutation as FP8 pairs them with A pieces 2q + h.
+        // MXFP4 weights: per 64-element sub-step u, an 8-byte LDS read per weight subtile gives
+        // lane group q = lane >> 4 the codes of K elements 16q .. 16q+15 of the sub-step
+        // (32 bytes of a row: pieces 2u and 2u+1), and one byte the scale of their block
+        // (2u + (q >> 1)); the same K permutation as FP8 pairs them with A pieces 2q + h.
         const int q = lane >> 4;
         const char* Ss = Bs + Cfg::BROWS * Cfg::ROWB_B;
-        uint32_t raw[TN * NB][2];
-        float sc[TN * NB];
 #pragma unroll
-        for (int j = 0; j < TN * NB; ++j) {
-          const int r = (j < TN ? 0 : BN - TN * 16) + rb + j * 16;
-          const uint2 v = *(const uint2*)(Bs + r * 32 + ((((q >> 1) ^ ((r >> 2) & 1)) << 4) | ((q & 1) << 3)));
-          raw[j][0] = v.x;
-          raw[j][1] = v.y;
-          sc[j] = e8m0_to_f32(*(const uint8_t*)(Ss + (q >> 1) * Cfg::BROWS + r));
-        }
+        for (int u = 0; u < KSUB; ++u) {
+          const char* Au = As + u * Cfg::A_SLOT;
+          uint32_t raw[TN * NB][2];
+          float sc[TN * NB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4_t b[TN * NB];
+          for (int j = 0; j < TN * NB; ++j) {
+            const int m = j < TN ? 0 : 1, rm = rb + (j - m * TN) * 16;   // matrix, row in it
+            const int r = m * BN + rm;
+            const uint2 v = *(const uint2*)(Bs + b_piece<Cfg>(r, 2 * u + (q >> 1)) + ((q & 1) << 3));
+            raw[j][0] = v.x;
+            raw[j][1] = v.y;
+            sc[j] = e8m0_to_f32(*(const uint8_t*)(Ss + (m * 2 * KSUB + 2 * u + (q >> 1)) * BN + rm));
+          }
 #pragma unroll
-          for (int j = 0; j < TN * NB; ++j) b[j] = e2m1x8_to_bf16(raw[j][h], sc[j]);
+          for (int h = 0; h < 2; ++h) {
+            u32x4_t b[TN * NB];
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {
-              const u32x4_t a = *(const u32x4_t*)(As + swz(ra + i * 16, 2 * (lane >> 4) + h));
+            for (int j = 0; j < TN * NB; ++j) b[j] = e2m1x8_to_bf16(raw[j][h], sc[j]);
 #pragma unroll
-              for (int j = 0; j < TN; ++j) {
-                Mfma<T>::step(acc0[i][j], a, b[j]);
-                if constexpr (GATED) Mfma<T>::step(acc1[i][j], a, b[TN + j]);
+            for (int i = 0; i < TM; ++i) {
+              if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {
+                const u32x4_t a = *(const u32x4_t*)(Au + swz(ra + i * 16, 2 * (lane >> 4) + h));
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                  Mfma<T>::step(acc0[i][j], a, b[j]);
+                  if constexpr (GATED) Mfma<T>::step(acc1[i][j], a, b[TN + j]);
+                }
               }
             }
           }
         }
         return;
       } else if constexpr (WF == 1) {
-        // FP8 weights: one 16-byte LDS read per weight subtile gives lane group q = lane >> 4
-        // the codes of K elements 16q .. 16q+15 of the step; the MFMA of half h takes
-        // 16q + 8h .. 16q + 8h + 7 from both operands (the same permutation of the
-        // contraction index on A and B leaves every dot product unchanged), so the A
-        // fragment of half h is 16-byte piece 2q + h of the activation row.
-        u32x4_t raw[TN * NB];
+        // FP8 weights: per 64-element sub-step u, one 16-byte LDS read per weight subtile gives
+        // lane group q = lane >> 4 the codes of K elements 16q .. 16q+15 of the sub-step (piece
+        // 4u + q of the row); the MFMA of half h takes 16q + 8h .. 16q + 8h + 7 from both
+        // operands (the same permutation of the contraction index on A and B leaves every dot
+        // product unchanged), so the A fragment of half h is 16-byte piece 2q + h of the
+        // sub-step's activation row.
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          raw[j] = *(const u32x4_t*)(Bs + swz64(rb + j * 16, lane >> 4));
-          if constexpr (GATED) raw[TN + j] = *(const u32x4_t*)(Bs + swz64(BN + rb + j * 16, lane >> 4));
-        }
+        for (int u = 0; u < KSUB; ++u) {
+          const char* Au = As + u * Cfg::A_SLOT;
+          u32x4_t raw[TN * NB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4_t b[TN * NB];
+          for (int j = 0; j < TN; ++j) {
+            raw[j] = *(const u32x4_t*)(Bs + b_piece<Cfg>(rb + j * 16, 4 * u + (lane >> 4)));
+            if constexpr (GATED)
+              raw[TN + j] = *(const u32x4_t*)(Bs + b_piece<Cfg>(BN + rb + j * 16, 4 * u + (lane >> 4)));
+          }
 #pragma unroll
-          for (int j = 0; j < TN * NB; ++j) b[j] = e4m3x8_to_bf16(raw[j][2 * h], raw[j][2 * h + 1]);
+          for (int h = 0; h < 2; ++h) {
+            u32x4_t b[TN * NB];
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {
-              const u32x4_t a = *(const u32x4_t*)(As + swz(ra + i * 16, 2 * (lane >> 4) + h));
+            for (int j = 0; j < TN * NB; ++j) b[j] = e4m3x8_to_bf16(raw[j][2 * h], raw[j][2 * h + 1]);
 #pragma unroll
-              for (int j = 0; j < TN; ++j) {
-                Mfma<T>::step(acc0[i][j], a, b[j]);
-                if constexpr (GATED) Mfma<T>::step(acc1[i][j], a, b[TN + j]);
+            for (int i = 0; i < TM; ++i) {
+              if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {
+                const u32x4_t a = *(const u32x4_t*)(Au + swz(ra + i * 16, 2 * (lane >> 4) + h));
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                  Mfma<T>::step(acc0[i][j], a, b[j]);
+                  if constexpr (GATED) Mfma<T>::step(acc1[i][j], a, b[TN + j]);
+                }
               }
             }
           }
@@ -423,7 +455,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
       for (int p = 0; p < STAGES - 1; ++p)
         if (p < nk) {
-          issue_a<Cfg>(a_slot(p), (uint32_t)p * 128, rsA, voffA, wave, lane);
+          issue_a<Cfg>(a_slot(p), (uint32_t)p * KB_A, rsA, voffA, wave, lane);
           issue_w(p, p);
         }
       int slot = 0;
@@ -432,7 +464,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         block_barrier();                                // ... for every wave; slot ks-1 is free
         if (ks + STAGES - 1 < nk) {
           const int fs = slot == 0 ? STAGES - 1 : slot - 1;
-          issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * 128, rsA, voffA, wave, lane);
+          issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * KB_A, rsA, voffA, wave, lane);
           issue_w(fs, ks + STAGES - 1);
         }
         compute(a_slot(slot), b_slot(slot));
@@ -452,7 +484,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         if (ks + 1 < nk) wait_vmcnt<Cfg::LPS_B>();
         else wait_vmcnt<0>();
         block_barrier();                                // step ks visible; slots of ks-1 free
-        if (ks + 1 < nk) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * 128, rsA, voffA, wave, lane);
+        if (ks + 1 < nk) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * KB_A, rsA, voffA, wave, lane);
         if (ks + 2 < nk)
           issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
         compute(a_slot(ks & 1), b_slot(bs));
