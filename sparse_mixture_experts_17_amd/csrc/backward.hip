@@ -260,7 +260,7 @@ hipError_t launch_to_bf16(const float* src, size_t n, void* dst, hipStream_t str
 //   aux:                                   dp_e += d_aux * E * f_e / T,  f_e = counts_e / (T k),
 //   softmax: dr = p (dp - sum_e p_e dp_e);  sigmoid (p = sigma(r)): dr = dp p (1 - p).
 // One block = 16 tokens, one wave per token at a time; lane l holds experts 64 q + l.
-template <typename T>
+template <typename T, int NQ>   // NQ: 64-expert chunks per lane (E <= 64 NQ)
 __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
                                                          const float* __restrict__ b_r, int T_, int d, int E, int k,
                                                          int renorm, int scoring, const int32_t* __restrict__ idx,
@@ -284,10 +284,10 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x
     const int tl = wave * 4 + tt;
     const int t = t0 + tl;
     if (t >= T_) break;
-    float v[16], p[16];
+    float v[NQ], p[NQ];
     float m = -INFINITY, inv = 1.f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int e = q * 64 + lane;
       v[q] = (q < nq && e < E) ? logits[tl * E + e] : -INFINITY;
       m = fmaxf(m, v[q]);
@@ -296,14 +296,14 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x
       m = wave_max(m);
       float s = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) s += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
+      for (int q = 0; q < NQ; ++q) s += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
       s = wave_sum(s);
       inv = 1.f / s;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) p[q] = (v[q] == -INFINITY) ? 0.f : expf(v[q] - m) * inv;
+      for (int q = 0; q < NQ; ++q) p[q] = (v[q] == -INFINITY) ? 0.f : expf(v[q] - m) * inv;
     } else {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) p[q] = (v[q] == -INFINITY) ? 0.f : 1.f / (1.f + expf(-v[q]));
+      for (int q = 0; q < NQ; ++q) p[q] = (v[q] == -INFINITY) ? 0.f : 1.f / (1.f + expf(-v[q]));
     }
     // slot gradients (wave-uniform), S and sum_j dg_j g_j in slot order
     float dgs[16];
@@ -321,9 +321,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x
       G = fmaf(dg, gate[(size_t)t * k + j], G);
       if (dgate && lane == 0) dgate[(size_t)t * k + j] = dg;
     }
-    float dp[16];
+    float dp[NQ];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int e = q * 64 + lane;
       dp[q] = (q < nq && e < E) ? aux_scale * (float)counts[e] : 0.f;
     }
@@ -331,21 +331,49 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x
       const int e = idx[(size_t)t * k + j];
       const float dpk = renorm ? (dgs[j] - G) / S : dgs[j];
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
+      for (int q = 0; q < NQ; ++q)
         if (e == q * 64 + lane) dp[q] += dpk;
     }
     float c = 0.f;
     if (!sigm) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) c = fmaf(p[q], dp[q], c);
+      for (int q = 0; q < NQ; ++q) c = fmaf(p[q], dp[q], c);
       c = wave_sum(c);
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int e = q * 64 + lane;
       if (q < nq && e < E) dr[(size_t)t * E + e] = sigm ? dp[q] * p[q] * (1.f - p[q]) : p[q] * (dp[q] - c);
     }
   }
+}
+
+template <typename T, int NQ>
+static void router_bwd_launch(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
+                              const float* b_r, int T_, int d, int E, int k, int renorm, int scoring,
+                              const int32_t* idx, const float* gate, const int32_t* row_of, const int32_t* counts,
+                              const float* part, int npart, float d_aux, float* dr, float* dgate) {
+  auto kern = router_bwd_kernel<T, NQ>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k, renorm,
+                     scoring, idx, gate, row_of, counts, part, npart, d_aux, dr, dgate);
+}
+
+template <typename T>
+static void router_bwd_launch_nq(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
+                                 const float* b_r, int T_, int d, int E, int k, int renorm, int scoring,
+                                 const int32_t* idx, const float* gate, const int32_t* row_of,
+                                 const int32_t* counts, const float* part, int npart, float d_aux, float* dr,
+                                 float* dgate) {
+  if (E <= 64)
+    router_bwd_launch<T, 1>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, idx, gate, row_of, counts,
+                            part, npart, d_aux, dr, dgate);
+  else if (E <= 256)
+    router_bwd_launch<T, 4>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, idx, gate, row_of, counts,
+                            part, npart, d_aux, dr, dgate);
+  else
+    router_bwd_launch<T, 16>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, idx, gate, row_of, counts,
+                             part, npart, d_aux, dr, dgate);
 }
 
 hipError_t launch_router_bwd(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E, int k,
@@ -354,17 +382,12 @@ hipError_t launch_router_bwd(int dtype, const void* x, const void* w_r, const fl
                              float* dgate, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const size_t lds = (size_t)router_ksplit(E) * kRouteTokens * E * sizeof(float);
-  if (dtype == 1) {
-    auto kern = router_bwd_kernel<uint16_t>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kern, dim3(route_blocks(T)), dim3(256), lds, stream, (const uint16_t*)x, (const uint16_t*)w_r,
-                       b_r, T, d, E, k, renorm, scoring, idx, gate, row_of, counts, part, npart, d_aux, dr, dgate);
-  } else {
-    auto kern = router_bwd_kernel<float>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kern, dim3(route_blocks(T)), dim3(256), lds, stream, (const float*)x, (const float*)w_r, b_r,
-                       T, d, E, k, renorm, scoring, idx, gate, row_of, counts, part, npart, d_aux, dr, dgate);
-  }
+  if (dtype == 1)
+    router_bwd_launch_nq<uint16_t>(route_blocks(T), lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, idx, gate,
+                                   row_of, counts, part, npart, d_aux, dr, dgate);
+  else
+    router_bwd_launch_nq<float>(route_blocks(T), lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, idx, gate,
+                                row_of, counts, part, npart, d_aux, dr, dgate);
   return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ namespace moe {
 //          k rounds of wave arg-max (ties -> lower index), gates, LDS histogram.
 // Phase 3: per-block partial sums of p (fixed order over waves) and histogram to global.
 
-template <typename T>
+// NQ: 64-expert chunks per lane (E <= 64 NQ), so small expert counts skip empty chunks.
+template <typename T, int NQ>
 __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
                                                      const float* __restrict__ b_r, int T_, int d, int E,
                                                      int k, int renorm, int scoring, int n_group,
@@ -57,41 +58,41 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
   // ---- phase 2: scores and top-k, one token per wave at a time
   // Lane l holds experts e = 64 q + l.  sel = the selection score (logit for softmax, affinity
   // plus bias for sigmoid); num = the gate numerator (exp(r - max) or the affinity).
-  const int nq = (E + 63) / 64;   // <= 16
+  const int nq = (E + 63) / 64;   // <= NQ
   const int gsz = E / n_group;
   float* srow = selrow + wave * E;
-  float pacc[16];
+  float pacc[NQ];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) pacc[q] = 0.f;
+  for (int q = 0; q < NQ; ++q) pacc[q] = 0.f;
   for (int tt = 0; tt < 4; ++tt) {
     const int tl = wave * 4 + tt;
     const int t = t0 + tl;
     if (t >= T_) break;
-    float v[16];
+    float v[NQ];
     float m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       int e = q * 64 + lane;
       v[q] = (q < nq && e < E) ? logits[tl * E + e] : -INFINITY;
       m = fmaxf(m, v[q]);
     }
     float inv = 1.f;
-    float sel[16];
+    float sel[NQ];
     if (!sigm) {
       m = wave_max(m);
       float s = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) s += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
+      for (int q = 0; q < NQ; ++q) s += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
       s = wave_sum(s);
       inv = 1.f / s;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         pacc[q] += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m) * inv;
         sel[q] = v[q];
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         const int e = q * 64 + lane;
         const bool ok = v[q] != -INFINITY;
         const float a = ok ? 1.f / (1.f + expf(-v[q])) : 0.f;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
     if (n_group > 1) {
       // best selection score per group (lanes < n_group), then the topk_group best groups
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         const int e = q * 64 + lane;
         if (q < nq && e < E) srow[e] = sel[q];
       }
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
         allowed |= 1ull << bg;
       }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         const int e = q * 64 + lane;
         if (q < nq && e < E && !((allowed >> (e / gsz)) & 1ull)) sel[q] = -INFINITY;
       }
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
       float bv = -INFINITY;
       int be = 0x7fffffff;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {     // ascending expert index within the lane: '>' keeps the lowest
+      for (int q = 0; q < NQ; ++q) {     // ascending expert index within the lane: '>' keeps the lowest
         int e = q * 64 + lane;
         if (q < nq && e < E && !((taken >> q) & 1u) && sel[q] > bv) { bv = sel[q]; be = e; }
       }
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
 
   // ---- phase 3: block partials
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     int e = q * 64 + lane;
     if (q < nq && e < E) psum[wave * E + e] = pacc[q];
   }
@@ -175,23 +176,43 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
   }
 }
 
+template <typename T, int NQ>
+static void router_launch(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r, const float* b_r,
+                          int T_, int d, int E, int k, int renorm, int scoring, int n_group, int topk_group,
+                          int32_t* idx, float* gate, float* p_part, int32_t* hist) {
+  auto kern = router_kernel<T, NQ>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k, renorm,
+                     scoring, n_group, topk_group, idx, gate, p_part, hist);
+}
+
+template <typename T>
+static void router_launch_nq(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
+                             const float* b_r, int T_, int d, int E, int k, int renorm, int scoring, int n_group,
+                             int topk_group, int32_t* idx, float* gate, float* p_part, int32_t* hist) {
+  if (E <= 64)
+    router_launch<T, 1>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                        p_part, hist);
+  else if (E <= 256)
+    router_launch<T, 4>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                        p_part, hist);
+  else
+    router_launch<T, 16>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                         p_part, hist);
+}
+
 hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E,
                          int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx, float* gate,
                          float* p_part, int32_t* hist, hipStream_t stream) {
   const int nb = route_blocks(T);
   const size_t lds =
       (size_t)(router_ksplit(E) * kRouteTokens * E + 8 * E) * sizeof(float) + (size_t)E * sizeof(int);
-  if (dtype == 1) {
-    auto kern = router_kernel<uint16_t>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const uint16_t*)x, (const uint16_t*)w_r, b_r,
-                       T, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part, hist);
-  } else {
-    auto kern = router_kernel<float>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const float*)x, (const float*)w_r, b_r, T, d,
-                       E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part, hist);
-  }
+  if (dtype == 1)
+    router_launch_nq<uint16_t>(nb, lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx,
+                               gate, p_part, hist);
+  else
+    router_launch_nq<float>(nb, lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx,
+                            gate, p_part, hist);
   return hipGetLastError();
 }
 

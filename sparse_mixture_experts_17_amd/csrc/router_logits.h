@@ -13,12 +13,30 @@ __host__ __device__ inline int router_ksplit(int E) {
   return groups == 1 ? 4 : (groups == 2 ? 2 : 1);
 }
 
-// Partial logits of NTL consecutive expert tiles over chunks [c0, c1) of 64 bytes.
+// Partial logits of NTL consecutive expert tiles over chunks [c0, c1) of 64 bytes.  With one
+// or two expert tiles the loads of U = 8 chunks are issued before their MFMAs (the
+// accumulation order over chunks is unchanged), so eight chunks' memory latency overlaps; with
+// more tiles each chunk already has NTL + 1 loads in flight (measured: batching them too is
+// slower at 256 experts).
 template <typename T, int NTL>
 __device__ __forceinline__ void router_tiles(const char* xrow, const char* const* wrow, int c0, int c1,
                                              f32x4_t* acc) {
-#pragma unroll 8
-  for (int c = c0; c < c1; ++c) {
+  constexpr int U = NTL >= 3 ? 1 : 8;
+  int c = c0;
+  for (; U > 1 && c + U <= c1; c += U) {
+    u32x4_t a[U], b[U][NTL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u] = *(const u32x4_t*)(xrow + (size_t)(c + u) * 64);
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) b[u][j] = *(const u32x4_t*)(wrow[j] + (size_t)(c + u) * 64);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) Mfma<T>::step(acc[j], a[u], b[u][j]);
+  }
+  for (; c < c1; ++c) {
     const u32x4_t a = *(const u32x4_t*)(xrow + (size_t)c * 64);
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
