@@ -176,6 +176,138 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
   }
 }
 
+// Router for E <= EB <= 16 experts (measured: at 64 experts the serial per-thread work costs
+// more than router_kernel's wave per token).  Phase 1 as above.  Phase 2 gives each of the block's 16
+// tokens one thread, which holds the token's E logits in registers: max, softmax sum (in
+// expert order), group limit and the k arg-max passes need no cross-lane exchange.  The
+// selection rule is router_kernel's: highest score, ties to the lower index (groups too).
+// LDS: the four K-partial slots of the logits, reused after the sum as slot 0 = logits,
+// slot 1 = p, slot 2 = selection scores (group limit only), slot 3 = chosen experts.
+template <typename T, int EB>
+__global__ __launch_bounds__(256) void router_tpt_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
+                                                         const float* __restrict__ b_r, int T_, int d, int E,
+                                                         int k, int renorm, int scoring, int n_group,
+                                                         int topk_group, int32_t* __restrict__ idx,
+                                                         float* __restrict__ gate, float* __restrict__ p_part,
+                                                         int32_t* __restrict__ hist) {
+  static_assert(EB <= 64, "E <= 64 keeps router_ksplit(E) == 4, so four logit slots exist");
+  constexpr int TB = kRouteTokens;
+  const bool sigm = scoring == 1;
+  extern __shared__ float smem[];
+  float* logits = smem;                                  // [TB][E]
+  float* pbuf = smem + TB * E;                           // [TB][E]
+  float* sbuf = smem + 2 * TB * E;                       // [TB][E]
+  int* cbuf = (int*)(smem + 3 * TB * E);                 // [TB][k]
+  int* lhist = (int*)(smem + 4 * TB * E);                // [E]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * TB;
+  const int ntok = min(TB, T_ - t0);
+  for (int i = tid; i < E; i += 256) lhist[i] = 0;
+
+  router_block_logits<T>(x, w_r, sigm ? nullptr : b_r, T_, d, E, t0, logits, wave, lane, tid);
+
+  if (tid < ntok) {
+    const int t = t0 + tid;
+    const float* lrow = logits + tid * E;
+    float* prow = pbuf + tid * E;
+    float v[EB], sel[EB];
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+      v[e] = e < E ? lrow[e] : -INFINITY;
+      m = fmaxf(m, v[e]);
+    }
+    float inv = 1.f;
+    if (!sigm) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EB; ++e) s += (v[e] == -INFINITY) ? 0.f : expf(v[e] - m);
+      inv = 1.f / s;
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        if (e < E) prow[e] = (v[e] == -INFINITY) ? 0.f : expf(v[e] - m) * inv;
+        sel[e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const bool ok = v[e] != -INFINITY;
+        const float a = ok ? 1.f / (1.f + expf(-v[e])) : 0.f;
+        if (e < E) prow[e] = a;
+        sel[e] = ok ? a + (b_r ? b_r[e] : 0.f) : -INFINITY;
+      }
+    }
+    if (n_group > 1) {
+      // best score per group, then the topk_group best groups; the others are masked out
+      const int gsz = E / n_group;
+      float* srow = sbuf + tid * E;
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+        if (e < E) srow[e] = sel[e];
+      uint64_t allowed = 0;
+      for (int r = 0; r < topk_group; ++r) {
+        float bv = -INFINITY;
+        int bg = -1;
+        for (int g = 0; g < n_group; ++g) {
+          if ((allowed >> g) & 1ull) continue;
+          float gb = -INFINITY;
+          for (int i = 0; i < gsz; ++i) gb = fmaxf(gb, srow[g * gsz + i]);
+          if (bg < 0 || gb > bv) { bv = gb; bg = g; }
+        }
+        allowed |= 1ull << bg;
+      }
+      int g = 0, gi = 0;
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        if (e < E && !((allowed >> g) & 1ull)) sel[e] = -INFINITY;
+        if (++gi == gsz) { gi = 0; ++g; }
+      }
+    }
+    // k passes of arg-max over the untaken experts; '>' in ascending order keeps the lowest index
+    int* crow = cbuf + tid * k;
+    uint64_t taken = 0;
+    float numsum = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int be = -1;
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+        if (e < E && !((taken >> e) & 1ull) && (be < 0 || sel[e] > bv)) { bv = sel[e]; be = e; }
+      taken |= 1ull << be;
+      const float lg = lrow[be];
+      numsum += sigm ? 1.f / (1.f + expf(-lg)) : expf(lg - m);
+      crow[j] = be;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int be = crow[j];
+      const float lg = lrow[be];
+      const float num = sigm ? 1.f / (1.f + expf(-lg)) : expf(lg - m);
+      idx[(size_t)t * k + j] = be;
+      gate[(size_t)t * k + j] = renorm ? num / numsum : (sigm ? num : num * inv);
+      atomicAdd(&lhist[be], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {                   // block partial of p, tokens in order
+    float ps = 0.f;
+    for (int tl = 0; tl < ntok; ++tl) ps += pbuf[tl * E + e];
+    p_part[(size_t)blockIdx.x * E + e] = ps;
+    hist[(size_t)blockIdx.x * E + e] = lhist[e];
+  }
+}
+
+template <typename T, int EB>
+static void router_tpt_launch(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
+                              const float* b_r, int T_, int d, int E, int k, int renorm, int scoring, int n_group,
+                              int topk_group, int32_t* idx, float* gate, float* p_part, int32_t* hist) {
+  auto kern = router_tpt_kernel<T, EB>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k, renorm,
+                     scoring, n_group, topk_group, idx, gate, p_part, hist);
+}
+
 template <typename T, int NQ>
 static void router_launch(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r, const float* b_r,
                           int T_, int d, int E, int k, int renorm, int scoring, int n_group, int topk_group,
@@ -190,7 +322,10 @@ template <typename T>
 static void router_launch_nq(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
                              const float* b_r, int T_, int d, int E, int k, int renorm, int scoring, int n_group,
                              int topk_group, int32_t* idx, float* gate, float* p_part, int32_t* hist) {
-  if (E <= 64)
+  if (E <= 16)
+    router_tpt_launch<T, 16>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx,
+                             gate, p_part, hist);
+  else if (E <= 64)
     router_launch<T, 1>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
                         p_part, hist);
   else if (E <= 256)
@@ -238,12 +373,65 @@ hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, h
 
 // ------------------------------------------------------------------------------ scan (1 block)
 //
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if ((int)(threadIdx.x & 63) >= o) x += y;
+  }
+  *total = __shfl(x, kWave - 1, kWave);
+  return x - v;
+}
+
+// The expert-level part of the scan for E <= 64, in one wave (lane e = expert e, cnt and pe
+// its totals, zero for e >= E): kept, offsets, tile starts, f, P and aux.  aux is summed by
+// the same halving tree as the 1024-wide version, so both give the same bits.
+__device__ __forceinline__ void scan_finish_wave(int e, int cnt, float pe, bool with_p, int T, int k, int E, int cap,
+                                                 int32_t* counts, int32_t* kept, int32_t* offsets, float* f,
+                                                 float* P, float* aux, int bm1, int32_t* tstart1, int bm2,
+                                                 int32_t* tstart2) {
+  const int kp = e < E ? (cap < 0 ? cnt : min(cnt, cap)) : 0;
+  int tot, tot1, tot2;
+  const int off = wave_excl_scan(kp, &tot);
+  const int ts1 = wave_excl_scan((kp + bm1 - 1) / bm1, &tot1);
+  const int ts2 = wave_excl_scan((kp + bm2 - 1) / bm2, &tot2);
+  if (e < E) {
+    if (counts) counts[e] = cnt;
+    kept[e] = kp;
+    offsets[e] = off;
+    tstart1[e] = ts1;
+    tstart2[e] = ts2;
+  }
+  if (e == 0) {
+    offsets[E] = tot;
+    tstart1[E] = tot1;
+    tstart2[E] = tot2;
+  }
+  if (with_p) {
+    const long long R = (long long)T * k;
+    const float fe = (e < E && R > 0) ? (float)((double)cnt / (double)R) : 0.f;
+    const float Pe = (e < E && T > 0) ? pe / (float)T : 0.f;
+    if (e < E) {
+      f[e] = fe;
+      P[e] = Pe;
+    }
+    float v = fe * Pe;
+#pragma unroll
+    for (int h = 32; h > 0; h >>= 1) v += __shfl_down(v, h, kWave);
+    if (e == 0) aux[0] = (float)E * v;
+  }
+}
+
 // Per-chunk bases by expert: chunk_base[b][e] = assignments to e in chunks < b;
-// counts[e] = all of them.  The chunks are cut into G = 1024 / E contiguous groups
-// so all 1024 threads work: thread (g, e) sums its group's chunks, a serial pass over
-// the G group sums per expert turns them into group bases, and each thread then
-// writes its chunks' bases.  kept = min(counts, cap); offsets and tile starts are
-// exclusive scans over experts.  f, P, aux use fixed-order sums.
+// counts[e] = all of them.  The chunks are cut into G <= 1024 / E contiguous groups of
+// about kScanBatch chunks, so most threads work and each reads its group in one batch of
+// loads: thread (g, e) sums its group's chunks, a serial pass over the G group sums per
+// expert turns them into group bases, and each thread then writes its chunks' bases.
+// kept = min(counts, cap); offsets and tile starts are exclusive scans over experts.
+// f, P, aux use fixed-order sums.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist,
                                                     const float* __restrict__ p_part, int nb, int T, int k,
                                                     int E, int cap, int32_t* __restrict__ counts,
@@ -256,15 +444,28 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   __shared__ int s_part[1024];
   __shared__ float s_red[1024];
   const int tid = threadIdx.x;
-  const int G = max(1, 1024 / E);
+  const int G = max(1, min(1024 / E, (nb + kScanBatch - 1) / kScanBatch));
   const int ge = tid / E, ee = tid - ge * E;              // group and expert of this thread
   const bool act = ge < G;
   const int b0 = act ? (int)((long long)ge * nb / G) : 0, b1 = act ? (int)((long long)(ge + 1) * nb / G) : 0;
+  // group sums, loads batched so kScanBatch of them are in flight; p summed in chunk order
   int c = 0;
   float ps = 0.f;
-  for (int b = b0; b < b1; ++b) c += hist[(size_t)b * E + ee];
-  if (p_part)
-    for (int b = b0; b < b1; ++b) ps += p_part[(size_t)b * E + ee];
+  for (int bb = b0; bb < b1; bb += kScanBatch) {
+    int h[kScanBatch];
+    float q[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const bool ok = bb + u < b1;
+      h[u] = ok ? hist[(size_t)(bb + u) * E + ee] : 0;
+      q[u] = (ok && p_part) ? p_part[(size_t)(bb + u) * E + ee] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      c += h[u];
+      if (bb + u < b1) ps += q[u];
+    }
+  }
   s_part[tid] = c;
   s_red[tid] = ps;
   __syncthreads();
@@ -281,10 +482,23 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   __syncthreads();
   if (act) {
     int run = s_part[tid];
-    for (int b = b0; b < b1; ++b) {
-      chunk_base[(size_t)b * E + ee] = run;
-      run += hist[(size_t)b * E + ee];
+    for (int bb = b0; bb < b1; bb += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) h[u] = bb + u < b1 ? hist[(size_t)(bb + u) * E + ee] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        if (bb + u < b1) {
+          chunk_base[(size_t)(bb + u) * E + ee] = run;
+          run += h[u];
+        }
     }
+  }
+  if (E <= kWave) {                                       // block-uniform
+    if (tid < kWave)
+      scan_finish_wave(tid, cnt, pe, p_part != nullptr, T, k, E, cap, counts, kept, offsets, f, P, aux, bm1,
+                       tstart1, bm2, tstart2);
+    return;
   }
   const int e = tid;
   const int kp = e < E ? (cap < 0 ? cnt : min(cnt, cap)) : 0;
@@ -325,12 +539,41 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// The same scan for few experts and few chunks (decode): one wave, lane e = expert e, chunks
+// summed in order.  With nb <= kScanBatch scan_kernel has a single group and sums in the
+// same order, so both give the same bits.
+__global__ __launch_bounds__(64) void scan_small_kernel(const int32_t* __restrict__ hist,
+                                                        const float* __restrict__ p_part, int nb, int T, int k,
+                                                        int E, int cap, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ chunk_base, float* __restrict__ f,
+                                                        float* __restrict__ P, float* __restrict__ aux, int bm1,
+                                                        int32_t* __restrict__ tstart1, int bm2,
+                                                        int32_t* __restrict__ tstart2) {
+  const int e = threadIdx.x;
+  int cnt = 0;
+  float pe = 0.f;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      chunk_base[(size_t)b * E + e] = cnt;
+      cnt += hist[(size_t)b * E + e];
+      if (p_part) pe += p_part[(size_t)b * E + e];
+    }
+  }
+  scan_finish_wave(e, cnt, pe, p_part != nullptr, T, k, E, cap, counts, kept, offsets, f, P, aux, bm1, tstart1, bm2,
+                   tstart2);
+}
+
 hipError_t launch_scan(const int32_t* hist, const float* p_part, int nb, int T, int k, int E, int cap,
                        int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* chunk_base, float* f,
                        float* P, float* aux, int bm1, int32_t* tstart1, int bm2, int32_t* tstart2,
                        hipStream_t stream) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, hist, p_part, nb, T, k, E, cap, counts, kept,
-                     offsets, chunk_base, f, P, aux, bm1, tstart1, bm2, tstart2);
+  if (E <= kWave && nb <= kScanBatch)
+    hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(kWave), 0, stream, hist, p_part, nb, T, k, E, cap, counts,
+                       kept, offsets, chunk_base, f, P, aux, bm1, tstart1, bm2, tstart2);
+  else
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, hist, p_part, nb, T, k, E, cap, counts, kept,
+                       offsets, chunk_base, f, P, aux, bm1, tstart1, bm2, tstart2);
   return hipGetLastError();
 }
 

@@ -46,6 +46,10 @@ SMALL = [
               d_e_shared=0, n_group=4, topk_group=2, renormalize=False),
     wl.scaled(BASE["mixtral_prefill"], name="softmax_grouped", T=180, d=256, d_e=128, E=48, k=3, n_group=6,
               topk_group=2, router_bias_var=0.5),
+    wl.scaled(BASE["mixtral_prefill"], name="softmax_grouped_e16", T=150, d=256, d_e=128, E=16, k=3, n_group=4,
+              topk_group=2, router_bias_var=0.5),
+    wl.scaled(BASE["deepseek_v3_grouped"], name="sigmoid_grouped_e12", T=130, d=256, d_e=128, E=12, k=2,
+              d_e_shared=0, n_group=3, topk_group=2, renormalize=False),
     wl.scaled(BASE["mixtral_prefill"], name="grouped_64", T=33, d=128, d_e=128, E=1024, k=16, n_group=64,
               topk_group=3),
     # FP8 E4M3 expert weights in every tile configuration
@@ -236,16 +240,32 @@ def test_degenerate_inputs():
     torch.cuda.synchronize()
     assert torch.all(out.f == 0) and torch.all(out.P == 0) and float(out.aux) == 0 and torch.all(out.counts == 0)
     assert torch.all(out.offsets == 0)
-    # router weight zero: every logit ties, experts 0..k-1 win with gates 1/k
+    # router weight zero: every logit ties, experts 0..k-1 win with gates 1/k (expert counts that
+    # take each router kernel: thread per token, wave per token with 1 and 4 chunks per lane)
+    for E in (300, 40, 8):
+        w = wl.scaled(BASE["mixtral_prefill"], name="ties", T=70, d=128, d_e=128, E=E, k=3)
+        inp = wl.make_inputs(w)
+        dev = upload(inp)
+        shape, _ = gp.shape_of(w)
+        out = moe.forward(shape, dev.x, torch.zeros_like(dev.w_r), None, dev.w_gate, dev.w_up, dev.w_down)
+        torch.cuda.synchronize()
+        assert torch.all(out.idx.cpu() == torch.arange(3, dtype=torch.int32)), E
+        assert torch.allclose(out.gate.cpu(), torch.full((70, 3), 1 / 3), atol=1e-7), E
+        assert torch.allclose(out.P.cpu(), torch.full((E,), 1 / E), atol=1e-7), E
+    # sigmoid scores with zero router weight and no bias: groups tie too, the lowest two of four
+    # groups are kept and experts 0..2 win, each gate 1/3 after renormalisation
+    for E in (16, 64):
+        wg = wl.scaled(BASE["deepseek_v3_grouped"], name="group_ties", T=50, d=128, d_e=128, E=E, k=3,
+                       d_e_shared=0, n_group=4, topk_group=2, router_bias_var=None)
+        ig = upload(wl.make_inputs(wg))
+        sg, _ = gp.shape_of(wg)
+        og = moe.forward(sg, ig.x, torch.zeros_like(ig.w_r), None, ig.w_gate, ig.w_up, ig.w_down)
+        torch.cuda.synchronize()
+        assert torch.all(og.idx.cpu() == torch.arange(3, dtype=torch.int32)), E
+        assert torch.allclose(og.gate.cpu(), torch.full((50, 3), 1 / 3), atol=1e-7), E
     w = wl.scaled(BASE["mixtral_prefill"], name="ties", T=70, d=128, d_e=128, E=8, k=3)
     inp = wl.make_inputs(w)
     dev = upload(inp)
-    shape, _ = gp.shape_of(w)
-    out = moe.forward(shape, dev.x, torch.zeros_like(dev.w_r), None, dev.w_gate, dev.w_up, dev.w_down)
-    torch.cuda.synchronize()
-    assert torch.all(out.idx.cpu() == torch.arange(3, dtype=torch.int32))
-    assert torch.allclose(out.gate.cpu(), torch.full((70, 3), 1 / 3), atol=1e-7)
-    assert torch.allclose(out.P.cpu(), torch.full((8,), 1 / 8), atol=1e-7)
     # capacity 0: every assignment dropped, y = 0 (no shared expert) -- the residual carries the token
     shape0 = moe.make_shape(w.T, w.d, w.d_e, w.E, w.k, capacity=0, dtype=moe.MOE_BF16)
     out = moe.forward(shape0, dev.x, dev.w_r, None, dev.w_gate, dev.w_up, dev.w_down)
