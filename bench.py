@@ -5,8 +5,10 @@ One step = one moe_forward call (router, dispatch, grouped SwiGLU experts, combi
 over one batch of synthetic tokens already resident in device memory.  Default
 workload: the Mixtral 8x7B layer shape at a prefill batch of 4096 tokens (bf16
 weights and activations, fp32 accumulate).  A decode-batch line (16 tokens, same
-weights) rides along as "secondary", and the backward pass of the prefill call as
-"secondary_backward".
+weights) rides along as "secondary", the split ABI's moe_permute (the gather of token
+rows into expert order) on the prefill routing as "secondary_permute", the backward pass
+of the prefill call as "secondary_backward", and decode with FP8 and MXFP4 expert weights
+as "secondary_fp8" and "secondary_mxfp4".
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize(); per-stage durations come from HIP events that the library
@@ -195,7 +197,51 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
     touched = int((kept > 0).sum())
     return dict(w=w, shape=shape, cap=cap, total_ms=total_ms, wall_s=t_wall, stages=stages, kernel_ms=kernel_ms,
                 steps=steps,
-                plain_ms=plain_ms, R_kept=R_kept, touched=touched, upload_s=t_up, dev=dev, inp=inp)
+                plain_ms=plain_ms, R_kept=R_kept, touched=touched, upload_s=t_up, dev=dev, inp=inp, out=out)
+
+
+def run_permute(info, steps, warmup):
+    """The split ABI's moe_permute on the forward's routing: histogram, scan, stable rank and the
+    gather of every kept assignment's token row into expert order (the fused forward instead
+    gathers inside the gate/up product's loads).  Timed with events around each call."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_17_amd as moe
+
+    w, shape, dev, out = info["w"], info["shape"], info["dev"], info["out"]
+    R = w.T * w.k
+    i32 = torch.int32
+    kept = torch.empty(w.E, dtype=i32, device="cuda")
+    offsets = torch.empty(w.E + 1, dtype=i32, device="cuda")
+    row_token = torch.empty(R, dtype=i32, device="cuda")
+    row_of = torch.empty((w.T, w.k), dtype=i32, device="cuda")
+    x_perm = torch.empty((R, w.d), dtype=dev.x.dtype, device="cuda")
+
+    def call():
+        moe.moe_permute(shape, dev.x, out.idx, kept, offsets, row_token, row_of, x_perm, out.ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a_, b_ in evs:
+        a_.record()
+        call()
+        b_.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
+    rk = int(kept.sum())
+    s = dev.x.element_size()
+    nbytes = 2 * rk * w.d * s + R * 4 * 3 + route_chunks(w.T) * w.E * 4 * 2
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": w.name + " (moe_permute, split ABI)", "ms_per_call": ms, "rows": rk,
+            "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "algorithmic": "kept rows x d x elem read + the same written, + idx, row_of, row_token, histograms"}
+
+
+def route_chunks(T):
+    return (T + 15) // 16
 
 
 def layer_work(w, R_kept, touched):
@@ -408,6 +454,10 @@ def main():
                          "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
             "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
         }
+    if not a.no_secondary and w.name == "mixtral_prefill":
+        print("[bench] secondary: moe_permute (split ABI) on the same routing", file=sys.stderr, flush=True)
+        line["secondary_permute"] = run_permute(info, max(a.steps, 20), a.warmup)
+        torch.cuda.empty_cache()
     if not a.no_secondary and w.name == "mixtral_prefill":
         print("[bench] secondary: backward pass on the same inputs", file=sys.stderr, flush=True)
         line["secondary_backward"] = run_backward(info, a.steps, a.warmup)

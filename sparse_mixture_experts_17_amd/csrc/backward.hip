@@ -295,9 +295,17 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x
     if (!sigm) {
       m = wave_max(m);
       float s = 0.f;
+      if (E <= 16) {
+        // the forward router for up to 16 experts sums the softmax terms in expert order
+        for (int e = 0; e < E; ++e) {
+          const float ve = logits[tl * E + e];
+          s += (ve == -INFINITY) ? 0.f : expf(ve - m);
+        }
+      } else {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) s += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
-      s = wave_sum(s);
+        for (int q = 0; q < NQ; ++q) s += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m);
+        s = wave_sum(s);
+      }
       inv = 1.f / s;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) p[q] = (v[q] == -INFINITY) ? 0.f : expf(v[q] - m) * inv;

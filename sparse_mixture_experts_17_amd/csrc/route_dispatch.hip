@@ -608,7 +608,7 @@ hipError_t launch_tile_sched(const int32_t* offsets, int E, int bm1, int32_t* ts
 // within its expert is the chunk's base for that expert plus the number of earlier
 // assignments in the chunk with the same expert (stable, arrival order).  Kept
 // assignments then copy their token row into x_perm with 16-byte loads and stores.
-template <typename T>
+template <typename T, bool COPY>
 __global__ __launch_bounds__(256) void rank_gather_kernel(const T* __restrict__ x, const int32_t* __restrict__ idx,
                                                           int T_, int d, int k, int E, int cap,
                                                           const int32_t* __restrict__ chunk_base,
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(256) void rank_gather_kernel(const T* __restrict__ 
       if (row >= 0) row_token[row] = t0 + tid / k;
     }
   }
-  if (!x_perm) return;                         // indices only; the GEMM gathers rows itself
+  if constexpr (!COPY) return;                 // indices only; the GEMM gathers rows itself
   __syncthreads();
   const int P = (int)((size_t)d * sizeof(T) / 16);   // 16-byte pieces per row
   // the copy of this chunk is shared by gridDim.y blocks (more blocks for small batches)
@@ -671,13 +671,18 @@ hipError_t launch_rank_gather(int dtype, const void* x, const int32_t* idx, int 
   const int nb = route_blocks(T);
   const int splits = x_perm ? std::max(1, std::min(16, 512 / nb)) : 1;
   const dim3 grid(nb, splits);
-  if (dtype == 1)
-    hipLaunchKernelGGL(rank_gather_kernel<uint16_t>, grid, dim3(256), 0, stream,
-                       (const uint16_t*)x, idx, T, d, k, E, cap, chunk_base, offsets, row_token, row_of,
-                       (uint16_t*)x_perm);
-  else
-    hipLaunchKernelGGL(rank_gather_kernel<float>, grid, dim3(256), 0, stream, (const float*)x,
-                       idx, T, d, k, E, cap, chunk_base, offsets, row_token, row_of, (float*)x_perm);
+  auto launch = [&](auto kern, auto* xt) {
+    using E_ = std::remove_const_t<std::remove_pointer_t<decltype(xt)>>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, xt, idx, T, d, k, E, cap, chunk_base, offsets, row_token,
+                       row_of, (E_*)x_perm);
+  };
+  if (dtype == 1) {
+    if (x_perm) launch(rank_gather_kernel<uint16_t, true>, (const uint16_t*)x);
+    else launch(rank_gather_kernel<uint16_t, false>, (const uint16_t*)x);
+  } else {
+    if (x_perm) launch(rank_gather_kernel<float, true>, (const float*)x);
+    else launch(rank_gather_kernel<float, false>, (const float*)x);
+  }
   return hipGetLastError();
 }
 
