@@ -33,6 +33,9 @@ struct GemmArgs {
   float* ep_part = nullptr;          // [rows, ep_npart] partial row dots (or NULL)
   const int32_t* ep_poff = nullptr;  // [G+1] column of each group's first row in ep_t (NULL: row)
   int ep_ldt = 0, ep_npart = 0;
+  // dense products only: number tiles n-tile-minor (all n-tiles of an m-tile consecutive, so one
+  // XCD reads each activation row once; for few n-tiles and B small enough to stay in L2)
+  int dense_n_minor = 0;
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
@@ -70,6 +73,14 @@ struct TileCoord {
 __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& args, int L, int ntn, int mt_live, int bpx, int BM) {
   const int32_t* __restrict__ offsets = args.offsets;
   const int32_t* __restrict__ tstart = args.tstart;
+  if (!offsets && args.dense_n_minor) {
+    TileCoord tc;
+    tc.g = 0;
+    tc.nt = L % ntn;
+    tc.row0 = (L / ntn) * BM;
+    tc.rows = min(BM, args.dense_rows - tc.row0);
+    return tc;
+  }
   const int mq = L / ntn;                              // any m-tile index in L's group range
   int g = 0, t0g = 0, t1g = mt_live;
   if (offsets) {

@@ -15,10 +15,21 @@ inline int route_blocks(int T) { return (T + kRouteTokens - 1) / kRouteTokens; }
 
 // Router: fp32 logits via MFMA, softmax or sigmoid scores, top-k (optionally limited to the
 // best topk_group of n_group expert groups; lowest index on ties), gates, per-block partial
-// sums of p (or s) and per-block expert histograms.
+// sums of p (or s) and per-block expert histograms.  When router_logits_by_gemm(E), the logits
+// come from a dense GEMM into `logits` ([T, E] fp32 scratch) first; otherwise `logits` is unused.
 hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d,
                          int E, int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx,
-                         float* gate, float* p_part, int32_t* hist, hipStream_t stream);
+                         float* gate, float* p_part, int32_t* hist, float* logits, hipStream_t stream);
+
+// Many experts: the fused router's blocks (16 tokens each) would each stream all of W_r; a tiled
+// GEMM reads it once per 64 tokens.  Used where the fused router does not split the contraction
+// across waves (more than 128 experts), so both accumulate every logit in the same order and
+// give the same bits, and where E is a whole number of 64-wide GEMM tiles.
+inline bool router_logits_by_gemm(int E) { return E > 128 && E % 64 == 0; }
+
+// Dense logits [T, E] = x [T, d] W_r^T in fp32 (tiles of 64 tokens x 64 experts).
+hipError_t launch_gemm_router(int dtype, const void* x, const void* w_r, int T, int d, int E, float* logits,
+                              hipStream_t stream);
 
 // Per-chunk expert histograms of an index array (dispatch without the router).
 hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t stream);

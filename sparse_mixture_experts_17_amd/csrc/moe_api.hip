@@ -38,7 +38,7 @@ int down_ksplit(const moe_shape& s, GemmKind kind) {
 }
 
 struct Layout {
-  size_t p_part, hist, chunk_base, counts, kept, offsets, row_token, row_of, tstart1, tstart2;
+  size_t p_part, hist, chunk_base, counts, kept, offsets, row_token, row_of, tstart1, tstart2, logits;
   size_t x_perm, h, o, sh_h, sh_o, total;
   int ksplit;   // K chunks of the routed down product in the forward (partials at o + c * T*k*d)
 };
@@ -62,6 +62,7 @@ Layout layout(const moe_shape& s) {
   L.row_of = take(R * sizeof(int32_t));
   L.tstart1 = take((E + 1) * sizeof(int32_t));
   L.tstart2 = take((E + 1) * sizeof(int32_t));
+  L.logits = take(router_logits_by_gemm(s.E) ? (size_t)s.T * E * sizeof(float) : 0);
   L.x_perm = take(R * (size_t)s.d * es);
   L.h = take(R * (size_t)s.d_e * es);
   L.ksplit = down_ksplit(s, choose_kind(std::max<long long>((long long)R, 1), s.E, s.capacity));
@@ -175,7 +176,8 @@ moe_status run_router(const moe_shape& s, const void* x, const void* w_r, const 
   const int nb = route_blocks(s.T);
   if (s.T > 0)
     MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, s.scoring, s.n_group,
-                          s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
+                          s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist),
+                          at<float>(ws, L.logits), st));
   MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts,
                       kept, offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm1, at<int32_t>(ws, L.tstart1),
                       bm2, at<int32_t>(ws, L.tstart2), st));
@@ -344,7 +346,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   MOE_MARK(MOE_STAGE_ROUTER);
   if (s.T > 0)
     MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, s.scoring, s.n_group,
-                          s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist), st));
+                          s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist),
+                          at<float>(ws, L.logits), st));
   MOE_MARK(MOE_STAGE_SCAN);
   MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts, kept,
                       offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm1, ts1, bm2, ts2, st));

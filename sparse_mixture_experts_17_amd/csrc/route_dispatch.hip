@@ -31,29 +31,45 @@ namespace moe {
 // Phase 3: per-block partial sums of p (fixed order over waves) and histogram to global.
 
 // NQ: 64-expert chunks per lane (E <= 64 NQ), so small expert counts skip empty chunks.
-template <typename T, int NQ>
-__global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
+// WAVES = 4: the block computes its logits (phase 1 above).  WAVES = 8 or 16: the logits come
+// from the router GEMM's [T, E] output (logits_in), and more waves share the 16 tokens, so each
+// wave's chain of shuffles covers fewer tokens.
+template <typename T, int NQ, int WAVES = 4>
+__global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
                                                      const float* __restrict__ b_r, int T_, int d, int E,
                                                      int k, int renorm, int scoring, int n_group,
                                                      int topk_group, int32_t* __restrict__ idx,
                                                      float* __restrict__ gate, float* __restrict__ p_part,
-                                                     int32_t* __restrict__ hist) {
-  constexpr int TB = kRouteTokens;
-  const int ksplit = router_ksplit(E);
+                                                     int32_t* __restrict__ hist,
+                                                     const float* __restrict__ logits_in) {
+  constexpr int TB = kRouteTokens, NT = WAVES * 64, TPW = TB / WAVES;   // tokens per wave
+  static_assert(WAVES == 4 || WAVES == 8 || WAVES == 16, "16 tokens over the waves");
+  const int slots = WAVES == 4 ? router_ksplit(E) : 1;
   const bool sigm = scoring == 1;
   extern __shared__ float smem[];
-  float* logits = smem;                          // [TB][E]  (partials: [ksplit][TB][E])
-  float* psum = smem + ksplit * TB * E;          // [4][E]
-  float* selrow = psum + 4 * E;                  // [4][E]  selection scores of a wave's token
-  int* lhist = (int*)(selrow + 4 * E);           // [E]
+  float* logits = smem;                          // [TB][E]  (partials: [slots][TB][E])
+  float* psum = smem + slots * TB * E;           // [WAVES][E]
+  float* selrow = psum + WAVES * E;              // [WAVES][E]  selection scores of a wave's token
+  int* lhist = (int*)(selrow + WAVES * E);       // [E]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
-  for (int i = tid; i < E; i += 256) lhist[i] = 0;
+  for (int i = tid; i < E; i += NT) lhist[i] = 0;
 
-  // ---- phase 1: logits
-  router_block_logits<T>(x, w_r, sigm ? nullptr : b_r, T_, d, E, t0, logits, wave, lane, tid);
+  // ---- phase 1: logits (computed here, or read from the GEMM's [T, E] output; the bias is added
+  // the same way in both)
+  if constexpr (WAVES == 4) {
+    router_block_logits<T>(x, w_r, sigm ? nullptr : b_r, T_, d, E, t0, logits, wave, lane, tid);
+  } else {
+    const float* bb = sigm ? nullptr : b_r;
+    for (int i = tid; i < TB * E; i += NT) {
+      const int tl = i / E, e = i - tl * E;
+      const int t = min(t0 + tl, T_ - 1);                 // rows past T repeat row T-1; never used
+      logits[i] = logits_in[(size_t)t * E + e] + (bb ? bb[e] : 0.f);
+    }
+    __syncthreads();
+  }
 
   // ---- phase 2: scores and top-k, one token per wave at a time
   // Lane l holds experts e = 64 q + l.  sel = the selection score (logit for softmax, affinity
@@ -64,8 +80,8 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
   float pacc[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) pacc[q] = 0.f;
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tl = wave * 4 + tt;
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tl = wave * TPW + tt;
     const int t = t0 + tl;
     if (t >= T_) break;
     float v[NQ];
@@ -170,8 +186,11 @@ __global__ __launch_bounds__(256) void router_kernel(const T* __restrict__ x, co
     if (q < nq && e < E) psum[wave * E + e] = pacc[q];
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    p_part[(size_t)blockIdx.x * E + e] = ((psum[e] + psum[E + e]) + psum[2 * E + e]) + psum[3 * E + e];
+  for (int e = tid; e < E; e += NT) {
+    float ps = psum[e];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) ps += psum[w * E + e];   // waves in order
+    p_part[(size_t)blockIdx.x * E + e] = ps;
     hist[(size_t)blockIdx.x * E + e] = lhist[e];
   }
 }
@@ -308,46 +327,65 @@ static void router_tpt_launch(int nb, size_t lds, hipStream_t stream, const void
                      scoring, n_group, topk_group, idx, gate, p_part, hist);
 }
 
-template <typename T, int NQ>
-static void router_launch(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r, const float* b_r,
+template <typename T, int NQ, int WAVES = 4>
+static void router_launch(int nb, hipStream_t stream, const void* x, const void* w_r, const float* b_r,
                           int T_, int d, int E, int k, int renorm, int scoring, int n_group, int topk_group,
-                          int32_t* idx, float* gate, float* p_part, int32_t* hist) {
-  auto kern = router_kernel<T, NQ>;
+                          int32_t* idx, float* gate, float* p_part, int32_t* hist, const float* logits_in) {
+  const int slots = WAVES == 4 ? router_ksplit(E) : 1;
+  const size_t lds = (size_t)(slots * kRouteTokens * E + 2 * WAVES * E) * sizeof(float) + (size_t)E * sizeof(int);
+  auto kern = router_kernel<T, NQ, WAVES>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k, renorm,
-                     scoring, n_group, topk_group, idx, gate, p_part, hist);
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(WAVES * 64), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k,
+                     renorm, scoring, n_group, topk_group, idx, gate, p_part, hist, logits_in);
 }
 
 template <typename T>
-static void router_launch_nq(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
-                             const float* b_r, int T_, int d, int E, int k, int renorm, int scoring, int n_group,
-                             int topk_group, int32_t* idx, float* gate, float* p_part, int32_t* hist) {
-  if (E <= 16)
+static void router_launch_nq(int nb, hipStream_t stream, const void* x, const void* w_r, const float* b_r, int T_,
+                             int d, int E, int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx,
+                             float* gate, float* p_part, int32_t* hist, const float* logits_in) {
+  if (logits_in) {              // many experts, logits from the GEMM (E > 128)
+    if (E <= 256)
+      router_launch<T, 4, 16>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                              p_part, hist, logits_in);
+    else if (E <= 512)
+      router_launch<T, 16, 16>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                               p_part, hist, logits_in);
+    else                        // 8 waves keep the per-wave LDS rows within 160 KB
+      router_launch<T, 16, 8>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                              p_part, hist, logits_in);
+  } else if (E <= 16) {
+    const size_t lds = (size_t)(router_ksplit(E) * kRouteTokens * E + 8 * E) * sizeof(float) + (size_t)E * sizeof(int);
     router_tpt_launch<T, 16>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx,
                              gate, p_part, hist);
-  else if (E <= 64)
-    router_launch<T, 1>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                        p_part, hist);
-  else if (E <= 256)
-    router_launch<T, 4>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                        p_part, hist);
-  else
-    router_launch<T, 16>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                         p_part, hist);
+  } else if (E <= 64) {
+    router_launch<T, 1>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part,
+                        hist, nullptr);
+  } else if (E <= 256) {
+    router_launch<T, 4>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part,
+                        hist, nullptr);
+  } else {
+    router_launch<T, 16>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part,
+                         hist, nullptr);
+  }
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E,
                          int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx, float* gate,
-                         float* p_part, int32_t* hist, hipStream_t stream) {
+                         float* p_part, int32_t* hist, float* logits, hipStream_t stream) {
   const int nb = route_blocks(T);
-  const size_t lds =
-      (size_t)(router_ksplit(E) * kRouteTokens * E + 8 * E) * sizeof(float) + (size_t)E * sizeof(int);
+  const float* logits_in = nullptr;
+  if (router_logits_by_gemm(E)) {
+    if (!logits) return hipErrorInvalidValue;
+    const hipError_t e = launch_gemm_router(dtype, x, w_r, T, d, E, logits, stream);
+    if (e != hipSuccess) return e;
+    logits_in = logits;
+  }
   if (dtype == 1)
-    router_launch_nq<uint16_t>(nb, lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx,
-                               gate, p_part, hist);
+    router_launch_nq<uint16_t>(nb, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                               p_part, hist, logits_in);
   else
-    router_launch_nq<float>(nb, lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx,
-                            gate, p_part, hist);
+    router_launch_nq<float>(nb, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                            p_part, hist, logits_in);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ BASE = {w: wl.get(w) for w in wl.WORKLOADS}
 SMALL = [
     BASE["tiny_fp32"],
     wl.scaled(BASE["tiny_fp32"], name="fp32_ragged", T=77, d=256, d_e=384, E=6, k=3),
+    wl.scaled(BASE["tiny_fp32"], name="fp32_many_experts", T=100, d=256, d_e=128, E=192, k=4),
     wl.scaled(BASE["switch_capacity"], name="switch_small", T=1000, d=256, d_e=512, E=64, k=1),
     wl.scaled(BASE["switch_capacity"], name="switch_raw_p", T=700, d=256, d_e=256, E=16, k=1, renormalize=False,
               capacity_factor=2.0),
@@ -241,8 +242,9 @@ def test_degenerate_inputs():
     assert torch.all(out.f == 0) and torch.all(out.P == 0) and float(out.aux) == 0 and torch.all(out.counts == 0)
     assert torch.all(out.offsets == 0)
     # router weight zero: every logit ties, experts 0..k-1 win with gates 1/k (expert counts that
-    # take each router kernel: thread per token, wave per token with 1 and 4 chunks per lane)
-    for E in (300, 40, 8):
+    # take each router path: logits from the GEMM, wave per token with 4 and 1 chunks per lane,
+    # thread per token)
+    for E in (320, 300, 40, 8):
         w = wl.scaled(BASE["mixtral_prefill"], name="ties", T=70, d=128, d_e=128, E=E, k=3)
         inp = wl.make_inputs(w)
         dev = upload(inp)
