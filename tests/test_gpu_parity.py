@@ -104,13 +104,16 @@ def _upload_i32(a):
 
 
 @needs_gpu
-@pytest.mark.parametrize("variant", ["softmax", "sigmoid_grouped", "fp8_weights", "mxfp4_weights"])
+@pytest.mark.parametrize("variant", ["softmax", "sigmoid_grouped", "fp8_weights", "mxfp4_weights", "many_experts"])
 def test_split_calls_compose(variant):
     """moe_route -> moe_permute -> moe_expert_ffn (+ shared) -> moe_combine equals moe_forward."""
     extra = {"softmax": {}, "fp8_weights": dict(weights="fp8_e4m3"), "mxfp4_weights": dict(weights="mxfp4"),
-             "sigmoid_grouped": dict(scoring="sigmoid", n_group=4, topk_group=2, router_bias_var=1e-3)}[variant]
-    w = wl.scaled(BASE["deepseek_v3"], name="split", T=211, d=256, d_e=128, E=16, k=3, d_e_shared=256,
-                  capacity_factor=1.1, **extra)
+             "sigmoid_grouped": dict(scoring="sigmoid", n_group=4, topk_group=2, router_bias_var=1e-3),
+             # 256 experts: moe_route takes the logits-GEMM router path
+             "many_experts": dict(E=256, k=8)}[variant]
+    kw = dict(name="split", T=211, d=256, d_e=128, E=16, k=3, d_e_shared=256, capacity_factor=1.1)
+    kw.update(extra)
+    w = wl.scaled(BASE["deepseek_v3"], **kw)
     inp = wl.make_inputs(w)
     dev = upload(inp)
     shape, cap = gp.shape_of(w)
