@@ -393,8 +393,8 @@ def main():
     a = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the layer is measured at its per-GPU shape; "
-                          "multi-GPU expert parallelism is design-only (see DESIGN.md)", "n_gpus": a.gpus}))
+        print(json.dumps({"error": "one GPU only: the layer is measured at its per-GPU shape; expert "
+                          "parallelism across GPUs is not implemented", "n_gpus": a.gpus}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
