@@ -268,7 +268,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x
                                                          const int32_t* __restrict__ row_of,
                                                          const int32_t* __restrict__ counts,
                                                          const float* __restrict__ part, int npart, float d_aux,
-                                                         float* __restrict__ dr, float* __restrict__ dgate) {
+                                                         float* __restrict__ dr, float* __restrict__ dgate,
+                                                         const float* __restrict__ logits_in, int lsplit) {
   constexpr int TB = kRouteTokens;
   const bool sigm = scoring == 1;
   extern __shared__ float smem[];
@@ -276,7 +277,10 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const T* __restrict__ x
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
-  router_block_logits<T>(x, w_r, sigm ? nullptr : b_r, T_, d, E, t0, logits, wave, lane, tid);
+  if (logits_in)     // the forward read the router GEMM's logits too
+    router_block_logits_from(logits_in, lsplit, T_, E, t0, sigm ? nullptr : b_r, logits, tid, 256);
+  else
+    router_block_logits<T>(x, w_r, sigm ? nullptr : b_r, T_, d, E, t0, logits, wave, lane, tid);
 
   const int nq = (E + 63) / 64;
   const float aux_scale = T_ > 0 ? d_aux * (float)E / ((float)T_ * (float)T_ * (float)k) : 0.f;
@@ -360,11 +364,12 @@ template <typename T, int NQ>
 static void router_bwd_launch(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
                               const float* b_r, int T_, int d, int E, int k, int renorm, int scoring,
                               const int32_t* idx, const float* gate, const int32_t* row_of, const int32_t* counts,
-                              const float* part, int npart, float d_aux, float* dr, float* dgate) {
+                              const float* part, int npart, float d_aux, float* dr, float* dgate,
+                              const float* logits_in, int lsplit) {
   auto kern = router_bwd_kernel<T, NQ>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k, renorm,
-                     scoring, idx, gate, row_of, counts, part, npart, d_aux, dr, dgate);
+                     scoring, idx, gate, row_of, counts, part, npart, d_aux, dr, dgate, logits_in, lsplit);
 }
 
 template <typename T>
@@ -372,30 +377,38 @@ static void router_bwd_launch_nq(int nb, size_t lds, hipStream_t stream, const v
                                  const float* b_r, int T_, int d, int E, int k, int renorm, int scoring,
                                  const int32_t* idx, const float* gate, const int32_t* row_of,
                                  const int32_t* counts, const float* part, int npart, float d_aux, float* dr,
-                                 float* dgate) {
+                                 float* dgate, const float* logits_in, int lsplit) {
   if (E <= 64)
     router_bwd_launch<T, 1>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, idx, gate, row_of, counts,
-                            part, npart, d_aux, dr, dgate);
+                            part, npart, d_aux, dr, dgate, logits_in, lsplit);
   else if (E <= 256)
     router_bwd_launch<T, 4>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, idx, gate, row_of, counts,
-                            part, npart, d_aux, dr, dgate);
+                            part, npart, d_aux, dr, dgate, logits_in, lsplit);
   else
     router_bwd_launch<T, 16>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, idx, gate, row_of, counts,
-                             part, npart, d_aux, dr, dgate);
+                             part, npart, d_aux, dr, dgate, logits_in, lsplit);
 }
 
 hipError_t launch_router_bwd(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E, int k,
                              int renorm, int scoring, const int32_t* idx, const float* gate, const int32_t* row_of,
                              const int32_t* counts, const float* part, int npart, float d_aux, float* dr,
-                             float* dgate, hipStream_t stream) {
+                             float* dgate, float* logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  const float* logits_in = nullptr;
+  if (router_logits_by_gemm(E)) {   // the forward's logits path, recomputed the same way
+    if (!logits) return hipErrorInvalidValue;
+    const hipError_t e = launch_gemm_router(dtype, x, w_r, T, d, E, logits, stream);
+    if (e != hipSuccess) return e;
+    logits_in = logits;
+  }
+  const int lsplit = router_gemm_ksplit(d);
   const size_t lds = (size_t)router_ksplit(E) * kRouteTokens * E * sizeof(float);
   if (dtype == 1)
     router_bwd_launch_nq<uint16_t>(route_blocks(T), lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, idx, gate,
-                                   row_of, counts, part, npart, d_aux, dr, dgate);
+                                   row_of, counts, part, npart, d_aux, dr, dgate, logits_in, lsplit);
   else
     router_bwd_launch_nq<float>(route_blocks(T), lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, idx, gate,
-                                row_of, counts, part, npart, d_aux, dr, dgate);
+                                row_of, counts, part, npart, d_aux, dr, dgate, logits_in, lsplit);
   return hipGetLastError();
 }
 

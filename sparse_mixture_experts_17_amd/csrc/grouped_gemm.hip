@@ -105,7 +105,9 @@ hipError_t launch_gemm_router(int dtype, const void* x, const void* w_r, int T, 
   if (!router_logits_by_gemm(E) || d % 64 != 0) return hipErrorInvalidValue;
   GemmArgs a{x, nullptr, w_r, nullptr, nullptr, nullptr, nullptr, nullptr, 1, T, E, d, logits};
   a.dense_n_minor = 1;   // an XCD's tiles share their token rows; W_r (E x d) stays in its L2
-  // 64 x 64 tiles: about one per CU at 4096 tokens x 256 experts
+  a.ksplit = router_gemm_ksplit(d);
+  a.split_stride = (size_t)T * E;
+  // 64 x 64 tiles, times the K chunks: 1,024 work items at 4096 tokens x 256 experts
   const int tiles_m = (T + 63) / 64;
   if (dtype == 1) return launch_cfg<uint16_t, 64, 64, 2, 2, false, 4, 4>(a, tiles_m, stream);
   return launch_cfg<float, 64, 64, 2, 2, false, 4, 4>(a, tiles_m, stream);

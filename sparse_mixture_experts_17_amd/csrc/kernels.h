@@ -16,18 +16,27 @@ inline int route_blocks(int T) { return (T + kRouteTokens - 1) / kRouteTokens; }
 // Router: fp32 logits via MFMA, softmax or sigmoid scores, top-k (optionally limited to the
 // best topk_group of n_group expert groups; lowest index on ties), gates, per-block partial
 // sums of p (or s) and per-block expert histograms.  When router_logits_by_gemm(E), the logits
-// come from a dense GEMM into `logits` ([T, E] fp32 scratch) first; otherwise `logits` is unused.
+// come from a dense GEMM into `logits` (router_gemm_ksplit(d) partial [T, E] fp32 arrays) first;
+// otherwise `logits` is unused.
 hipError_t launch_router(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d,
                          int E, int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx,
                          float* gate, float* p_part, int32_t* hist, float* logits, hipStream_t stream);
 
-// Many experts: the fused router's blocks (16 tokens each) would each stream all of W_r; a tiled
-// GEMM reads it once per 64 tokens.  Used where the fused router does not split the contraction
-// across waves (more than 128 experts), so both accumulate every logit in the same order and
-// give the same bits, and where E is a whole number of 64-wide GEMM tiles.
-inline bool router_logits_by_gemm(int E) { return E > 128 && E % 64 == 0; }
+// 64 or more experts (a whole number of 64-wide tiles): a 16-token router block would stream all
+// of W_r, so a tiled GEMM computes the logits instead, its contraction cut into router_gemm_ksplit
+// chunks for parallelism.  The forward and the backward both read these logits, summing the
+// chunks in order, so both see the same bits.
+inline bool router_logits_by_gemm(int E) { return E >= 64 && E % 64 == 0; }
+inline int router_gemm_ksplit(int d) {
+  const int steps = d / 64;                               // 64-element K steps
+  return steps % 4 == 0 ? 4 : (steps % 2 == 0 ? 2 : 1);
+}
+inline size_t router_logits_bytes(int T, int d, int E) {
+  return router_logits_by_gemm(E) ? (size_t)router_gemm_ksplit(d) * (size_t)T * (size_t)E * sizeof(float) : 0;
+}
 
-// Dense logits [T, E] = x [T, d] W_r^T in fp32 (tiles of 64 tokens x 64 experts).
+// Dense partial logits: chunk c of router_gemm_ksplit(d) writes logits + c T E = x [T, d] W_r^T over
+// its K range, in fp32 (tiles of 64 tokens x 64 experts).
 hipError_t launch_gemm_router(int dtype, const void* x, const void* w_r, int T, int d, int E, float* logits,
                               hipStream_t stream);
 
@@ -116,11 +125,12 @@ hipError_t launch_gather_t(int src_dtype, int dst_dtype, const void* src, int C,
 hipError_t launch_zero_gaps(int dtype, void* dst, int nrows, int ldt, const int32_t* offsets, const int32_t* poff,
                             int E, int n_dense, int pad_dense, hipStream_t stream);
 hipError_t launch_to_bf16(const float* src, size_t n, void* dst, hipStream_t stream);
-// dr [T, E] = dL/dlogits; dgate [T, k] (may be NULL) = sum of each kept row's partial dots
+// dr [T, E] = dL/dlogits; dgate [T, k] (may be NULL) = sum of each kept row's partial dots.
+// `logits`: scratch of router_logits_bytes(T, d, E) bytes (the logits GEMM's output), or unused.
 hipError_t launch_router_bwd(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E, int k,
                              int renorm, int scoring, const int32_t* idx, const float* gate, const int32_t* row_of,
                              const int32_t* counts, const float* part, int npart, float d_aux, float* dr,
-                             float* dgate, hipStream_t stream);
+                             float* dgate, float* logits, hipStream_t stream);
 // dw_r [E, d] = dr^T x; db_r [E] = sum_t dr (zeros when zero_bias), skipped when NULL;
 // part: scratch of dwr_workspace_bytes(T, d, E)
 size_t dwr_workspace_bytes(int T, int d, int E);

@@ -62,7 +62,7 @@ Layout layout(const moe_shape& s) {
   L.row_of = take(R * sizeof(int32_t));
   L.tstart1 = take((E + 1) * sizeof(int32_t));
   L.tstart2 = take((E + 1) * sizeof(int32_t));
-  L.logits = take(router_logits_by_gemm(s.E) ? (size_t)s.T * E * sizeof(float) : 0);
+  L.logits = take(router_logits_bytes(s.T, s.d, s.E));
   L.x_perm = take(R * (size_t)s.d * es);
   L.h = take(R * (size_t)s.d_e * es);
   L.ksplit = down_ksplit(s, choose_kind(std::max<long long>((long long)R, 1), s.E, s.capacity));
@@ -77,7 +77,7 @@ Layout layout(const moe_shape& s) {
 // expert's rows from a 64-aligned column (ldt bounds the padded total).
 struct BwdLayout {
   size_t poff, koff_dense, ts1, ts2, g_row, wdT, wguT, dyb, a, b, hT, dab, dabT, part, dr, dX, xT, doT;
-  size_t swdT, swguT, sa, sb, shT, sdab, sdabT, sdX, sdyT, sxT, dwr_part, total;
+  size_t swdT, swguT, sa, sb, shT, sdab, sdabT, sdX, sdyT, sxT, dwr_part, logits, total;
   int ldt, ldts, npart;
   GemmKind kind, skind;
 };
@@ -124,6 +124,7 @@ BwdLayout bwd_layout(const moe_shape& s) {
   L.sdyT = take(des > 0 ? d * ldts * es : 0);
   L.sxT = take(des > 0 ? d * ldts * es : 0);
   L.dwr_part = take(dwr_workspace_bytes(s.T, s.d, s.E));
+  L.logits = take(router_logits_bytes(s.T, s.d, s.E));
   L.total = off;
   return L;
 }
@@ -473,7 +474,7 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const void* w_r, 
   }
   MOE_MARK(MOE_BSTAGE_ROUTER_BWD);
   MOE_HIP(launch_router_bwd(s.dtype, x, w_r, b_r, T, d, E, s.k, s.renormalize, s.scoring, idx, gate, row_of, counts,
-                            part, L.npart, d_aux, dr, dgate, st));
+                            part, L.npart, d_aux, dr, dgate, at<float>(ws, L.logits), st));
   MOE_MARK(MOE_BSTAGE_DX_EXPERT);
   if (T > 0)
     MOE_HIP(launch_gemm_down(kind, s.dtype, 0, dab, wguT, nullptr, offsets, ts2, E, 0, tiles2, d, 2 * de, dX, 1, 0,

@@ -32,8 +32,8 @@ namespace moe {
 
 // NQ: 64-expert chunks per lane (E <= 64 NQ), so small expert counts skip empty chunks.
 // WAVES = 4: the block computes its logits (phase 1 above).  WAVES = 8 or 16: the logits come
-// from the router GEMM's [T, E] output (logits_in), and more waves share the 16 tokens, so each
-// wave's chain of shuffles covers fewer tokens.
+// from the router GEMM's lsplit partial [T, E] arrays (logits_in), and more waves share the 16
+// tokens, so each wave's chain of shuffles covers fewer tokens.
 template <typename T, int NQ, int WAVES = 4>
 __global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
                                                      const float* __restrict__ b_r, int T_, int d, int E,
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict_
                                                      int topk_group, int32_t* __restrict__ idx,
                                                      float* __restrict__ gate, float* __restrict__ p_part,
                                                      int32_t* __restrict__ hist,
-                                                     const float* __restrict__ logits_in) {
+                                                     const float* __restrict__ logits_in, int lsplit) {
   constexpr int TB = kRouteTokens, NT = WAVES * 64, TPW = TB / WAVES;   // tokens per wave
   static_assert(WAVES == 4 || WAVES == 8 || WAVES == 16, "16 tokens over the waves");
   const int slots = WAVES == 4 ? router_ksplit(E) : 1;
@@ -62,13 +62,7 @@ __global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict_
   if constexpr (WAVES == 4) {
     router_block_logits<T>(x, w_r, sigm ? nullptr : b_r, T_, d, E, t0, logits, wave, lane, tid);
   } else {
-    const float* bb = sigm ? nullptr : b_r;
-    for (int i = tid; i < TB * E; i += NT) {
-      const int tl = i / E, e = i - tl * E;
-      const int t = min(t0 + tl, T_ - 1);                 // rows past T repeat row T-1; never used
-      logits[i] = logits_in[(size_t)t * E + e] + (bb ? bb[e] : 0.f);
-    }
-    __syncthreads();
+    router_block_logits_from(logits_in, lsplit, T_, E, t0, sigm ? nullptr : b_r, logits, tid, NT);
   }
 
   // ---- phase 2: scores and top-k, one token per wave at a time
@@ -330,42 +324,46 @@ static void router_tpt_launch(int nb, size_t lds, hipStream_t stream, const void
 template <typename T, int NQ, int WAVES = 4>
 static void router_launch(int nb, hipStream_t stream, const void* x, const void* w_r, const float* b_r,
                           int T_, int d, int E, int k, int renorm, int scoring, int n_group, int topk_group,
-                          int32_t* idx, float* gate, float* p_part, int32_t* hist, const float* logits_in) {
+                          int32_t* idx, float* gate, float* p_part, int32_t* hist, const float* logits_in,
+                          int lsplit) {
   const int slots = WAVES == 4 ? router_ksplit(E) : 1;
   const size_t lds = (size_t)(slots * kRouteTokens * E + 2 * WAVES * E) * sizeof(float) + (size_t)E * sizeof(int);
   auto kern = router_kernel<T, NQ, WAVES>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kern, dim3(nb), dim3(WAVES * 64), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k,
-                     renorm, scoring, n_group, topk_group, idx, gate, p_part, hist, logits_in);
+                     renorm, scoring, n_group, topk_group, idx, gate, p_part, hist, logits_in, lsplit);
 }
 
 template <typename T>
 static void router_launch_nq(int nb, hipStream_t stream, const void* x, const void* w_r, const float* b_r, int T_,
                              int d, int E, int k, int renorm, int scoring, int n_group, int topk_group, int32_t* idx,
-                             float* gate, float* p_part, int32_t* hist, const float* logits_in) {
-  if (logits_in) {              // many experts, logits from the GEMM (E > 128)
-    if (E <= 256)
+                             float* gate, float* p_part, int32_t* hist, const float* logits_in, int lsplit) {
+  if (logits_in) {              // logits from the GEMM (64 or more experts)
+    if (E <= 64)
+      router_launch<T, 1, 16>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
+                              p_part, hist, logits_in, lsplit);
+    else if (E <= 256)
       router_launch<T, 4, 16>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                              p_part, hist, logits_in);
+                              p_part, hist, logits_in, lsplit);
     else if (E <= 512)
       router_launch<T, 16, 16>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                               p_part, hist, logits_in);
+                               p_part, hist, logits_in, lsplit);
     else                        // 8 waves keep the per-wave LDS rows within 160 KB
       router_launch<T, 16, 8>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                              p_part, hist, logits_in);
+                              p_part, hist, logits_in, lsplit);
   } else if (E <= 16) {
     const size_t lds = (size_t)(router_ksplit(E) * kRouteTokens * E + 8 * E) * sizeof(float) + (size_t)E * sizeof(int);
     router_tpt_launch<T, 16>(nb, lds, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx,
                              gate, p_part, hist);
   } else if (E <= 64) {
     router_launch<T, 1>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part,
-                        hist, nullptr);
+                        hist, nullptr, 1);
   } else if (E <= 256) {
     router_launch<T, 4>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part,
-                        hist, nullptr);
+                        hist, nullptr, 1);
   } else {
     router_launch<T, 16>(nb, stream, x, w_r, b_r, T_, d, E, k, renorm, scoring, n_group, topk_group, idx, gate, p_part,
-                         hist, nullptr);
+                         hist, nullptr, 1);
   }
 }
 
@@ -380,12 +378,13 @@ hipError_t launch_router(int dtype, const void* x, const void* w_r, const float*
     if (e != hipSuccess) return e;
     logits_in = logits;
   }
+  const int lsplit = router_gemm_ksplit(d);
   if (dtype == 1)
     router_launch_nq<uint16_t>(nb, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                               p_part, hist, logits_in);
+                               p_part, hist, logits_in, lsplit);
   else
     router_launch_nq<float>(nb, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group, idx, gate,
-                            p_part, hist, logits_in);
+                            p_part, hist, logits_in, lsplit);
   return hipGetLastError();
 }
 

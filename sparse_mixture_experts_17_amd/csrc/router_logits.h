@@ -102,4 +102,21 @@ __device__ __forceinline__ void router_block_logits(const T* __restrict__ x, con
   __syncthreads();
 }
 
+// The same [kRouteTokens][E] LDS logits from the router GEMM's output: ksp partial [T, E] arrays
+// summed in chunk order, then the bias when b_r != NULL; ends with a block barrier.
+__device__ __forceinline__ void router_block_logits_from(const float* __restrict__ lg, int ksp, int T_, int E,
+                                                         int t0, const float* __restrict__ b_r, float* logits,
+                                                         int tid, int nthreads) {
+  const size_t chunk = (size_t)T_ * E;
+  for (int i = tid; i < kRouteTokens * E; i += nthreads) {
+    const int tl = i / E, e = i - tl * E;
+    const int t = min(t0 + tl, T_ - 1);                   // rows past T repeat row T-1; never used
+    const float* src = lg + (size_t)t * E + e;
+    float v = src[0];
+    for (int c = 1; c < ksp; ++c) v += src[c * chunk];
+    logits[i] = v + (b_r ? b_r[e] : 0.f);
+  }
+  __syncthreads();
+}
+
 }  // namespace moe
