@@ -40,6 +40,28 @@ inline size_t router_logits_bytes(int T, int d, int E) {
 hipError_t launch_gemm_router(int dtype, const void* x, const void* w_r, int T, int d, int E, float* logits,
                               hipStream_t stream);
 
+// Routing and dispatch of a batch that is one router block (decode: at most 16 tokens, at most
+// 16 experts) in one launch: the router block also runs the scan's expert pass and the ranks.
+// The outputs equal launch_router + launch_scan + launch_rank_gather (without x_perm) bit for bit.
+struct SmallDispatch {
+  int cap = -1;
+  int32_t* counts = nullptr;       // may be NULL
+  int32_t* kept = nullptr;
+  int32_t* offsets = nullptr;
+  float* f = nullptr;
+  float* P = nullptr;
+  float* aux = nullptr;
+  int bm1 = 1, bm2 = 1;
+  int32_t* tstart1 = nullptr;
+  int32_t* tstart2 = nullptr;
+  int32_t* row_token = nullptr;
+  int32_t* row_of = nullptr;
+};
+inline bool route_small_ok(int T, int E) { return T >= 1 && T <= kRouteTokens && E <= 16; }
+hipError_t launch_route_small(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E, int k,
+                              int renorm, int scoring, int n_group, int topk_group, int32_t* idx, float* gate,
+                              const SmallDispatch& sd, hipStream_t stream);
+
 // Per-chunk expert histograms of an index array (dispatch without the router).
 hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t stream);
 

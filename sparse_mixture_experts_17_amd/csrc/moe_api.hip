@@ -345,17 +345,39 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   int32_t* ts1 = at<int32_t>(ws, L.tstart1);
   int32_t* ts2 = at<int32_t>(ws, L.tstart2);
   MOE_MARK(MOE_STAGE_ROUTER);
-  if (s.T > 0)
+  // A batch of one router block with few experts (decode) routes and dispatches in one launch;
+  // its scan and permute stages are then empty.
+  const bool small = route_small_ok(s.T, s.E);
+  if (small) {
+    SmallDispatch sd;
+    sd.cap = s.capacity;
+    sd.counts = counts;
+    sd.kept = kept;
+    sd.offsets = offsets;
+    sd.f = f;
+    sd.P = P;
+    sd.aux = aux;
+    sd.bm1 = bm1;
+    sd.bm2 = bm2;
+    sd.tstart1 = ts1;
+    sd.tstart2 = ts2;
+    sd.row_token = row_token;
+    sd.row_of = row_of;
+    MOE_HIP(launch_route_small(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, s.scoring, s.n_group,
+                               s.topk_group, idx, gate, sd, st));
+  } else if (s.T > 0) {
     MOE_HIP(launch_router(s.dtype, x, w_r, b_r, s.T, s.d, s.E, s.k, s.renormalize, s.scoring, s.n_group,
                           s.topk_group, idx, gate, at<float>(ws, L.p_part), at<int32_t>(ws, L.hist),
                           at<float>(ws, L.logits), st));
+  }
   MOE_MARK(MOE_STAGE_SCAN);
-  MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts, kept,
-                      offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm1, ts1, bm2, ts2, st));
+  if (!small)
+    MOE_HIP(launch_scan(at<int32_t>(ws, L.hist), at<float>(ws, L.p_part), nb, s.T, s.k, s.E, s.capacity, counts,
+                        kept, offsets, at<int32_t>(ws, L.chunk_base), f, P, aux, bm1, ts1, bm2, ts2, st));
   // The forward pass does not materialise x_perm: the permute stage produces the row
   // indices and the gate/up GEMM gathers token rows of x through them as it loads.
   MOE_MARK(MOE_STAGE_PERMUTE);
-  if (s.T > 0)
+  if (!small && s.T > 0)
     MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
                                offsets, row_token, row_of, nullptr, st));
   MOE_MARK(MOE_STAGE_GATE_UP);

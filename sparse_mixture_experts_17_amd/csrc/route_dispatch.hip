@@ -18,6 +18,60 @@
 
 namespace moe {
 
+// ------------------------------------------------------------------------------ wave scans
+
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if ((int)(threadIdx.x & 63) >= o) x += y;
+  }
+  *total = __shfl(x, kWave - 1, kWave);
+  return x - v;
+}
+
+// The expert-level part of the scan for E <= 64, in one wave (lane e = expert e, cnt and pe
+// its totals, zero for e >= E): kept, offsets, tile starts, f, P and aux; returns expert e's
+// first row.  aux is summed by the same halving tree as the 1024-wide version, so both give
+// the same bits.
+__device__ __forceinline__ int scan_finish_wave(int e, int cnt, float pe, bool with_p, int T, int k, int E, int cap,
+                                                int32_t* counts, int32_t* kept, int32_t* offsets, float* f,
+                                                float* P, float* aux, int bm1, int32_t* tstart1, int bm2,
+                                                int32_t* tstart2) {
+  const int kp = e < E ? (cap < 0 ? cnt : min(cnt, cap)) : 0;
+  int tot, tot1, tot2;
+  const int off = wave_excl_scan(kp, &tot);
+  const int ts1 = wave_excl_scan((kp + bm1 - 1) / bm1, &tot1);
+  const int ts2 = wave_excl_scan((kp + bm2 - 1) / bm2, &tot2);
+  if (e < E) {
+    if (counts) counts[e] = cnt;
+    kept[e] = kp;
+    offsets[e] = off;
+    tstart1[e] = ts1;
+    tstart2[e] = ts2;
+  }
+  if (e == 0) {
+    offsets[E] = tot;
+    tstart1[E] = tot1;
+    tstart2[E] = tot2;
+  }
+  if (with_p) {
+    const long long R = (long long)T * k;
+    const float fe = (e < E && R > 0) ? (float)((double)cnt / (double)R) : 0.f;
+    const float Pe = (e < E && T > 0) ? pe / (float)T : 0.f;
+    if (e < E) {
+      f[e] = fe;
+      P[e] = Pe;
+    }
+    float v = fe * Pe;
+#pragma unroll
+    for (int h = 32; h > 0; h >>= 1) v += __shfl_down(v, h, kWave);
+    if (e == 0) aux[0] = (float)E * v;
+  }
+  return off;
+}
+
 // ------------------------------------------------------------------------------ router
 //
 // One block = 16 tokens x all E experts, 4 waves.
@@ -196,13 +250,13 @@ __global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict_
 // selection rule is router_kernel's: highest score, ties to the lower index (groups too).
 // LDS: the four K-partial slots of the logits, reused after the sum as slot 0 = logits,
 // slot 1 = p, slot 2 = selection scores (group limit only), slot 3 = chosen experts.
-template <typename T, int EB>
+template <typename T, int EB, bool FUSE>
 __global__ __launch_bounds__(256) void router_tpt_kernel(const T* __restrict__ x, const T* __restrict__ w_r,
                                                          const float* __restrict__ b_r, int T_, int d, int E,
                                                          int k, int renorm, int scoring, int n_group,
                                                          int topk_group, int32_t* __restrict__ idx,
                                                          float* __restrict__ gate, float* __restrict__ p_part,
-                                                         int32_t* __restrict__ hist) {
+                                                         int32_t* __restrict__ hist, SmallDispatch sd) {
   static_assert(EB <= 64, "E <= 64 keeps router_ksplit(E) == 4, so four logit slots exist");
   constexpr int TB = kRouteTokens;
   const bool sigm = scoring == 1;
@@ -212,6 +266,7 @@ __global__ __launch_bounds__(256) void router_tpt_kernel(const T* __restrict__ x
   float* sbuf = smem + 2 * TB * E;                       // [TB][E]
   int* cbuf = (int*)(smem + 3 * TB * E);                 // [TB][k]
   int* lhist = (int*)(smem + 4 * TB * E);                // [E]
+  int* s_off = lhist + E;                                // [E] (FUSE: each expert's first row)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -303,22 +358,62 @@ __global__ __launch_bounds__(256) void router_tpt_kernel(const T* __restrict__ x
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {                   // block partial of p, tokens in order
-    float ps = 0.f;
-    for (int tl = 0; tl < ntok; ++tl) ps += pbuf[tl * E + e];
-    p_part[(size_t)blockIdx.x * E + e] = ps;
-    hist[(size_t)blockIdx.x * E + e] = lhist[e];
+  if constexpr (!FUSE) {
+    for (int e = tid; e < E; e += 256) {                 // block partial of p, tokens in order
+      float ps = 0.f;
+      for (int tl = 0; tl < ntok; ++tl) ps += pbuf[tl * E + e];
+      p_part[(size_t)blockIdx.x * E + e] = ps;
+      hist[(size_t)blockIdx.x * E + e] = lhist[e];
+    }
+  } else {
+    // The whole batch is this block (one chunk of the counting sort, so every chunk base is 0):
+    // wave 0 runs the scan's expert pass on the block totals (p summed over tokens in order, as
+    // the block partial would be), then each assignment takes its rank among the earlier
+    // assignments to the same expert, in arrival order, and its row.
+    if (wave == 0) {
+      const int e = lane;
+      float ps = 0.f;
+      if (e < E)
+        for (int tl = 0; tl < ntok; ++tl) ps += pbuf[tl * E + e];
+      const int off = scan_finish_wave(e, e < E ? lhist[e] : 0, ps, true, T_, k, E, sd.cap, sd.counts, sd.kept,
+                                       sd.offsets, sd.f, sd.P, sd.aux, sd.bm1, sd.tstart1, sd.bm2, sd.tstart2);
+      if (e < E) s_off[e] = off;
+    }
+    __syncthreads();
+    if (tid < ntok * k) {
+      const int e = cbuf[tid];                           // slot tid = token tid / k, choice tid % k
+      int r = 0;
+      for (int j = 0; j < tid; ++j) r += (cbuf[j] == e);
+      const int row = (sd.cap < 0 || r < sd.cap) ? s_off[e] + r : -1;
+      sd.row_of[tid] = row;
+      if (row >= 0) sd.row_token[row] = tid / k;
+    }
   }
 }
 
-template <typename T, int EB>
+template <typename T, int EB, bool FUSE = false>
 static void router_tpt_launch(int nb, size_t lds, hipStream_t stream, const void* x, const void* w_r,
                               const float* b_r, int T_, int d, int E, int k, int renorm, int scoring, int n_group,
-                              int topk_group, int32_t* idx, float* gate, float* p_part, int32_t* hist) {
-  auto kern = router_tpt_kernel<T, EB>;
+                              int topk_group, int32_t* idx, float* gate, float* p_part, int32_t* hist,
+                              const SmallDispatch& sd = SmallDispatch{}) {
+  auto kern = router_tpt_kernel<T, EB, FUSE>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kern, dim3(nb), dim3(256), lds, stream, (const T*)x, (const T*)w_r, b_r, T_, d, E, k, renorm,
-                     scoring, n_group, topk_group, idx, gate, p_part, hist);
+                     scoring, n_group, topk_group, idx, gate, p_part, hist, sd);
+}
+
+hipError_t launch_route_small(int dtype, const void* x, const void* w_r, const float* b_r, int T, int d, int E, int k,
+                              int renorm, int scoring, int n_group, int topk_group, int32_t* idx, float* gate,
+                              const SmallDispatch& sd, hipStream_t stream) {
+  if (!route_small_ok(T, E)) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(router_ksplit(E) * kRouteTokens * E + 8 * E) * sizeof(float) + (size_t)E * sizeof(int);
+  if (dtype == 1)
+    router_tpt_launch<uint16_t, 16, true>(1, lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group,
+                                          topk_group, idx, gate, nullptr, nullptr, sd);
+  else
+    router_tpt_launch<float, 16, true>(1, lds, stream, x, w_r, b_r, T, d, E, k, renorm, scoring, n_group, topk_group,
+                                       idx, gate, nullptr, nullptr, sd);
+  return hipGetLastError();
 }
 
 template <typename T, int NQ, int WAVES = 4>
@@ -410,56 +505,6 @@ hipError_t launch_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, h
 
 // ------------------------------------------------------------------------------ scan (1 block)
 //
-__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if ((int)(threadIdx.x & 63) >= o) x += y;
-  }
-  *total = __shfl(x, kWave - 1, kWave);
-  return x - v;
-}
-
-// The expert-level part of the scan for E <= 64, in one wave (lane e = expert e, cnt and pe
-// its totals, zero for e >= E): kept, offsets, tile starts, f, P and aux.  aux is summed by
-// the same halving tree as the 1024-wide version, so both give the same bits.
-__device__ __forceinline__ void scan_finish_wave(int e, int cnt, float pe, bool with_p, int T, int k, int E, int cap,
-                                                 int32_t* counts, int32_t* kept, int32_t* offsets, float* f,
-                                                 float* P, float* aux, int bm1, int32_t* tstart1, int bm2,
-                                                 int32_t* tstart2) {
-  const int kp = e < E ? (cap < 0 ? cnt : min(cnt, cap)) : 0;
-  int tot, tot1, tot2;
-  const int off = wave_excl_scan(kp, &tot);
-  const int ts1 = wave_excl_scan((kp + bm1 - 1) / bm1, &tot1);
-  const int ts2 = wave_excl_scan((kp + bm2 - 1) / bm2, &tot2);
-  if (e < E) {
-    if (counts) counts[e] = cnt;
-    kept[e] = kp;
-    offsets[e] = off;
-    tstart1[e] = ts1;
-    tstart2[e] = ts2;
-  }
-  if (e == 0) {
-    offsets[E] = tot;
-    tstart1[E] = tot1;
-    tstart2[E] = tot2;
-  }
-  if (with_p) {
-    const long long R = (long long)T * k;
-    const float fe = (e < E && R > 0) ? (float)((double)cnt / (double)R) : 0.f;
-    const float Pe = (e < E && T > 0) ? pe / (float)T : 0.f;
-    if (e < E) {
-      f[e] = fe;
-      P[e] = Pe;
-    }
-    float v = fe * Pe;
-#pragma unroll
-    for (int h = 32; h > 0; h >>= 1) v += __shfl_down(v, h, kWave);
-    if (e == 0) aux[0] = (float)E * v;
-  }
-}
-
 // Per-chunk bases by expert: chunk_base[b][e] = assignments to e in chunks < b;
 // counts[e] = all of them.  The chunks are cut into G <= 1024 / E contiguous groups of
 // about kScanBatch chunks, so most threads work and each reads its group in one batch of
