@@ -5,7 +5,8 @@ One step = one moe_forward call (router, dispatch, grouped SwiGLU experts, combi
 over one batch of synthetic tokens already resident in device memory.  Default
 workload: the Mixtral 8x7B layer shape at a prefill batch of 4096 tokens (bf16
 weights and activations, fp32 accumulate).  A decode-batch line (16 tokens, same
-weights) rides along as "secondary", the split ABI's moe_permute (the gather of token
+weights) rides along as "secondary" (also timed as replays of the call captured in a HIP
+graph: ms_per_step_graph), the split ABI's moe_permute (the gather of token
 rows into expert order) on the prefill routing as "secondary_permute", the backward pass
 of the prefill call as "secondary_backward", and decode with FP8 and MXFP4 expert weights
 as "secondary_fp8" and "secondary_mxfp4".
@@ -111,7 +112,7 @@ def measured_traffic(workload: str, stage: str):
     return t.get("per_launch_bytes", {}).get(workload, {}).get(stage)
 
 
-def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
+def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up", graph=False):
     """Upload a workload and time moe_forward on it.
 
     Timed region: `steps` calls, each recording HIP events only at the start and end of
@@ -192,12 +193,35 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up"):
     torch.cuda.synchronize()
     plain_ms = a.elapsed_time(b) / steps
     stages = {n: float(v) for n, v in zip(names, stage_ms.mean(axis=0))}
+    graph_ms = None
+    if graph:
+        # the same call captured once in a HIP graph and replayed (no per-launch host work)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            call()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for s_ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / steps
+        del g
     kept = out.kept.cpu().numpy()
     R_kept = int(kept.sum())
     touched = int((kept > 0).sum())
     return dict(w=w, shape=shape, cap=cap, total_ms=total_ms, wall_s=t_wall, stages=stages, kernel_ms=kernel_ms,
                 steps=steps,
-                plain_ms=plain_ms, R_kept=R_kept, touched=touched, upload_s=t_up, dev=dev, inp=inp, out=out)
+                plain_ms=plain_ms, graph_ms=graph_ms, R_kept=R_kept, touched=touched, upload_s=t_up, dev=dev, inp=inp,
+                out=out)
 
 
 def run_permute(info, steps, warmup):
@@ -273,6 +297,7 @@ def secondary_line(dec, fmt):
     return {
         "workload": wd.name, "value": wd.T / (dms / 1e3), "unit": "tokens/s", "ms_per_step": dms,
         "stages_ms": dec["stages"], "experts_touched": dec["touched"], "ms_per_step_unmarked": dec["plain_ms"],
+        "ms_per_step_graph": dec["graph_ms"],
         "roofline": {"kernel": f"grouped_gemm gate_up (decode tiles, {fmt} weights)", "bound": "hbm",
                      "achieved": gb, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
                      "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
@@ -441,7 +466,7 @@ def main():
     }
     if not a.no_secondary and w.name == "mixtral_prefill":
         print("[bench] secondary: mixtral_decode on the same weights", file=sys.stderr, flush=True)
-        dec = run_gpu("mixtral_decode", max(a.steps, 20), a.warmup, dev_weights=info["dev"])
+        dec = run_gpu("mixtral_decode", max(a.steps, 20), a.warmup, dev_weights=info["dev"], graph=True)
         wd = dec["w"]
         dwork = layer_work(wd, dec["R_kept"], dec["touched"])
         dms = dec["total_ms"] / max(a.steps, 20)
@@ -449,6 +474,7 @@ def main():
         line["secondary"] = {
             "workload": wd.name, "value": wd.T / (dms / 1e3), "unit": "tokens/s", "ms_per_step": dms,
             "stages_ms": dec["stages"], "experts_touched": dec["touched"], "ms_per_step_unmarked": dec["plain_ms"],
+            "ms_per_step_graph": dec["graph_ms"],
             "roofline": {"kernel": "grouped_gemm gate_up (decode tiles)", "bound": "hbm", "achieved": gb,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
                          "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
@@ -471,7 +497,7 @@ def main():
         del dec
         print("[bench] secondary: mixtral_decode_mxfp4 (MXFP4 expert weights)", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-        dec = run_gpu("mixtral_decode_mxfp4", max(a.steps, 20), a.warmup)
+        dec = run_gpu("mixtral_decode_mxfp4", max(a.steps, 20), a.warmup, graph=True)
         line["secondary_mxfp4"] = secondary_line(dec, "MXFP4")
     if not a.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
