@@ -2,14 +2,15 @@
 
 TEST INFRASTRUCTURE (see the package docstring).
 
-Zero to Frontier §13.1, "Total and active parameters": one MoE layer with E
-SwiGLU experts of width d_e, a bias-free d x E router and k experts per token
-stores 3 d d_e E + d E parameters and uses 3 d d_e k + d E per token.  The
-whole-model count follows the page's exercise "Total and active parameters of an
-MoE model": every FFN and expert is a bias-free SwiGLU, each layer has two
-RMSNorm gains of size d, one final norm, shared experts are always active, the
-first n_dense layers keep a dense FFN of width d_ff, and embedding matrices are
-counted in full in both numbers (one matrix if tied, two otherwise).
+Zero to Frontier §13.1, "Total and active parameters" (and its exercise "Total and
+active parameters of an MoE model"): a layer's experts are E SwiGLU blocks of three
+d x d_e matrices each, plus a d x E router matrix with no bias; a token touches its k
+experts and the whole router.  For a whole decoder the counting rules taken from the
+same exercise: no linear layer carries a bias; each block has two RMSNorm gain
+vectors of length d and the model one more at the end; shared experts count as
+active for every token; the first n_dense blocks use a dense SwiGLU FFN of width
+d_ff instead of experts; the embedding (and, when untied, the output projection)
+counts fully in both totals.
 
 FLOPs: "FLOPs per token, and the 6N rule for MoE" and the dense-vs-MoE table of
 the "In PyTorch" section give 2 FLOPs per active matrix parameter per token

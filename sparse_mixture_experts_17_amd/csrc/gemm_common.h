@@ -40,6 +40,11 @@ struct GemmArgs {
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufFlags = 0x00020000;
+// Range of every buffer resource: the whole unsigned 32-bit offset space.  The offsets are
+// 32-bit byte offsets from the resource base (a gathered token row of x sits at up to
+// T*d*elem bytes past it, which the host keeps below 2^32); a smaller range would turn loads
+// past it into zeros without an error.
+constexpr int kBufRange = static_cast<int>(0xFFFFFFFFu);
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

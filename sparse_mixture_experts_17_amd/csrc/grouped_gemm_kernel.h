@@ -294,9 +294,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride) + ks0 * KB_A;
     const char* B0b = (const char*)args.B0 + brow0 * row_stride_b + ks0 * KB_B;
     const char* B1b = GATED ? (const char*)args.B1 + brow0 * row_stride_b + ks0 * KB_B : B0b;
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, 0x7fffffff, kBufFlags);
-    const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, 0x7fffffff, kBufFlags);
-    const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, 0x7fffffff, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, kBufRange, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, kBufRange, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, kBufRange, kBufFlags);
 
     uint32_t voffA[A_IT], voffB[B_IT];
     tile_offsets<Cfg>(args, wave, lane, row0, rows, row_stride, row_stride_b, voffA, voffB);
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     uint32_t voffS = 0;
     if constexpr (WF == 2) {
       const size_t gs = (size_t)g * (K / 32) * N + ks0 * 2 * KSUB * N;
-      rsS0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S0 + gs), 0, 0x7fffffff, kBufFlags);
-      rsS1 = GATED ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S1 + gs), 0, 0x7fffffff, kBufFlags)
+      rsS0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S0 + gs), 0, kBufRange, kBufFlags);
+      rsS1 = GATED ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)args.S1 + gs), 0, kBufRange, kBufFlags)
                    : rsS0;
       constexpr int PPM = BN / 16, PPMS = 2 * KSUB * PPM;
       const int qs = wave * Cfg::PW_S + min(lane, Cfg::PW_S - 1);   // [matrix][block c][piece p]

@@ -80,9 +80,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_large_kernel(GemmArgs args) 
     const char* Ab = (const char*)args.A + (args.a_rows ? 0 : (size_t)row0 * row_stride);
     const char* B0b = (const char*)args.B0 + ((size_t)g * N + (size_t)nt * BN) * row_stride;
     const char* B1b = GATED ? (const char*)args.B1 + ((size_t)g * N + (size_t)nt * BN) * row_stride : B0b;
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, 0x7fffffff, kBufFlags);
-    const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, 0x7fffffff, kBufFlags);
-    const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, 0x7fffffff, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, kBufRange, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)B0b, 0, kBufRange, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)B1b, 0, kBufRange, kBufFlags);
 
     // lane -> (row, swizzled piece) of each 16-byte load; rows past `rows` repeat the last
     uint32_t voffA[Cfg::A_IT], voffB[Cfg::B_IT];

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict_
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         pacc[q] += (v[q] == -INFINITY) ? 0.f : expf(v[q] - m) * inv;
-        sel[q] = v[q];
+        sel[q] = v[q] == v[q] ? v[q] : -INFINITY;   // a NaN logit (non-finite input) ranks last
       }
     } else {
 #pragma unroll
@@ -161,7 +161,8 @@ __global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict_
         const bool ok = v[q] != -INFINITY;
         const float a = ok ? 1.f / (1.f + expf(-v[q])) : 0.f;
         pacc[q] += a;
-        sel[q] = ok ? a + (b_r ? b_r[e] : 0.f) : -INFINITY;
+        const float sv = a + (b_r ? b_r[e] : 0.f);
+        sel[q] = ok && sv == sv ? sv : -INFINITY;
       }
     }
     if (n_group > 1) {
@@ -201,12 +202,15 @@ __global__ __launch_bounds__(WAVES * 64) void router_kernel(const T* __restrict_
     int my_e = 0;
     float my_num = 0.f, numsum = 0.f;
     for (int j = 0; j < k; ++j) {
+      // Each lane's candidate is its best untaken expert, at least its lowest untaken one (so a
+      // token whose scores are all -inf still gets a valid index); the reduction ranks by score,
+      // then lower index, and the 0x7fffffff of a lane with no untaken expert loses every tie.
       float bv = -INFINITY;
       int be = 0x7fffffff;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {     // ascending expert index within the lane: '>' keeps the lowest
         int e = q * 64 + lane;
-        if (q < nq && e < E && !((taken >> q) & 1u) && sel[q] > bv) { bv = sel[q]; be = e; }
+        if (q < nq && e < E && !((taken >> q) & 1u) && (be == 0x7fffffff || sel[q] > bv)) { bv = sel[q]; be = e; }
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {

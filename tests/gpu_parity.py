@@ -9,7 +9,8 @@ Protocol
   3. Dispatch (kept, offsets, row_token, row_of, dropped set) bit-exact against the
      oracle's dispatch of the GPU's idx; x_perm rows bit-identical to x rows.
   4. Output: max|y - y_oracle| / rms(y_oracle) <= 1e-4 (fp32) or 2e-2 (bf16), the
-     oracle run with the GPU's routing; at full size on sampled tokens.
+     oracle run with the GPU's routing, over every token (at full size too; the oracle
+     streams the experts).
   5. Backward: every gradient (dx, dW_r, db_r, dW_g, dW_u, dW_d, the shared expert's, dL/dg)
      against the oracle's backward with the GPU's routing: ||G - G_oracle|| / ||G_oracle||
      <= BWD_FROB and max|G - G_oracle| / max|G_oracle| <= BWD_PEAK per tensor and per expert
@@ -106,6 +107,70 @@ def experts_f64(inp, es, threads=16):
         return dict(ex.map(one, sorted(set(int(e) for e in es))))
 
 
+class LazyExperts:
+    """Float64 routed-expert weights for the oracle, drawn on demand with a bounded window of
+    experts drawn ahead in threads, so a full-size check holds about `window` experts in host
+    memory at a time (the oracle asks for experts in ascending order)."""
+
+    def __init__(self, inp, window=16, threads=16, tag=""):
+        self.inp, self.window, self.tag = inp, window, tag
+        self.E = inp.wl.E
+        self.pool = cf.ThreadPoolExecutor(max_workers=threads)
+        self.futs = {}
+        self.t0 = time.time()
+
+    def __len__(self):
+        return self.E
+
+    def __getitem__(self, e):
+        for f in range(e, min(self.E, e + self.window)):
+            if f not in self.futs:
+                self.futs[f] = self.pool.submit(expert_f64, self.inp, f)
+        for f in [f for f in self.futs if f < e]:
+            del self.futs[f]
+        out = self.futs.pop(e).result()
+        if self.E >= 64 and (e + 1) % 64 == 0:
+            log(f"  [{self.tag}] oracle through expert {e + 1}/{self.E} ({time.time() - self.t0:.1f}s)")
+        return out
+
+    def close(self):
+        self.pool.shutdown(wait=True, cancel_futures=True)
+        self.futs.clear()
+
+
+def check_valid_choice(w, sel, pick, own, slack=mo.NEAR_TIE):
+    """A near-tie token's GPU choice `pick` must be a top-k the selection rule could have made
+    had the scores moved by less than `slack`: k distinct experts in descending score order,
+    none below the oracle's k-th score by more than `slack`, and an allowed set of experts in
+    which no unpicked expert scores more than `slack` above the lowest pick.  Without groups
+    every expert is allowed.  Under the group limit the allowed set is topk_group groups: the
+    groups of the picks, every group whose score clearly beats the topk_group-th group score
+    (by more than `slack`), and, to fill up, groups within `slack` of that score; every group in
+    it must score at least the topk_group-th group score minus `slack`."""
+    pick = np.asarray(pick, np.int64)
+    assert len(set(pick.tolist())) == w.k, pick
+    assert np.all(np.diff(sel[pick]) <= slack), ("slots not in descending order", pick, sel[pick])
+    low = sel[pick].min()
+    assert low >= np.sort(sel[np.asarray(own, np.int64)])[0] - slack, ("pick below the oracle's k-th", pick)
+    if w.n_group == 1:
+        others = np.ones(w.E, bool)
+        others[pick] = False
+        assert not np.any(sel[others] > low + slack), ("a higher unpicked expert", pick)
+        return
+    gs = w.E // w.n_group
+    gsc = sel.reshape(w.n_group, gs).max(axis=1)
+    gth = np.sort(gsc)[::-1][w.topk_group - 1]              # the topk_group-th group score
+    must = set((pick // gs).tolist()) | set(np.nonzero(gsc > gth + slack)[0].tolist())
+    assert len(must) <= w.topk_group, ("more groups than allowed", pick)
+    assert all(gsc[g] >= gth - slack for g in must), ("pick outside the allowed groups", pick, gsc)
+    for g in must:                     # inside the allowed groups the picks are the top-k
+        members = np.arange(g * gs, (g + 1) * gs)
+        rest = members[~np.isin(members, pick)]
+        assert not np.any(sel[rest] > low + slack), ("a higher unpicked expert", pick, g)
+    fill = [g for g in range(w.n_group) if g not in must and gth - slack <= gsc[g] <= low + slack]
+    assert len(fill) >= w.topk_group - len(must), ("allowed groups cannot be completed", pick)
+
+
 def check_routing(w, inp, idx, gate, counts, f, P, aux):
     """Steps 1-2; returns (p, near-tie tokens, flipped tokens)."""
     x = f64(inp.x, w)
@@ -117,8 +182,7 @@ def check_routing(w, inp, idx, gate, counts, f, P, aux):
     flipped = [int(t) for t in nt if not np.array_equal(idx[t], own_idx[t])]
     for t in flipped:          # a near tie may go either way, but the choice must be a valid top-k
         sel = p[t] if w.scoring == "softmax" else p[t] + (0 if inp.b_r is None else inp.b_r)
-        kth = np.sort(sel[own_idx[t]])[0]
-        assert len(set(idx[t])) == w.k and np.all(sel[idx[t]] >= kth - 1e-6)
+        check_valid_choice(w, sel, idx[t], own_idx[t])
     g_ref = mo.gates(p, idx, w.renormalize)
     assert np.max(np.abs(gate - g_ref)) <= 1e-5, np.max(np.abs(gate - g_ref))
     c_ref, f_ref, P_ref, aux_ref = mo.load_balance_stats(p, idx, w.E)
@@ -139,8 +203,10 @@ def check_dispatch(w, idx, cap, kept, offsets, row_token, row_of):
     return d
 
 
-def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
-    """Forward on the GPU + every protocol check.  sample=None: all tokens' y checked."""
+def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False, assert_y=True):
+    """Forward on the GPU + every protocol check.  sample=None: all tokens' y checked (the oracle
+    runs over every expert, a window of experts in memory at a time).  assert_y=False leaves
+    the output bound to the caller (the measured error is returned)."""
     t0 = time.time()
     inp = wl.make_inputs(w, seed)
     dev = upload(inp)
@@ -168,10 +234,14 @@ def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
     x = f64(inp.x, w)
     sh = shared_f64(inp)
     if sample is None:
-        ex = experts_f64(inp, range(w.E))
-        ref = mo.moe_forward(x, f64(inp.w_r, w), [ex[e] for e in range(w.E)], w.k, cap, inp.b_r, w.renormalize,
-                             sh, idx=h["idx"], **router_kw(w))
+        ex = LazyExperts(inp, tag=w.name)
+        try:
+            ref = mo.moe_forward(x, f64(inp.w_r, w), ex, w.k, cap, inp.b_r, w.renormalize, sh, idx=h["idx"],
+                                 **router_kw(w))
+        finally:
+            ex.close()
         y_ref, y = ref.y, h["y"]
+        del ref
     else:
         toks = np.asarray(sample)
         kept_mask = disp.row_of[toks] >= 0
@@ -184,7 +254,8 @@ def run_forward(w: wl.Workload, seed=0, sample=None, repeat_check=False):
     dropped = int(disp.dropped.size)
     log(f"[{w.name}] T={w.T} d={w.d} d_e={w.d_e} E={w.E} k={w.k} cap={cap}: max|dy|/rms={err:.3e} "
         f"near_ties={len(nt)} flipped={len(flipped)} dropped={dropped} ({time.time() - t0:.1f}s)")
-    assert err <= TOL[w.dtype], err
+    if assert_y:
+        assert err <= TOL[w.dtype], err
     return dict(err=err, near_ties=len(nt), flipped=len(flipped), dropped=dropped, host=h)
 
 

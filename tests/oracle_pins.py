@@ -260,6 +260,53 @@ def pin_near_ties():
     assert list(mo.near_ties(p2, 1)) == [] and list(mo.near_ties(p2, 3)) == []
 
 
+def pin_near_ties_grouped():
+    """Near ties under the group limit, on hand-built selection scores.
+
+    Eight experts in four groups of two ({0,1}, {2,3}, {4,5}, {6,7}), two groups allowed.  A token
+    is reported when either decision rests on a gap below 1e-6: the topk_group-th against the
+    next group score, or the k-th against the next expert score among the allowed experts.
+    Gaps elsewhere (between allowed groups, inside excluded groups) must not report it.
+    """
+    e = 5e-7
+    k2 = np.array([
+        [0.9, 0.2, 0.5, 0.1, 0.5 + e, 0.3, 0.1, 0.0],    # 2nd vs 3rd group score: reported
+        [0.9, 0.7, 0.7 + e, 0.1, 0.2, 0.1, 0.0, 0.05],   # 2nd vs 3rd allowed expert: reported
+        [0.9, 0.1, 0.5, 0.3, 0.2, 0.1, 0.05, 0.0],       # no small gap
+        [0.9, 0.8, 0.5, 0.0, 0.5 - e, 0.0, 0.1, 0.0],    # 2nd vs 3rd group: reported (the experts agree)
+    ])
+    assert list(mo.near_ties_grouped(k2, 2, 4, 2)) == [0, 1, 3]
+    k3 = np.array([
+        [0.9, 0.3, 0.8, 0.1, 0.3 - e, 0.0, 0.0, 0.0],    # tie with an expert of an excluded group only
+        [0.9, 0.5, 0.9 - e, 0.0, 0.2, 0.0, 0.1, 0.0],    # 1st vs 2nd (both allowed): not a decision
+        [0.9, 0.8, 0.7, 0.6, 0.5, 0.4, 0.3, 0.2],        # no small gap
+        [0.9, 0.85, 0.6, 0.55, 0.6 + e, 0.0, 0.1, 0.0],  # 2nd vs 3rd group score: reported
+    ])
+    assert list(mo.near_ties_grouped(k3, 3, 4, 2)) == [3]
+    # every group allowed: only the expert decision counts (row 3's group gap no longer decides)
+    assert list(mo.near_ties_grouped(k2[3:4], 2, 4, 4)) == []
+    assert list(mo.near_ties_grouped(k2[1:2], 2, 4, 4)) == [0]
+    # one group: the plain near-tie rule
+    g = _rng(41)
+    sc = g.random((200, 8))
+    sc[::3, 5] = sc[::3, 2] + 3e-7
+    for k in (1, 2, 3):
+        assert np.array_equal(mo.near_ties_grouped(sc, k, 1, 1), mo.near_ties(sc, k))
+    # tokens not reported keep their chosen set under any perturbation that moves each
+    # score by less than a quarter of the threshold
+    sc = g.random((400, 12)) * 1e-5                     # many gaps near the threshold
+    for k, ng, tg in ((2, 4, 2), (3, 3, 1), (4, 6, 3)):
+        nt = set(mo.near_ties_grouped(sc, k, ng, tg).tolist())
+        assert 0 < len(nt) < sc.shape[0]
+        base = mo.group_limited_top_k(sc, k, ng, tg)
+        for trial in range(20):
+            pert = sc + (g.random(sc.shape) - 0.5) * 0.5e-6
+            moved = mo.group_limited_top_k(pert, k, ng, tg)
+            for t in range(sc.shape[0]):
+                if t not in nt:
+                    assert set(base[t]) == set(moved[t]), (k, ng, tg, t)
+
+
 def pin_dispatch_invariants():
     g = _rng(6)
     for (T, E, k, cap) in [(50, 5, 2, -1), (50, 5, 2, 7), (33, 4, 3, 0), (64, 8, 1, 5), (0, 3, 2, 4)]:

@@ -63,6 +63,37 @@ def test_shape_validation(kw, status):
     assert _lib.lib().moe_workspace_bytes(C.byref(_shape(**kw)), C.byref(n)) == status
 
 
+@pytest.mark.parametrize("dtype,elem", [(moe.MOE_BF16, 2), (moe.MOE_F32, 4)])
+def test_gather_offset_boundary(dtype, elem):
+    """The forward gathers token rows of x with 32-bit byte offsets from one buffer base, so
+    T*d*elem must stay below 2^32: the largest accepted T has every row's last 16-byte piece
+    below 2^32, and one more token is rejected before any device work."""
+    d = 8192
+    t_max = (1 << 32) // (d * elem) - 1
+    last_piece = (t_max - 1) * d * elem + d * elem - 16
+    assert last_piece + 16 <= (1 << 32) - 1 and last_piece >= 1 << 31    # past the old 2 GiB range
+    n = C.c_size_t()
+    ok = _shape(T=t_max, d=d, d_e=128, E=4, k=1, dtype=dtype)
+    assert _lib.lib().moe_workspace_bytes(C.byref(ok), C.byref(n)) == 0
+    bad = _shape(T=t_max + 1, d=d, d_e=128, E=4, k=1, dtype=dtype)
+    assert _lib.lib().moe_workspace_bytes(C.byref(bad), C.byref(n)) == 3
+
+
+def test_buffer_resources_cover_32bit_offsets():
+    """Every buffer resource the kernels build spans the whole 32-bit offset range (a narrower
+    range would read offsets past it as zeros)."""
+    import glob
+    import re
+    src = os.path.join(os.path.dirname(__file__), "..", "sparse_mixture_experts_17_amd", "csrc")
+    calls = []
+    for f in glob.glob(os.path.join(src, "*.h")) + glob.glob(os.path.join(src, "*.hip")):
+        text = open(f).read()
+        calls += re.findall(r"make_buffer_rsrc\(([^;]*?)\)\s*[;:]", text)
+    assert calls
+    for c in calls:
+        assert re.search(r",\s*0\s*,\s*kBufRange\s*,\s*kBufFlags$", c.strip()), c
+
+
 @pytest.mark.parametrize("kw", [dict(scoring=1), dict(n_group=4, topk_group=2), dict(E=256, k=8, n_group=64,
                                                                                        topk_group=2, scoring=1)])
 def test_shape_validation_accepts_router_variants(kw):

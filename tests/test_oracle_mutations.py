@@ -13,7 +13,7 @@ from oracle import moe_oracle as mo
 
 _orig = {name: getattr(mo, name) for name in
          ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
-          "capacity", "dispatch", "near_ties", "sigmoid", "group_limited_top_k", "route", "e4m3_decode",
+          "capacity", "dispatch", "near_ties", "near_ties_grouped", "sigmoid", "group_limited_top_k", "route", "e4m3_decode",
           "dequantize_rows", "e2m1_decode", "e8m0_decode", "dequantize_mx_rows", "silu_grad",
           "swiglu_backward", "router_backward", "moe_backward"]}
 
@@ -279,6 +279,50 @@ def _bwd_sigmoid_bias_grad(x, w_r, experts, k, dy, *a, **kw):
     return G
 
 
+def _ntg_excuse_all(score, k, n_group, topk_group, threshold=mo.NEAR_TIE):
+    return np.arange(score.shape[0])
+
+
+def _ntg_report_none(score, k, n_group, topk_group, threshold=mo.NEAR_TIE):
+    return np.zeros(0, dtype=np.int64)
+
+
+def _ntg_mask_ignored(score, k, n_group, topk_group, threshold=mo.NEAR_TIE):
+    """Expert decision taken over every expert instead of the allowed ones."""
+    grp = _orig["near_ties_grouped"](score, k, n_group, topk_group, threshold)
+    out = set(grp.tolist())
+    g_only = _orig["near_ties_grouped"](score, k, n_group, n_group, threshold)   # expert gaps, all allowed
+    out -= set(g_only.tolist())
+    out |= set(mo.near_ties(score, k, threshold).tolist())
+    gs = score.shape[1] // n_group
+    if topk_group < n_group:
+        gsc = -np.sort(-score.reshape(score.shape[0], n_group, gs).max(axis=2), axis=1)
+        out |= set(np.nonzero(gsc[:, topk_group - 1] - gsc[:, topk_group] < threshold)[0].tolist())
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def _ntg_group_off_by_one(score, k, n_group, topk_group, threshold=mo.NEAR_TIE):
+    """Group decision read between the (topk_group-1)-th and topk_group-th group scores."""
+    T, E = score.shape
+    gs = E // n_group
+    out = set(_orig["near_ties_grouped"](score, k, n_group, n_group, threshold).tolist())
+    if topk_group > 1:
+        gsc = -np.sort(-score.reshape(T, n_group, gs).max(axis=2), axis=1)
+        out |= set(np.nonzero(gsc[:, topk_group - 2] - gsc[:, topk_group - 1] < threshold)[0].tolist())
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def _ntg_no_group_decision(score, k, n_group, topk_group, threshold=mo.NEAR_TIE):
+    """Only the expert decision among the allowed experts is checked."""
+    T, E = score.shape
+    gs = E // n_group
+    allowed_sel = mo.group_limited_top_k(score, min(E, topk_group * gs), n_group, topk_group)
+    masked = np.full_like(score, -np.inf)
+    np.put_along_axis(masked, allowed_sel.astype(np.int64), np.take_along_axis(score, allowed_sel.astype(np.int64),
+                                                                                 axis=1), axis=1)
+    return mo.near_ties(masked, k, threshold) if k < topk_group * gs else np.zeros(0, dtype=np.int64)
+
+
 MUTANTS = [
     ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
     ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
@@ -290,6 +334,9 @@ MUTANTS = [
     ("capacity", _capacity_no_k), ("capacity", _capacity_ceil),
     ("dispatch", _dispatch_keep_last), ("dispatch", _dispatch_no_cap),
     ("near_ties", _near_ties_off_by_one),
+    ("near_ties_grouped", _ntg_excuse_all), ("near_ties_grouped", _ntg_report_none),
+    ("near_ties_grouped", _ntg_mask_ignored), ("near_ties_grouped", _ntg_group_off_by_one),
+    ("near_ties_grouped", _ntg_no_group_decision),
     ("sigmoid", _sigmoid_sign), ("group_limited_top_k", _group_score_sum),
     ("group_limited_top_k", _group_ignored), ("group_limited_top_k", _group_interleaved),
     ("route", _route_bias_in_gates),
