@@ -230,6 +230,31 @@ moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_r, c
                        int32_t *offsets, int32_t *row_token, int32_t *row_of,
                        void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
 
+/* moe_forward for callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc.  The same layer, the same
+ * kernels and bit-identical outputs as moe_forward; instead of a caller workspace it uses a
+ * scratch array of MOE_STATIC_SCRATCH_BYTES (64 MiB) compiled into the library, one per GPU,
+ * held by each GPU the library runs on until the process ends.  It allocates nothing (no
+ * hipMalloc, hipFree or allocating library call); the device address of the current device's
+ * scratch is looked up (hipGetSymbolAddress) on that device's first call.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (two streams,
+ * two host threads, or a call enqueued while another is still running) race and give wrong
+ * results.  Calls ordered on one stream are safe.  No part of the scratch needs clearing
+ * between calls (every byte a call reads is written earlier in the same call).
+ * Errors: as moe_forward, checked on the host before any HIP call; a shape whose workspace
+ * (moe_workspace_bytes) exceeds MOE_STATIC_SCRATCH_BYTES -> MOE_ERR_WORKSPACE (e.g. more than
+ * about 600 tokens at the Mixtral 8x7B layer shape, or 160 at the DeepSeek-V3 shape with its
+ * shared expert); more than 64 GPUs, or a failed lookup -> MOE_ERR_HIP. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_shape *shape, const void *x, const void *w_r, const float *b_r,
+                               const void *w_gate, const void *w_up, const void *w_down,
+                               const void *ws_gate, const void *ws_up, const void *ws_down,
+                               const moe_wscales *scales, const moe_wscales *shared_scales,
+                               float *y, int32_t *idx, float *gate, int32_t *counts, int32_t *kept,
+                               float *f, float *P, float *aux,
+                               int32_t *offsets, int32_t *row_token, int32_t *row_of,
+                               void *stream, void *const *stage_events);
+
 /* ---------------------------------------------------------------- backward pass */
 
 /* Workspace bytes needed by moe_backward for this shape (validates it; native weights only). */

@@ -15,6 +15,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_W_NATIVE, MOE_W_FP8_E4M3, MOE_W_MXFP4 = 0, 1, 2
 MOE_NUM_STAGES = 8
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 STAGE_NAMES = ["router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
 MOE_NUM_BSTAGES = 9
 BSTAGE_NAMES = ["prep", "recompute", "down_bwd", "router_bwd", "dx_expert", "wgrad_down", "wgrad_gate_up",
@@ -48,6 +49,8 @@ SIGNATURES = {
     "moe_combine": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P]),
     "moe_forward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 9 + [C.POINTER(MoeWScales)] * 2 + [_P] * 11
                     + [_P, C.c_size_t, _P, _P]),
+    "moe_forward_noalloc": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 9 + [C.POINTER(MoeWScales)] * 2 + [_P] * 11
+                            + [_P, _P]),
     "moe_backward_workspace_bytes": (C.c_int, [C.POINTER(MoeShape), C.POINTER(C.c_size_t)]),
     "moe_backward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 16 + [C.c_float] + [_P] * 10
                      + [_P, C.c_size_t, _P, _P]),

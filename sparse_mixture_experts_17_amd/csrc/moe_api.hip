@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
 #include "moe.h"
@@ -203,6 +204,47 @@ moe_status run_ffn(const moe_shape& s, int G, const void* A, const int32_t* offs
   return MOE_OK;
 }
 
+// Host checks of moe_forward's arguments other than the workspace (shape, then pointers).
+moe_status forward_args(const moe_shape* shape, const void* x, const void* w_r, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* ws_gate, const void* ws_up, const void* ws_down,
+                        const moe_wscales* scales, const moe_wscales* shared_scales, const float* y,
+                        const int32_t* idx, const float* gate, const int32_t* counts, const int32_t* kept,
+                        const float* f, const float* P, const float* aux) {
+  moe_status v = check_shape(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if ((s.T > 0 && (!x || !w_r || !w_gate || !w_up || !w_down || !y || !idx || !gate)) || !counts || !kept || !f ||
+      !P || !aux)
+    return MOE_ERR_NULL;
+  if (s.d_e_shared > 0 && s.T > 0 && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_NULL;
+  if (s.T > 0 && (!scales_ok(s, scales) || (s.d_e_shared > 0 && !scales_ok(s, shared_scales)))) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+// Scratch of moe_forward_noalloc: one copy per GPU (the code object's device memory), held
+// until the process ends.  In host code `scratch` names a host-side stand-in, not the device
+// memory: the device address comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the device's first call).
+moe_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,14 +351,11 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
                        int32_t* idx, float* gate, int32_t* counts, int32_t* kept,
                        float* f, float* P, float* aux, int32_t* offsets, int32_t* row_token, int32_t* row_of,
                        void* ws, size_t ws_bytes, void* stream, void* const* stage_events) {
-  moe_status v = check_shape(shape);
+  moe_status v = forward_args(shape, x, w_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, scales, shared_scales, y,
+                              idx, gate, counts, kept, f, P, aux);
   if (v != MOE_OK) return v;
+  if (!ws) return MOE_ERR_NULL;
   const moe_shape& s = *shape;
-  if ((s.T > 0 && (!x || !w_r || !w_gate || !w_up || !w_down || !y || !idx || !gate)) || !counts || !kept || !f ||
-      !P || !aux || !ws)
-    return MOE_ERR_NULL;
-  if (s.d_e_shared > 0 && s.T > 0 && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_NULL;
-  if (s.T > 0 && (!scales_ok(s, scales) || (s.d_e_shared > 0 && !scales_ok(s, shared_scales)))) return MOE_ERR_NULL;
   const bool w8 = s.wfmt != MOE_W_NATIVE;
   const moe_wscales& sc = w8 && s.T > 0 ? *scales : kNoScales;
   const moe_wscales& ssc = w8 && s.T > 0 && s.d_e_shared > 0 ? *shared_scales : kNoScales;
@@ -411,6 +450,26 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   MOE_MARK(MOE_NUM_STAGES);
 #undef MOE_MARK
   return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const void* w_r, const float* b_r,
+                               const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                               const void* ws_up, const void* ws_down, const moe_wscales* scales,
+                               const moe_wscales* shared_scales, float* y, int32_t* idx, float* gate, int32_t* counts,
+                               int32_t* kept, float* f, float* P, float* aux, int32_t* offsets, int32_t* row_token,
+                               int32_t* row_of, void* stream, void* const* stage_events) {
+  moe_status v = forward_args(shape, x, w_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, scales, shared_scales, y,
+                              idx, gate, counts, kept, f, P, aux);
+  if (v != MOE_OK) return v;
+  if (layout(*shape).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  v = static_scratch(&ws);
+  if (v != MOE_OK) return v;
+  // Every workspace byte the layer reads is written earlier in the same call, so the scratch
+  // needs no clearing between calls.
+  return moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, scales, shared_scales, y, idx,
+                     gate, counts, kept, f, P, aux, offsets, row_token, row_of, ws, (size_t)MOE_STATIC_SCRATCH_BYTES,
+                     stream, stage_events);
 }
 
 moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes) {

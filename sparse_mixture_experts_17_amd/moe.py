@@ -112,6 +112,18 @@ def moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_dow
         stage_events))
 
 
+def moe_forward_noalloc(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, scales, shared_scales, y,
+                        idx, gate, counts, kept, f, P, aux, offsets, row_token, row_of, stream=None,
+                        stage_events=None) -> None:
+    """moe_forward without a workspace: the library's static per-GPU scratch is used (calls that
+    overlap on one GPU race)."""
+    check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        C.byref(shape), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
+        _ptr(ws_up), _ptr(ws_down), _scales(scales), _scales(shared_scales), _ptr(y), _ptr(idx), _ptr(gate),
+        _ptr(counts), _ptr(kept), _ptr(f), _ptr(P),
+        _ptr(aux), _ptr(offsets), _ptr(row_token), _ptr(row_of), _stream(stream), stage_events))
+
+
 # ------------------------------------------------------------------ convenience
 
 @dataclass

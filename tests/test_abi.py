@@ -21,7 +21,8 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
     assert names == sorted(["moe_capacity", "moe_workspace_bytes", "moe_status_str", "moe_route", "moe_permute",
-                            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_backward_workspace_bytes",
+                            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
+                            "moe_backward_workspace_bytes",
                             "moe_backward"])
     lib = _lib.lib()
     for n in names:
@@ -220,6 +221,24 @@ def _bwd(lib, s, a, ws_bytes, d_aux=0.0):
     """moe_backward with pointers a = x w_r b_r w_gate w_up w_down ws_gate ws_up ws_down idx gate counts
     offsets row_token row_of dy | dx dw_r db_r dw_gate dw_up dw_down dws_gate dws_up dws_down dgate ws."""
     return lib.moe_backward(C.byref(s), *a[:16], C.c_float(d_aux), *a[16:26], a[26], ws_bytes, None, None)
+
+
+def test_noalloc_forward_host_checks():
+    """moe_forward_noalloc rejects, before any HIP call, a shape whose workspace exceeds the
+    static scratch (MOE_ERR_WORKSPACE) and missing pointers (MOE_ERR_NULL)."""
+    lib = _lib.lib()
+    big = _shape(T=4096, d=4096, d_e=14336, E=8, k=2, dtype=moe.MOE_BF16)
+    assert moe.moe_workspace_bytes(big) > moe.MOE_STATIC_SCRATCH_BYTES
+    p = C.c_void_p(64)                                      # never dereferenced: rejected first
+    ptrs = [p] * 6 + [None] * 3
+    outs = [p] * 8
+    assert lib.moe_forward_noalloc(C.byref(big), *ptrs, None, None, *outs, None, None, None, None, None) == 4
+    small = _shape(T=16, d=512, d_e=1024, E=8, k=2, dtype=moe.MOE_BF16)
+    assert moe.moe_workspace_bytes(small) <= moe.MOE_STATIC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(C.byref(small), *ptrs, None, None, None, *outs[1:], None, None, None, None,
+                                   None) == 1
+    bad = _shape(k=0)
+    assert lib.moe_forward_noalloc(C.byref(bad), *ptrs, None, None, *outs, None, None, None, None, None) == 2
 
 
 def test_backward_rejects_null_small_workspace_and_quantised_weights():
