@@ -9,7 +9,11 @@ weights) rides along as "secondary" (also timed as replays of the call captured 
 graph: ms_per_step_graph), the split ABI's moe_permute (the gather of token
 rows into expert order) on the prefill routing as "secondary_permute", the backward pass
 of the prefill call as "secondary_backward", and decode with FP8 and MXFP4 expert weights
-as "secondary_fp8" and "secondary_mxfp4".
+as "secondary_fp8" and "secondary_mxfp4", and the two HBM-bound prefill-sized workloads -- the
+Switch top-1 layer with capacity factor 1.25 and the DeepSeek-V3-shaped layer with 256 routed
+experts and a shared expert -- as "secondary_switch" and "secondary_deepseek".  Every line
+carries routing health (dropped fraction, MaxVio, per-expert counts; with the CPU baseline, the
+oracle's near-tie tokens and how many the GPU routed differently).
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize(); per-stage durations come from HIP events that the library
@@ -287,6 +291,68 @@ def layer_work(w, R_kept, touched):
                 bytes_layer=bytes_layer)
 
 
+def health(info):
+    """Routing health of a call, from the GPU's own outputs: the dropped fraction of assignments
+    (kevinluzbetak.com capacity worked example: the per-layer health check), MaxVio = (busiest
+    expert's load - mean load) / mean load over the assignments before capacity
+    (jacopoparretti.dev, "A bias"), per-expert counts, and the touched experts."""
+    w, out = info["w"], info["out"]
+    counts = out.counts.cpu().numpy().astype(int)
+    kept = out.kept.cpu().numpy().astype(int)
+    R = w.T * w.k
+    mean = R / w.E
+    return {"dropped_fraction": (R - int(kept.sum())) / R if R else 0.0,
+            "dropped_assignments": R - int(kept.sum()),
+            "maxvio": (int(counts.max()) - mean) / mean if R else 0.0,
+            "experts_touched": int((kept > 0).sum()), "aux": float(out.aux.cpu()[0]),
+            "counts": counts.tolist()}
+
+
+def stage_rates(info):
+    """Achieved GB/s of the HBM-bound small stages from their algorithmic bytes (router: x, W_r,
+    indices and gates; combine: kept expert rows in fp32 + y, + the shared expert's output)."""
+    w, st = info["w"], info["stages"]
+    s = 2 if w.dtype == "bf16" else 4
+    R = info["R_kept"]
+    rb = w.T * w.d * s + w.E * w.d * s + w.T * w.k * 8
+    cb = R * w.d * 4 + w.T * w.d * 4 + (w.T * w.d * 4 if w.d_e_shared else 0)
+    out = {}
+    for name, b in (("router", rb), ("combine", cb)):
+        ms = st[name]
+        out[name] = {"ms": ms, "algorithmic_bytes": b, "gbs": b / (ms / 1e3) / 1e9 if ms > 0 else None,
+                     "frac_hbm": b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS if ms > 0 else None}
+    return out
+
+
+def streaming_line(info, kernel_name):
+    """JSON object of an HBM-bound prefill-sized workload (Switch capacity, DeepSeek-V3 shape):
+    tokens/s, stage times, the dominant kernel's HBM roofline and the layer's fractions."""
+    w = info["w"]
+    ms = info["total_ms"] / info["steps"]
+    work = layer_work(w, info["R_kept"], info["touched"])
+    gu_ms = info["kernel_ms"]
+    gb = work["bytes_gate_up"] / (gu_ms / 1e3) / 1e9
+    st = info["stages"]
+    dn = st["down"]
+    return {
+        "workload": w.name, "value": w.T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+        "config": {"T": w.T, "d": w.d, "d_e": w.d_e, "E": w.E, "k": w.k, "capacity": info["cap"],
+                   "d_e_shared": w.d_e_shared},
+        "stages_ms": st, "ms_per_step_unmarked": info["plain_ms"],
+        "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": gb, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gb / PEAK_HBM_GBS, "traffic": measured_traffic(w.name, "gate_up"), "avg_ms": gu_ms,
+                     "algorithmic": "gate+up weights of touched experts + gathered x rows + h rows"},
+        "down": {"gbs": work["bytes_down"] / (dn / 1e3) / 1e9, "frac_hbm": work["bytes_down"] / (dn / 1e3) / 1e9
+                 / PEAK_HBM_GBS, "traffic": measured_traffic(w.name, "down")},
+        "layer": {"algorithmic_bytes": work["bytes_layer"], "flops": work["flops_layer"],
+                  "frac_hbm": work["bytes_layer"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                  "frac_mfma": work["flops_layer"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "hbm_roofline_ms": work["bytes_layer"] / (PEAK_HBM_GBS * 1e9) * 1e3},
+        "stage_rates": stage_rates(info),
+        "health": health(info),
+    }
+
+
 def secondary_line(dec, fmt):
     """JSON object of a decode run with quantised expert weights."""
     wd = dec["w"]
@@ -302,6 +368,7 @@ def secondary_line(dec, fmt):
                      "achieved": gb, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
                      "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
         "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "health": health(dec),
     }
 
 
@@ -372,6 +439,21 @@ def run_backward(info, steps, warmup, kernel_stage="dx_expert"):
                      "avg_ms": kernel_ms,
                      "algorithmic": f"4*d*d_e FLOPs per kept row x {R} rows"},
     }
+
+
+def oracle_routing_check(info, idx):
+    """CPU-baseline leg: the oracle's routing of the same tokens against the GPU's idx -- the
+    near-tie tokens (k-th and (k+1)-th scores within 1e-6) and how many of them the GPU routed
+    differently; every other token must match exactly."""
+    import numpy as np
+    import workloads as wl
+    from oracle import moe_oracle as mo
+    w, inp = info["w"], info["inp"]
+    _, _, own, _, nt = mo.route(wl.as_f64(inp.x, w.dtype), wl.as_f64(inp.w_r, w.dtype), w.k, inp.b_r,
+                                w.renormalize, scoring=w.scoring, n_group=w.n_group, topk_group=w.topk_group)
+    differ = np.nonzero((own != idx).any(axis=1))[0]
+    return {"near_ties": int(len(nt)), "flipped": int(np.isin(differ, nt).sum()),
+            "other_mismatches": int((~np.isin(differ, nt)).sum())}
 
 
 def cpu_baseline(info, target_s):
@@ -463,6 +545,8 @@ def main():
         "layer": layer,
         "stages_ms": st,
         "ms_per_step_unmarked": info["plain_ms"],
+        "stage_rates": stage_rates(info),
+        "health": health(info),
     }
     if not a.no_secondary and w.name == "mixtral_prefill":
         print("[bench] secondary: mixtral_decode on the same weights", file=sys.stderr, flush=True)
@@ -479,6 +563,7 @@ def main():
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gb / PEAK_HBM_GBS,
                          "traffic": measured_traffic(wd.name, "gate_up"), "avg_ms": dec["kernel_ms"]},
             "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "health": health(dec),
         }
     if not a.no_secondary and w.name == "mixtral_prefill":
         print("[bench] secondary: moe_permute (split ABI) on the same routing", file=sys.stderr, flush=True)
@@ -499,9 +584,22 @@ def main():
         torch.cuda.empty_cache()
         dec = run_gpu("mixtral_decode_mxfp4", max(a.steps, 20), a.warmup, graph=True)
         line["secondary_mxfp4"] = secondary_line(dec, "MXFP4")
+    routed = [(line, info, info["out"].idx.cpu().numpy())]
+    if not a.no_secondary and w.name == "mixtral_prefill":
+        for key, name, kern in (("secondary_switch", "switch_capacity", "grouped_gemm gate_up (stream tiles)"),
+                                ("secondary_deepseek", "deepseek_v3",
+                                 "grouped_gemm gate_up (stream tiles, 256 routed experts)")):
+            print(f"[bench] secondary: {name}", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+            sec = run_gpu(name, max(a.steps, 10), a.warmup)
+            line[key] = streaming_line(sec, kern)
+            routed.append((line[key], {"w": sec["w"], "inp": sec["inp"]}, sec["out"].idx.cpu().numpy()))
+            del sec
     if not a.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(info, a.cpu_seconds)
+        for obj, inf, idx in routed:
+            obj.setdefault("health", {})["oracle_routing"] = oracle_routing_check(inf, idx)
     print(json.dumps(line))
 
 
