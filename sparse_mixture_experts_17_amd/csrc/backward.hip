@@ -69,8 +69,7 @@ template <> struct Elem4<uint16_t> {
     f[2] = bf16_bits_to_f32(v.y & 0xffffu); f[3] = bf16_bits_to_f32(v.y >> 16);
   }
   __device__ static V from_f32(const float* f) {
-    return V{f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16),
-             f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16)};
+    return V{f32x2_to_bf16x2_bits(f[0], f[1]), f32x2_to_bf16x2_bits(f[2], f[3])};
   }
 };
 template <> struct Elem4<float> {

@@ -19,13 +19,29 @@ constexpr int kNumXcd = 8;     // MI355X: 8 accelerator complex dies, one L2 eac
 // bf16 is stored as raw 16-bit patterns (uint16_t); fp32 as float.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even (gfx950's v_cvt_pk_bf16_f32); NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
+
+// Two floats rounded to bf16 (nearest even) in one instruction: lo in bits 0-15, hi in 16-31.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{lo, hi}), b2_t));
+}
+
+// sigmoid(a) = 1 / (1 + e^-a) from the hardware's exp2 and reciprocal (about 1 ulp each; the
+// products round their results to bf16 or keep fp32 partials, so this is far below the
+// rounding that follows).
+__device__ __forceinline__ float sigmoid_fast(float a) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+}
+
+// h = SiLU(a) * b = a * b * sigmoid(a).  Every kernel that forms h (the forward's gate/up
+// epilogue and the backward's recompute and down-product epilogues) calls this one function,
+// so they all round the same h.
+__device__ __forceinline__ float silu_mul(float a, float b) { return (a * b) * sigmoid_fast(a); }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.  Used where an
 // accumulator array is indexed inside a loop body too large for the unroller: a loop left

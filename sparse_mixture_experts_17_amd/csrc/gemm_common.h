@@ -126,49 +126,46 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& args, int L, int
 }
 
 // Epilogue: lane holds rows 4*(lane/16)+q of each 16x16 tile, column lane%16.  The gated
-// product stores SiLU(a) * b in the activation type, the plain one fp32.
+// product stores SiLU(a) * b in the activation type, the plain one fp32.  Row addresses are
+// formed once per (subtile row, q); the row test is per row, not per element.
 template <typename Cfg, typename Acc>
 __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0, const Acc& acc1, int wm, int wn,
                                            int lane, int g, int nt, int row0, int rows, size_t c_off = 0) {
   using T = typename Cfg::Elem;
   const int N = args.N;
+  const int c0 = nt * Cfg::BN_ + wn * Cfg::WTN + (lane & 15);
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j)
+    for (int q = 0; q < 4; ++q) {
+      const int r = wm * Cfg::WTM + i * 16 + (lane >> 4) * 4 + q;
+      if (r >= rows) continue;
+      const size_t o = (size_t)(row0 + r) * N + c0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = wm * Cfg::WTM + i * 16 + (lane >> 4) * 4 + q;
-        const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
-        if (r < rows) {
-          const size_t o = (size_t)(row0 + r) * N + col;
-          if constexpr (Cfg::WF_ == 1) {                   // row scales of FP8 weights
-            const size_t sc = (size_t)g * N + col;
-            if constexpr (Cfg::NB == 2) {
-              const float a = acc0[i][j][q] * args.S0[sc], b = acc1[i][j][q] * args.S1[sc];
-              const float h = __fdividef(a, 1.f + __expf(-a)) * b;
-              ((T*)args.C)[o] = ElemOut<T>::from_f32(h);
-            } else {
-              ((float*)args.C)[c_off + o] = acc0[i][j][q] * args.S0[sc];
-            }
-          } else if constexpr (Cfg::NB == 2) {
-            const float a = acc0[i][j][q], b = acc1[i][j][q];
-            const float h = __fdividef(a, 1.f + __expf(-a)) * b;   // SiLU(a) * b (fast exp/divide: the
-                                                                    // result is rounded to bf16)
-            ((T*)args.C)[o] = ElemOut<T>::from_f32(h);
+      for (int j = 0; j < Cfg::TN; ++j) {
+        const int col = c0 + j * 16;
+        if constexpr (Cfg::WF_ == 1) {                   // row scales of FP8 weights
+          const size_t sc = (size_t)g * N + col;
+          if constexpr (Cfg::NB == 2) {
+            const float h = silu_mul(acc0[i][j][q] * args.S0[sc], acc1[i][j][q] * args.S1[sc]);
+            ((T*)args.C)[o + j * 16] = ElemOut<T>::from_f32(h);
           } else {
-            ((float*)args.C)[c_off + o] = acc0[i][j][q];
+            ((float*)args.C)[c_off + o + j * 16] = acc0[i][j][q] * args.S0[sc];
           }
+        } else if constexpr (Cfg::NB == 2) {
+          ((T*)args.C)[o + j * 16] = ElemOut<T>::from_f32(silu_mul(acc0[i][j][q], acc1[i][j][q]));
+        } else {
+          ((float*)args.C)[c_off + o + j * 16] = acc0[i][j][q];
         }
       }
+    }
 }
 
 // Four consecutive values of T as one 8-byte (bf16) or 16-byte (fp32) store.
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float* v) {
   if constexpr (sizeof(T) == 2) {
-    *(uint2*)p = uint2{(uint32_t)ElemOut<T>::from_f32(v[0]) | ((uint32_t)ElemOut<T>::from_f32(v[1]) << 16),
-                       (uint32_t)ElemOut<T>::from_f32(v[2]) | ((uint32_t)ElemOut<T>::from_f32(v[3]) << 16)};
+    *(uint2*)p = uint2{f32x2_to_bf16x2_bits(v[0], v[1]), f32x2_to_bf16x2_bits(v[2], v[3])};
   } else {
     *(float4*)p = float4{v[0], v[1], v[2], v[3]};
   }
@@ -203,7 +200,7 @@ __device__ __forceinline__ void store_save_ab(const GemmArgs& args, const Acc& a
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float a = acc0[i][j][q], b = acc1[i][j][q];
-        h[q] = __fdividef(a, 1.f + __expf(-a)) * b;
+        h[q] = silu_mul(a, b);
         if (rl + q < rows) {
           const size_t o = (size_t)(row0 + rl + q) * N + col;
           args.ep_a[o] = a;
@@ -253,10 +250,10 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
             const int row = row0 + rl + q;
             const size_t o = (size_t)row * N + col;
             const float a = args.ep_a[o], b = args.ep_b[o], u = acc0[i][j][q];
-            const float silu = __fdividef(a, 1.f + __expf(-a));
-            const float h = ElemOut<T>::to_f32(ElemOut<T>::from_f32(silu * b));
+            const float sg = sigmoid_fast(a);
+            const float silu = a * sg;
+            const float h = ElemOut<T>::to_f32(ElemOut<T>::from_f32(silu_mul(a, b)));
             part[q] = fmaf(h, u, part[q]);
-            const float sg = __fdividef(1.f, 1.f + __expf(-a));
             const float dh = gr[q] * u;
             da[q] = dh * b * sg * (1.f + a * (1.f - sg));
             db[q] = dh * silu;
