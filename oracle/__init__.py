@@ -11,7 +11,8 @@ stored element type, so the oracle sees the same values the GPU receives.
 Modules
   moe_oracle   the layer: router, softmax, top-k, gates, aux statistics,
                capacity dispatch, SwiGLU experts, combine, near-tie report,
-               the FP8 (E4M3) and MXFP4 weight decodes, and the backward pass
+               the FP8 (E4M3) and MXFP4 weight decodes, the E4M3 encoder and
+               MXFP8 rounding of activations, and the backward pass
                (gradients with the routing held fixed)
   bruteforce   pure-Python evaluation of the dense "every expert, unchosen
                gates zero" form, for tiny inputs

@@ -6,13 +6,61 @@ It evaluates the dense form that Zero to Frontier §13.1 uses to check its
 worked example ("A worked example small enough to check by hand"): run every
 expert on every token and multiply the unchosen ones by a zero gate.  It is an
 independent second implementation of the same definition: nested loops over
-Python floats, ``math.exp``, a selection loop for the top-k, and a per-expert
-arrival counter for the capacity rule, so a NumPy slip in the main oracle (a
-transposed operand, a wrong axis, a dropped term) cannot repeat here.
+Python floats, ``math.exp``, a selection loop for the top-k, a per-expert
+arrival counter for the capacity rule, and a table search for the E4M3 rounding
+of MXFP8 activations, so a NumPy slip in the main oracle (a transposed operand, a
+wrong axis, a dropped term, a wrong rounding rule) cannot repeat here.
 """
 from __future__ import annotations
 
 import math
+import struct
+
+
+def _f32(v):
+    """v rounded to the nearest float32 (struct's pack does the rounding)."""
+    return struct.unpack("f", struct.pack("f", v))[0]
+
+
+def _e4m3_table():
+    """(value, code) of every non-negative finite E4M3 code, built from the bit fields."""
+    out = []
+    for ex in range(16):
+        for man in range(8):
+            if ex == 15 and man == 7:
+                continue                                   # NaN
+            val = (man / 8.0) * 2.0 ** -6 if ex == 0 else (1.0 + man / 8.0) * 2.0 ** (ex - 7)
+            out.append((val, (ex << 3) | man))
+    return out
+
+
+_E4M3 = _e4m3_table()
+
+
+def _round_e4m3(w):
+    """Nearest E4M3 value by search over the table, ties to the even code, saturating."""
+    a = min(abs(w), 448.0)
+    best = None
+    for val, code in _E4M3:
+        key = (abs(val - a), code & 1)
+        if best is None or key < best[0]:
+            best = (key, val)
+    return math.copysign(best[1], w)
+
+
+def _mxfp8_row(row):
+    """A row rounded to MXFP8: blocks of 32 share 2^X, X = floor(log2 block max) - 8."""
+    out = []
+    for b0 in range(0, len(row), 32):
+        blk = row[b0:b0 + 32]
+        amax = max(abs(v) for v in blk)
+        if amax == 0.0:
+            x = -127
+        else:
+            x = max(-127, min(127, math.frexp(amax)[1] - 1 - 8))
+        sc = 2.0 ** x
+        out.extend(_round_e4m3(v / sc) * sc for v in blk)
+    return out
 
 
 def _matvec(W, v):
@@ -24,10 +72,12 @@ def _silu(z):
     return z / (1.0 + math.exp(-z)) if z > -700 else 0.0
 
 
-def _expert(Wg, Wu, Wd, x):
+def _expert(Wg, Wu, Wd, x, act=None):
     a = _matvec(Wg, x)
     b = _matvec(Wu, x)
     h = [_silu(a[n]) * b[n] for n in range(len(a))]
+    if act == "mxfp8":                                     # h enters the down product as MXFP8
+        h = _mxfp8_row([_f32(v) for v in h])
     return _matvec(Wd, h)
 
 
@@ -46,14 +96,15 @@ def _select(score, k, allowed):
 
 
 def moe_dense_bruteforce(x, w_r, experts, k, cap=-1, b_r=None, renormalize=True, shared=None,
-                         scoring="softmax", n_group=1, topk_group=1):
+                         scoring="softmax", n_group=1, topk_group=1, act=None):
     """Returns (y, idx, gates) as nested lists.
 
     x [T][d]; w_r [E][d]; experts[e] = (Wg [d_e][d], Wu [d_e][d], Wd [d][d_e]);
     b_r [E] or None.  cap < 0: unlimited.  scoring "sigmoid": independent sigmoid
     affinities, b_r used only to choose, gates from the affinities; n_group > 1: only the
     topk_group groups (consecutive blocks of E / n_group experts) with the highest best
-    member may be chosen.
+    member may be chosen.  act "mxfp8": every expert product takes MXFP8 activations (x
+    rounded per token row, h rounded from its float32 value); the router sees x as given.
     """
     T = len(x)
     E = len(w_r)
@@ -89,13 +140,14 @@ def moe_dense_bruteforce(x, w_r, experts, k, cap=-1, b_r=None, renormalize=True,
             seen[e] += 1
             if cap < 0 or rank < cap:
                 gate_full[e] = g_sel[j]
+        xa = x[t] if act is None else _mxfp8_row(list(x[t]))
         y = [0.0] * d
         for e in range(E):                        # every expert runs
-            out = _expert(*experts[e], x[t])
+            out = _expert(*experts[e], xa, act)
             for i in range(d):
                 y[i] += gate_full[e] * out[i]
         if shared is not None:
-            out = _expert(*shared, x[t])
+            out = _expert(*shared, xa, act)
             for i in range(d):
                 y[i] += out[i]
         ys.append(y)

@@ -195,16 +195,24 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def swiglu_ffn(X: np.ndarray, w_g: np.ndarray, w_u: np.ndarray, w_d: np.ndarray) -> np.ndarray:
+def swiglu_ffn(X: np.ndarray, w_g: np.ndarray, w_u: np.ndarray, w_d: np.ndarray, act: str | None = None) -> np.ndarray:
     """FFN(X) = (SiLU(X W_g) * (X W_u)) W_d for rows X [m, d]; weights stored [out, in].
 
     Zero to Frontier §13.1, "The MoE layer" (each expert is a SwiGLU network);
     the kevinluzbetak.com layer's SwiGLU module (w1 = gate, w3 = up, w2 = down).
+    act="mxfp8": the activations entering each product are MXFP8 values (see
+    ``mxfp8_round_rows``): X as given (the caller passes it already rounded), and h rounded
+    from its float32 value before the down product.
     """
     X = np.asarray(X, np.float64)
     a = X @ np.asarray(w_g, np.float64).T
     b = X @ np.asarray(w_u, np.float64).T
-    return (silu(a) * b) @ np.asarray(w_d, np.float64).T
+    h = silu(a) * b
+    if act == "mxfp8":
+        h = mxfp8_round_rows(h.astype(np.float32))
+    elif act is not None:
+        raise ValueError(act)
+    return h @ np.asarray(w_d, np.float64).T
 
 
 # --------------------------------------------------------------------------- layer
@@ -301,7 +309,7 @@ def route(x, w_r, k: int, b_r=None, renormalize: bool = True, idx=None, scoring:
 
 def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: bool = True,
                 shared=None, idx=None, scoring: str = "softmax", n_group: int = 1,
-                topk_group: int = 1) -> Result:
+                topk_group: int = 1, act: str | None = None) -> Result:
     """The whole layer.
 
     experts: sequence (or any object with ``__getitem__`` and ``__len__``) whose
@@ -311,11 +319,14 @@ def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: b
     shared: (W_g, W_u, W_d) of an always-on expert added with weight 1, or None.
     idx: forced routing (int [T, k]); when given, gates are computed for it.
     scoring, n_group, topk_group: router variant (see ``route``).
+    act: None, or "mxfp8": the expert products take MXFP8 activations (x rounded once,
+    per token row; h rounded per row inside each expert); the router sees x unrounded.
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
     E = len(experts)
     r, p, idx, g, nt = route(x, w_r, k, b_r, renormalize, idx, scoring, n_group, topk_group)
+    xe = x if act is None else mxfp8_round_rows(x)
     counts, f, P, aux = load_balance_stats(p, idx, E)
     disp = dispatch(idx, E, cap)
     R_kept = int(disp.offsets[-1])
@@ -326,19 +337,20 @@ def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: b
             continue                              # unchosen experts never run
         toks = disp.row_token[lo:hi]
         wg, wu, wd = experts[e]
-        O[lo:hi] = swiglu_ffn(x[toks], wg, wu, wd)
+        O[lo:hi] = swiglu_ffn(xe[toks], wg, wu, wd, act)
     y = np.zeros((T, d), dtype=np.float64)
     for j in range(k):                            # fixed slot order
         rows = disp.row_of[:, j]
         keep = rows >= 0
         y[keep] += g[keep, j:j + 1] * O[rows[keep]]
     if shared is not None:
-        y += swiglu_ffn(x, *shared)
+        y += swiglu_ffn(xe, *shared, act=act)
     return Result(y=y, logits=r, p=p, idx=idx, gate=g, counts=counts, f=f, P=P, aux=aux,
                   disp=disp, near_tie=nt)
 
 
-def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared=None) -> np.ndarray:
+def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared=None,
+                       act: str | None = None) -> np.ndarray:
     """y for a few tokens, one token at a time, from their routing.
 
     x_rows [n, d]; idx_rows, gate_rows, kept_rows [n, k] (kept: bool).  expert_of(e)
@@ -346,6 +358,8 @@ def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared
     the per-token form of the layer, used to check sampled rows at full size.
     """
     x_rows = np.asarray(x_rows, np.float64)
+    if act is not None:
+        x_rows = mxfp8_round_rows(x_rows)
     n, d = x_rows.shape
     y = np.zeros((n, d))
     need: dict[int, list] = {}
@@ -357,13 +371,13 @@ def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared
     for e, tj in sorted(need.items()):
         wg, wu, wd = expert_of(e)
         ts = [t for t, _ in tj]
-        out = swiglu_ffn(x_rows[ts], wg, wu, wd)
+        out = swiglu_ffn(x_rows[ts], wg, wu, wd, act)
         for (t, j), row in zip(tj, out):
             contrib[t, j] = float(gate_rows[t, j]) * row
     for j in range(idx_rows.shape[1]):            # fixed slot order
         y += contrib[:, j]
     if shared is not None:
-        y += swiglu_ffn(x_rows, *shared)
+        y += swiglu_ffn(x_rows, *shared, act=act)
     return y
 
 
@@ -433,6 +447,73 @@ def dequantize_mx_rows(packed, scales, block: int = 32) -> np.ndarray:
     codes[:, 1::2] = packed >> 4
     sc = e8m0_decode(np.asarray(scales, dtype=np.uint8))          # [k/block, n]
     return e2m1_decode(codes) * np.repeat(sc.T, block, axis=1)
+
+
+# --------------------------------------------------------------------------- MXFP8 activations
+
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """The E4M3 code (uint8) nearest to each value, ties to the even code, magnitudes above
+    448 saturating to 448 (the format has no infinities).
+
+    Written from the format (see ``e4m3_decode``): a magnitude in [2^E, 2^(E+1)) with
+    E >= -6 has spacing 2^(E-3); below 2^-6 the subnormals have spacing 2^-9.  The sign is
+    kept, also on a value that rounds to zero (-0).  NaN is not an input here.
+    """
+    v = np.asarray(v, np.float64)
+    mag = np.minimum(np.abs(v), E4M3_MAX)
+    _, e = np.frexp(mag)                                   # mag = m 2^e, m in [0.5, 1)
+    E = np.where(mag > 0, e - 1, -7)
+    quantum = np.exp2(np.maximum(E, -6) - 3.0)
+    qm = np.round(mag / quantum) * quantum                 # np.round: half to even
+    qm = np.minimum(qm, E4M3_MAX)
+    # encode qm: exponent field and mantissa
+    _, e2 = np.frexp(qm)
+    E2 = np.where(qm > 0, e2 - 1, -7)
+    normal = E2 >= -6
+    expf = np.where(normal, E2 + 7, 0)
+    man = np.where(normal, qm / np.exp2(E2) - 1.0, qm / 2.0 ** -6) * 8.0
+    code = (expf.astype(np.int64) << 3) | np.round(man).astype(np.int64)
+    sign = np.signbit(v)                                   # a negative value that rounds to 0 is -0
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def mxfp8_quantize_rows(v, block: int = 32):
+    """OCP MXFP8 of the rows of v [n, k]: (codes uint8 [n, k], scales uint8 [n, k/block]).
+
+    Reading for the FP8 product's activations (the pages give FP8 as the storage of
+    DeepSeek-V3's weights -- jacopoparretti.dev, "Memory" -- but leave open how the
+    activations meet them): every block of 32 consecutive elements of a row shares an E8M0
+    scale 2^X with X = floor(log2(max |v| over the block)) - 8 (8 is the largest exponent
+    of E4M3, so the block maximum lands in [256, 512) before saturation at 448); each element
+    is the E4M3 code nearest v / 2^X.  An all-zero block gets the smallest scale, 2^-127.
+    The E8M0 byte is X + 127, kept in [0, 254].
+    """
+    v = np.asarray(v, np.float64)
+    n, kk = v.shape
+    blocks = v.reshape(n, kk // block, block)
+    amax = np.abs(blocks).max(axis=2)
+    _, e = np.frexp(amax)
+    X = np.where(amax > 0, e - 1 - 8, -127)
+    sc = np.clip(X + 127, 0, 254).astype(np.int64)
+    scaled = blocks / np.exp2(sc - 127.0)[:, :, None]
+    codes = e4m3_encode(scaled).reshape(n, kk)
+    return codes, sc.astype(np.uint8)
+
+
+def dequantize_mxfp8_rows(codes, scales, block: int = 32) -> np.ndarray:
+    """Values of MXFP8 rows: e4m3(code) * 2^(scale - 127), scales [n, k/block]."""
+    codes = np.asarray(codes, np.uint8)
+    sc = e8m0_decode(np.asarray(scales, np.uint8))
+    return e4m3_decode(codes) * np.repeat(sc, block, axis=1)
+
+
+def mxfp8_round_rows(v, block: int = 32) -> np.ndarray:
+    """v rounded to its MXFP8 value (quantise, then decode), float64."""
+    q, sc = mxfp8_quantize_rows(v, block)
+    return dequantize_mxfp8_rows(q, sc, block)
 
 
 def rel_err(y, y_ref) -> float:

@@ -307,6 +307,82 @@ def pin_near_ties_grouped():
                     assert set(base[t]) == set(moved[t]), (k, ng, tg, t)
 
 
+def pin_e4m3_encode_library():
+    """E4M3 rounding against torch's float8_e4m3fn conversion (round to nearest even): random
+    values over the whole range, every midpoint between neighbouring codes (ties must land on
+    the even code), every code's own value (exact round trip), saturation above 448."""
+    import torch
+    g = _rng(51)
+    v = g.standard_normal(100000) * np.exp2(g.integers(-14, 10, 100000))
+    v = np.clip(v, -448, 448)
+    want = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mo.e4m3_encode(v), want)
+    codes = np.arange(256, dtype=np.uint8)
+    vals = mo.e4m3_decode(codes)
+    ok = ~np.isnan(vals)
+    assert np.array_equal(mo.e4m3_encode(vals[ok]), codes[ok])
+    pos = np.sort(vals[ok & (vals > 0)])
+    mid = (pos[:-1] + pos[1:]) / 2
+    got = mo.e4m3_encode(mid)
+    assert np.array_equal(got, torch.from_numpy(mid.astype(np.float32)).to(torch.float8_e4m3fn)
+                          .view(torch.uint8).numpy())
+    assert np.all(got % 2 == 0)
+    assert list(mo.e4m3_encode(np.array([448.0, 463.9, 1e4, -1e4]))) == [0x7E, 0x7E, 0x7E, 0xFE]
+
+
+def pin_mxfp8_scale_rule():
+    """The MX block scale 2^X, X = floor(log2 block max) - 8, on hand-worked blocks, and the
+    rounding error bound it implies: at most half a step of E4M3 at the element's size
+    (2^-4 relative in the normal range; 2^(X-10) absolute below it), and elements above
+    448 * 2^X saturating to exactly that."""
+    rows = np.zeros((6, 64))
+    rows[0, :32] = 448.0                 # X = 0
+    rows[1, 5] = 1.0                     # X = -8
+    rows[2, 31] = -0.75                  # floor(log2 0.75) = -1: X = -9
+    rows[3, :] = 2.0 ** -140             # below the smallest scale: X clamps to -127
+    rows[4, 33] = 3.0                    # second block only: X = -7; first block all zero
+    rows[5, :32] = np.arange(32) * 0.25  # max 7.75: X = -6, and 7.75 * 2^6 = 496 saturates to 448
+    q, sc = mo.mxfp8_quantize_rows(rows)
+    assert sc.tolist() == [[127, 0], [119, 0], [118, 0], [0, 0], [0, 120], [121, 0]], sc.tolist()
+    back = mo.dequantize_mxfp8_rows(q, sc)
+    assert np.array_equal(back[:3], rows[:3]) and np.array_equal(back[4], rows[4])
+    assert back[5, 31] == 7.0 and back[5, 28] == 7.0 and back[5, 4] == 1.0
+    g = _rng(52)
+    v = g.standard_normal((40, 256)) * np.exp2(g.integers(-20, 20, (40, 1)))
+    q, sc = mo.mxfp8_quantize_rows(v)
+    back = mo.dequantize_mxfp8_rows(q, sc)
+    X = np.repeat(sc.astype(np.int64) - 127, 32, axis=1)
+    sat = np.abs(v) > 448.0 * np.exp2(X)               # the block maximum can land in (448, 512) * 2^X
+    normal = (np.abs(v) >= np.exp2(X - 6.0)) & ~sat
+    sub = np.abs(v) < np.exp2(X - 6.0)
+    assert sat.any() and normal.any() and sub.any()
+    assert np.all(np.abs(back - v)[normal] <= np.abs(v)[normal] * 2.0 ** -4)
+    assert np.all(np.abs(back - v)[sub] <= np.exp2(X[sub] - 10.0))
+    assert np.array_equal(np.abs(back)[sat], (448.0 * np.exp2(X))[sat])
+
+
+def pin_mxfp8_layer_bruteforce():
+    """The layer with MXFP8 activations against the pure-Python brute force (table-search
+    E4M3 rounding), with capacity, bias, a shared expert and both scorings."""
+    for seed, T, d, de, E, k, cap, scoring in [(61, 3, 64, 32, 4, 2, 2, "softmax"), (62, 4, 32, 64, 5, 1, -1,
+                                                                                      "sigmoid")]:
+        g = _rng(seed)
+        x = g.standard_normal((T, d))
+        w_r = g.standard_normal((E, d))
+        ex = [(g.standard_normal((de, d)) * .3, g.standard_normal((de, d)) * .3, g.standard_normal((d, de)) * .3)
+              for _ in range(E)]
+        sh = (g.standard_normal((32, d)) * .3, g.standard_normal((32, d)) * .3, g.standard_normal((d, 32)) * .3)
+        b = g.standard_normal(E) * 0.2
+        res = mo.moe_forward(x, w_r, ex, k, cap, b, True, sh, scoring=scoring, act="mxfp8")
+        yb, ib, _ = bf.moe_dense_bruteforce(x.tolist(), w_r.tolist(), [tuple(m.tolist() for m in e) for e in ex], k,
+                                            cap, b.tolist(), True, tuple(m.tolist() for m in sh), scoring, act="mxfp8")
+        assert np.array_equal(res.idx, np.array(ib))
+        assert np.allclose(res.y, np.array(yb), rtol=1e-12, atol=1e-12)
+        # the rounding changes the output by about the E4M3 step, not more
+        plain = mo.moe_forward(x, w_r, ex, k, cap, b, True, sh, scoring=scoring)
+        assert 1e-3 < mo.rel_err(res.y, plain.y) < 0.3
+
+
 def pin_dispatch_invariants():
     g = _rng(6)
     for (T, E, k, cap) in [(50, 5, 2, -1), (50, 5, 2, 7), (33, 4, 3, 0), (64, 8, 1, 5), (0, 3, 2, 4)]:

@@ -13,7 +13,7 @@ from oracle import moe_oracle as mo
 
 _orig = {name: getattr(mo, name) for name in
          ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
-          "capacity", "dispatch", "near_ties", "near_ties_grouped", "sigmoid", "group_limited_top_k", "route", "e4m3_decode",
+          "capacity", "dispatch", "near_ties", "near_ties_grouped", "sigmoid", "group_limited_top_k", "route", "e4m3_decode", "e4m3_encode", "mxfp8_quantize_rows", "mxfp8_round_rows",
           "dequantize_rows", "e2m1_decode", "e8m0_decode", "dequantize_mx_rows", "silu_grad",
           "swiglu_backward", "router_backward", "moe_backward"]}
 
@@ -323,6 +323,45 @@ def _ntg_no_group_decision(score, k, n_group, topk_group, threshold=mo.NEAR_TIE)
     return mo.near_ties(masked, k, threshold) if k < topk_group * gs else np.zeros(0, dtype=np.int64)
 
 
+def _enc_ties_away(v):
+    v = np.asarray(v, np.float64)
+    c = _orig["e4m3_encode"](v)
+    lo = mo.e4m3_decode(c)
+    up = mo.e4m3_decode(np.where(c % 2 == 0, c + 1, c).astype(np.uint8))
+    tie = np.isclose(np.abs(v) - np.abs(lo), np.abs(up) - np.abs(v), rtol=0, atol=0) & (c % 2 == 0) & (np.abs(v) > 0)
+    return np.where(tie & (np.abs(v) < 448), c + 1, c).astype(np.uint8)
+
+
+def _enc_truncate(v):
+    v = np.asarray(v, np.float64)
+    c = _orig["e4m3_encode"](v)
+    over = np.abs(mo.e4m3_decode(c)) > np.abs(v)
+    return np.where(over & (c % 128 > 0), c - 1, c).astype(np.uint8)
+
+
+def _enc_no_saturation(v):
+    v = np.asarray(v, np.float64)
+    c = _orig["e4m3_encode"](v)
+    return np.where(np.abs(v) > 448, np.uint8(0x7F) | (c & 0x80), c).astype(np.uint8)
+
+
+def _mxq_scale_minus7(v, block=32):
+    q, sc = _orig["mxfp8_quantize_rows"](v, block)
+    sc = np.minimum(sc.astype(np.int64) + 1, 254).astype(np.uint8)
+    vals = np.asarray(v, np.float64) / np.repeat(np.exp2(sc.astype(np.float64) - 127), block, axis=1)
+    return mo.e4m3_encode(vals), sc
+
+
+def _mxq_row_scale(v, block=32):
+    v = np.asarray(v, np.float64)
+    return _orig["mxfp8_quantize_rows"](v, v.shape[1])[0], np.repeat(
+        _orig["mxfp8_quantize_rows"](v, v.shape[1])[1], v.shape[1] // block, axis=1)
+
+
+def _mxr_identity(v, block=32):
+    return np.asarray(v, np.float64)
+
+
 MUTANTS = [
     ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
     ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
@@ -342,6 +381,9 @@ MUTANTS = [
     ("route", _route_bias_in_gates),
     ("e4m3_decode", _e4m3_bias8), ("e4m3_decode", _e4m3_no_subnormals), ("e4m3_decode", _e4m3_mantissa_16),
     ("dequantize_rows", _dequant_columns),
+    ("e4m3_encode", _enc_ties_away), ("e4m3_encode", _enc_truncate), ("e4m3_encode", _enc_no_saturation),
+    ("mxfp8_quantize_rows", _mxq_scale_minus7), ("mxfp8_quantize_rows", _mxq_row_scale),
+    ("mxfp8_round_rows", _mxr_identity),
     ("e2m1_decode", _e2m1_bias2), ("e2m1_decode", _e2m1_no_subnormal), ("e8m0_decode", _e8m0_bias128),
     ("dequantize_mx_rows", _mx_nibbles_swapped), ("dequantize_mx_rows", _mx_scales_transposed),
     ("silu_grad", _silu_grad_sigmoid), ("silu_grad", _silu_grad_sign),
