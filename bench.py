@@ -147,7 +147,8 @@ def run_gpu(wl_name, steps, warmup, dev_weights=None, kernel_stage="gate_up", gr
                            d_e_shared=w.d_e_shared, dtype=moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32,
                            scoring=1 if w.scoring == "sigmoid" else 0, n_group=w.n_group, topk_group=w.topk_group,
                            wfmt={"native": moe.MOE_W_NATIVE, "fp8_e4m3": moe.MOE_W_FP8_E4M3,
-                                 "mxfp4": moe.MOE_W_MXFP4}[w.weights])
+                                 "mxfp4": moe.MOE_W_MXFP4}[w.weights],
+                           afmt={None: moe.MOE_A_NATIVE, "mxfp8": moe.MOE_A_MXFP8}[w.act])
     out = moe.alloc_forward(shape)
     ev = HipEvents()
     nst = moe._lib.MOE_NUM_STAGES

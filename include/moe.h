@@ -37,7 +37,8 @@
  *   scoring in {MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID}; 1 <= n_group <= 64 dividing E;
  *   1 <= topk_group <= n_group; k <= topk_group * E / n_group; T*d*elem_size < 2^32 for
  *   moe_forward (its gather uses 32-bit byte offsets); wfmt in {MOE_W_NATIVE, MOE_W_FP8_E4M3,
- *   MOE_W_MXFP4}, quantised weights only with dtype MOE_BF16.
+ *   MOE_W_MXFP4}, quantised weights only with dtype MOE_BF16; afmt in {MOE_A_NATIVE,
+ *   MOE_A_MXFP8}, MOE_A_MXFP8 only with quantised weights.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -74,6 +75,7 @@ typedef struct {
   int32_t n_group;     /* expert groups (consecutive blocks of E / n_group); 1 = no group limit */
   int32_t topk_group;  /* groups a token may use (1 <= topk_group <= n_group; 1 when n_group = 1) */
   int32_t wfmt;        /* moe_wfmt of the expert weights (router weight: always dtype) */
+  int32_t afmt;        /* moe_afmt of the activations entering the expert products */
 } moe_shape;
 
 /* Storage of the expert weights (routed and shared).
@@ -92,6 +94,20 @@ typedef struct {
  *   Weights [G, rows, K/2] bytes; scales [G, K/32, rows] bytes (block-major).  Decoded values
  *   (element x scale, exact in bf16) feed bf16 products with fp32 accumulation. */
 typedef enum { MOE_W_NATIVE = 0, MOE_W_FP8_E4M3 = 1, MOE_W_MXFP4 = 2 } moe_wfmt;
+
+/* Activations entering the expert products (the router always sees x in dtype).
+ * MOE_A_NATIVE: x and h in dtype (bf16 with quantised weights: the decoded weights meet bf16
+ *   activations in bf16 products).
+ * MOE_A_MXFP8: both products run on gfx950's scaled FP8 MFMA.  x (per token row) and h (per
+ *   row) are OCP MXFP8: every 32 consecutive elements along the contraction share an E8M0 scale
+ *   2^X, X = floor(log2 of the block's largest magnitude) - 8, and each element is the nearest
+ *   E4M3 value of v / 2^X (ties to even, saturating at 448); h is rounded from its fp32 value.
+ *   The weights' own scales apply as in MOE_A_NATIVE (FP8: fp32 row scales; MXFP4: E8M0 block
+ *   scales, applied by the MFMA).  Requires wfmt MOE_W_FP8_E4M3 or MOE_W_MXFP4 (dtype bf16).
+ *   The pages store weights in 8 or 4 bits (jacopoparretti.dev, "Memory"; AI Engineering
+ *   Illustrated, "Total parameters and active parameters are different budgets") and leave the
+ *   activations' format open; MXFP8 is the form the scaled MFMA consumes.  Forward only. */
+typedef enum { MOE_A_NATIVE = 0, MOE_A_MXFP8 = 1 } moe_afmt;
 
 /* Scales of quantised expert weights (device pointers; G = E for routed experts, 1 for the
  * shared expert).  K is the contraction width of the matrix: d for W_g and W_u, d_e for W_d.
@@ -254,6 +270,14 @@ moe_status moe_forward_noalloc(const moe_shape *shape, const void *x, const void
                                float *f, float *P, float *aux,
                                int32_t *offsets, int32_t *row_token, int32_t *row_of,
                                void *stream, void *const *stage_events);
+
+/* MXFP8 rows (the MOE_A_MXFP8 activation format) of x [rows, K] (bf16, 16-byte aligned; device):
+ * codes [rows, K] E4M3 bytes and scales [rows, K/32] E8M0 bytes (device, caller-owned).  The
+ * same rounding the layer applies to its activations.  Errors: rows < 0 or K not a positive
+ * multiple of 32 -> MOE_ERR_SHAPE; a NULL pointer with rows > 0 -> MOE_ERR_NULL; a failed
+ * launch -> MOE_ERR_HIP. */
+moe_status moe_mxfp8_quantize(int32_t rows, int32_t K, const void *x, uint8_t *codes, uint8_t *scales,
+                              void *stream);
 
 /* ---------------------------------------------------------------- backward pass */
 

@@ -230,6 +230,7 @@ class Result:
     aux: float
     disp: Dispatch
     near_tie: np.ndarray   # token indices
+    y_bound: np.ndarray | None = None   # act="mxfp8" with mx_eps: per-element deviation bound of y
 
 
 # --------------------------------------------------------------------------- DeepSeek-V3 style router
@@ -309,7 +310,7 @@ def route(x, w_r, k: int, b_r=None, renormalize: bool = True, idx=None, scoring:
 
 def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: bool = True,
                 shared=None, idx=None, scoring: str = "softmax", n_group: int = 1,
-                topk_group: int = 1, act: str | None = None) -> Result:
+                topk_group: int = 1, act: str | None = None, mx_eps: float | None = None) -> Result:
     """The whole layer.
 
     experts: sequence (or any object with ``__getitem__`` and ``__len__``) whose
@@ -321,6 +322,8 @@ def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: b
     scoring, n_group, topk_group: router variant (see ``route``).
     act: None, or "mxfp8": the expert products take MXFP8 activations (x rounded once,
     per token row; h rounded per row inside each expert); the router sees x unrounded.
+    mx_eps (with act="mxfp8"): also return y_bound, the per-element bound of
+    ``swiglu_mx_deviation`` carried through the gates and the combine.
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
@@ -331,6 +334,8 @@ def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: b
     disp = dispatch(idx, E, cap)
     R_kept = int(disp.offsets[-1])
     O = np.zeros((R_kept, d), dtype=np.float64)
+    bound = mx_eps is not None and act == "mxfp8"
+    OB = np.zeros((R_kept, d), dtype=np.float64) if bound else None
     for e in range(E):
         lo, hi = int(disp.offsets[e]), int(disp.offsets[e + 1])
         if hi == lo:
@@ -338,24 +343,32 @@ def moe_forward(x, w_r, experts, k: int, cap: int = -1, b_r=None, renormalize: b
         toks = disp.row_token[lo:hi]
         wg, wu, wd = experts[e]
         O[lo:hi] = swiglu_ffn(xe[toks], wg, wu, wd, act)
+        if bound:
+            OB[lo:hi] = swiglu_mx_deviation(xe[toks], wg, wu, wd, mx_eps)[3]
     y = np.zeros((T, d), dtype=np.float64)
+    yb = np.zeros((T, d), dtype=np.float64) if bound else None
     for j in range(k):                            # fixed slot order
         rows = disp.row_of[:, j]
         keep = rows >= 0
         y[keep] += g[keep, j:j + 1] * O[rows[keep]]
+        if bound:
+            yb[keep] += np.abs(g[keep, j:j + 1]) * OB[rows[keep]]
     if shared is not None:
         y += swiglu_ffn(xe, *shared, act=act)
+        if bound:
+            yb += swiglu_mx_deviation(xe, *shared, mx_eps)[3]
     return Result(y=y, logits=r, p=p, idx=idx, gate=g, counts=counts, f=f, P=P, aux=aux,
-                  disp=disp, near_tie=nt)
+                  disp=disp, near_tie=nt, y_bound=yb)
 
 
 def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared=None,
-                       act: str | None = None) -> np.ndarray:
+                       act: str | None = None, mx_eps: float | None = None):
     """y for a few tokens, one token at a time, from their routing.
 
     x_rows [n, d]; idx_rows, gate_rows, kept_rows [n, k] (kept: bool).  expert_of(e)
     returns (W_g, W_u, W_d).  Evaluates sum_j kept * g_j FFN_{idx_j}(x) directly:
     the per-token form of the layer, used to check sampled rows at full size.
+    With act="mxfp8" and mx_eps, returns (y, y_bound) (see ``moe_forward``).
     """
     x_rows = np.asarray(x_rows, np.float64)
     if act is not None:
@@ -367,18 +380,25 @@ def outputs_for_tokens(x_rows, idx_rows, gate_rows, kept_rows, expert_of, shared
         for j in range(idx_rows.shape[1]):
             if kept_rows[t, j]:
                 need.setdefault(int(idx_rows[t, j]), []).append((t, j))
+    bound = mx_eps is not None and act == "mxfp8"
+    yb = np.zeros((n, d))
     contrib = np.zeros((n, idx_rows.shape[1], d))
     for e, tj in sorted(need.items()):
         wg, wu, wd = expert_of(e)
         ts = [t for t, _ in tj]
         out = swiglu_ffn(x_rows[ts], wg, wu, wd, act)
-        for (t, j), row in zip(tj, out):
+        ob = swiglu_mx_deviation(x_rows[ts], wg, wu, wd, mx_eps)[3] if bound else None
+        for i, ((t, j), row) in enumerate(zip(tj, out)):
             contrib[t, j] = float(gate_rows[t, j]) * row
+            if bound:
+                yb[t] += abs(float(gate_rows[t, j])) * ob[i]
     for j in range(idx_rows.shape[1]):            # fixed slot order
         y += contrib[:, j]
     if shared is not None:
         y += swiglu_ffn(x_rows, *shared, act=act)
-    return y
+        if bound:
+            yb += swiglu_mx_deviation(x_rows, *shared, mx_eps)[3]
+    return (y, yb) if bound else y
 
 
 # --------------------------------------------------------------------------- FP8 expert weights
@@ -480,6 +500,15 @@ def e4m3_encode(v) -> np.ndarray:
     return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
 
 
+def _mx_scale_code(amax) -> np.ndarray:
+    """E8M0 byte of MX blocks with largest magnitudes amax: floor(log2 amax) - 8 + 127 in [0, 254];
+    an all-zero block gets 0."""
+    amax = np.asarray(amax, np.float64)
+    _, e = np.frexp(amax)
+    X = np.where(amax > 0, e - 1 - 8, -127)
+    return np.clip(X + 127, 0, 254).astype(np.int64)
+
+
 def mxfp8_quantize_rows(v, block: int = 32):
     """OCP MXFP8 of the rows of v [n, k]: (codes uint8 [n, k], scales uint8 [n, k/block]).
 
@@ -494,10 +523,7 @@ def mxfp8_quantize_rows(v, block: int = 32):
     v = np.asarray(v, np.float64)
     n, kk = v.shape
     blocks = v.reshape(n, kk // block, block)
-    amax = np.abs(blocks).max(axis=2)
-    _, e = np.frexp(amax)
-    X = np.where(amax > 0, e - 1 - 8, -127)
-    sc = np.clip(X + 127, 0, 254).astype(np.int64)
+    sc = _mx_scale_code(np.abs(blocks).max(axis=2))
     scaled = blocks / np.exp2(sc - 127.0)[:, :, None]
     codes = e4m3_encode(scaled).reshape(n, kk)
     return codes, sc.astype(np.uint8)
@@ -514,6 +540,81 @@ def mxfp8_round_rows(v, block: int = 32) -> np.ndarray:
     """v rounded to its MXFP8 value (quantise, then decode), float64."""
     q, sc = mxfp8_quantize_rows(v, block)
     return dequantize_mxfp8_rows(q, sc, block)
+
+
+# --------------------------------------------------------------------------- MXFP8: reachable codes
+
+SILU_ARGMIN = -1.2784645427610738       # SiLU's only stationary point (its global minimum)
+
+
+def silu_range(lo, hi):
+    """(min, max) of SiLU over each interval [lo, hi]: SiLU falls to its minimum at SILU_ARGMIN
+    and rises after it, so the extremes are the end points and, inside, that minimum."""
+    lo = np.asarray(lo, np.float64)
+    hi = np.asarray(hi, np.float64)
+    sl, sh = silu(lo), silu(hi)
+    inside = (lo <= SILU_ARGMIN) & (SILU_ARGMIN <= hi)
+    return np.where(inside, silu(np.float64(SILU_ARGMIN)), np.minimum(sl, sh)), np.maximum(sl, sh)
+
+
+def mxfp8_round_interval(lo, hi, block: int = 32):
+    """Lowest and highest MXFP8 value each element of rows [n, k] can round to when every element
+    may take any value in its own interval [lo, hi].
+
+    The block scale follows the block maximum, which ranges over [largest lower magnitude, largest
+    upper magnitude]; every E8M0 code between the two end codes is reachable.  For a fixed scale
+    the rounding (nearest, saturating) never decreases with the value, so an element's extremes
+    under that scale are the roundings of lo and hi.
+    """
+    lo = np.asarray(lo, np.float64)
+    hi = np.asarray(hi, np.float64)
+    n, kk = lo.shape
+    L = lo.reshape(n, kk // block, block)
+    H = hi.reshape(n, kk // block, block)
+    straddle = (L <= 0) & (H >= 0)
+    mlo = np.where(straddle, 0.0, np.minimum(np.abs(L), np.abs(H)))
+    mhi = np.maximum(np.abs(L), np.abs(H))
+    c_lo = _mx_scale_code(mlo.max(axis=2))
+    c_hi = _mx_scale_code(mhi.max(axis=2))
+    qlo = np.full(L.shape, np.inf)
+    qhi = np.full(L.shape, -np.inf)
+    for off in range(int((c_hi - c_lo).max()) + 1 if n * kk else 0):
+        c = np.minimum(c_lo + off, c_hi)[:, :, None]
+        sc = np.exp2(c - 127.0)
+        qlo = np.minimum(qlo, e4m3_decode(e4m3_encode(L / sc)) * sc)
+        qhi = np.maximum(qhi, e4m3_decode(e4m3_encode(H / sc)) * sc)
+    return qlo.reshape(n, kk), qhi.reshape(n, kk)
+
+
+def swiglu_mx_deviation(X, w_g, w_u, w_d, eps: float):
+    """How far an implementation of the MXFP8 SwiGLU product may land from this oracle's, per
+    output element, when each of its dot products is within eps times the sum of its terms'
+    magnitudes of the exact value (what a floating-point accumulation gives).
+
+    X [m, d] are MXFP8 values (both sides round x identically, bit for bit).  a and b then lie
+    in [a - eps A, a + eps A] with A = |X| |W_g|^T (and the same for b); h = SiLU(a) b lies in the
+    range of SiLU over a's interval times b's interval, widened by 2^-20 relative for the fp32
+    rounding of h and the hardware exp and reciprocal behind SiLU; its MXFP8 value may be any
+    value reachable from that interval (``mxfp8_round_interval``) -- a value near a rounding
+    midpoint can go either way.  Returns (hq, qlo, qhi, bound): the oracle's rounded h, the
+    reachable range of each element, and per output element of h W_d^T the bound
+    sum_j dev_j |W_d[n, j]| + eps sum_j (|hq_j| + dev_j) |W_d[n, j]|, dev_j the larger distance
+    from hq_j to its range's ends.
+    """
+    X = np.asarray(X, np.float64)
+    wg, wu, wd = (np.asarray(w, np.float64) for w in (w_g, w_u, w_d))
+    a, b = X @ wg.T, X @ wu.T
+    da, db = eps * (np.abs(X) @ np.abs(wg).T), eps * (np.abs(X) @ np.abs(wu).T)
+    s_lo, s_hi = silu_range(a - da, a + da)
+    corners = np.stack([s_lo * (b - db), s_lo * (b + db), s_hi * (b - db), s_hi * (b + db)])
+    hlo, hhi = corners.min(axis=0), corners.max(axis=0)
+    hlo = hlo - np.abs(hlo) * 2.0 ** -20
+    hhi = hhi + np.abs(hhi) * 2.0 ** -20
+    hq = mxfp8_round_rows((silu(a) * b).astype(np.float32))
+    qlo, qhi = mxfp8_round_interval(hlo, hhi)
+    dev = np.maximum(qhi - hq, hq - qlo)
+    awd = np.abs(wd)
+    return hq, qlo, qhi, dev @ awd.T + eps * ((np.abs(hq) + dev) @ awd.T)
 
 
 def rel_err(y, y_ref) -> float:

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_W_NATIVE, MOE_W_FP8_E4M3, MOE_W_MXFP4 = 0, 1, 2
+MOE_A_NATIVE, MOE_A_MXFP8 = 0, 1
 MOE_NUM_STAGES = 8
 MOE_STATIC_SCRATCH_BYTES = 64 << 20
 STAGE_NAMES = ["router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
@@ -28,7 +29,7 @@ class MoeShape(C.Structure):
     _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("d_e", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("capacity", C.c_int32), ("renormalize", C.c_int32), ("d_e_shared", C.c_int32),
                 ("dtype", C.c_int32), ("scoring", C.c_int32), ("n_group", C.c_int32), ("topk_group", C.c_int32),
-                ("wfmt", C.c_int32)]
+                ("wfmt", C.c_int32), ("afmt", C.c_int32)]
 
 
 class MoeWScales(C.Structure):
@@ -51,6 +52,7 @@ SIGNATURES = {
                     + [_P, C.c_size_t, _P, _P]),
     "moe_forward_noalloc": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 9 + [C.POINTER(MoeWScales)] * 2 + [_P] * 11
                             + [_P, _P]),
+    "moe_mxfp8_quantize": (C.c_int, [C.c_int32, C.c_int32, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (C.c_int, [C.POINTER(MoeShape), C.POINTER(C.c_size_t)]),
     "moe_backward": (C.c_int, [C.POINTER(MoeShape)] + [_P] * 16 + [C.c_float] + [_P] * 10
                      + [_P, C.c_size_t, _P, _P]),

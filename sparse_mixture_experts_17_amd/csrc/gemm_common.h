@@ -36,6 +36,10 @@ struct GemmArgs {
   // dense products only: number tiles n-tile-minor (all n-tiles of an m-tile consecutive, so one
   // XCD reads each activation row once; for few n-tiles and B small enough to stay in L2)
   int dense_n_minor = 0;
+  // MXFP8 activations (grouped_gemm_mx.hip): E8M0 scales of A [rows of A, K/32] (gathered through
+  // a_rows like A), and of the gated product's MXFP8 output h [rows, N/32] (C then holds E4M3 codes)
+  const uint8_t* a_scales = nullptr;
+  uint8_t* c_scales = nullptr;
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).

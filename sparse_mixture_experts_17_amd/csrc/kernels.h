@@ -107,6 +107,26 @@ hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, c
                             const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
                             int N, int K, float* O, int ksplit, size_t split_stride, hipStream_t stream);
 
+// ---- FP8 products with MXFP8 activations (grouped_gemm_mx.hip)
+// OCP MXFP8 of the rows of x [rows, K] (bf16): codes [rows, K] E4M3, scales [rows, K/32] E8M0,
+// block scale 2^(floor(log2 max|v|) - 8), elements rounded to nearest even, saturated at 448.
+hipError_t launch_mxfp8_quantize(const void* x, int rows, int K, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
+// Rows per tile of the MXFP8 products for `kind`.
+int gemm_block_m_mx(GemmKind kind);
+// Gate/up product on the scaled MFMA: A = MXFP8 rows (codes [*, K] and scales [*, K/32], row
+// a_rows[r] when a_rows != NULL), weights wfmt 1 (E4M3 with row scales Sg, Su [G, N]) or 2
+// (MXFP4 with E8M0 [G, K/32, N]).  h = SiLU(a) * b is written as MXFP8: Hq [rows, N] codes,
+// Hs [rows, N/32] scales.
+hipError_t launch_gemm_gateup_mx(GemmKind kind, int wfmt, const uint8_t* A, const uint8_t* As, const int32_t* a_rows,
+                                 const void* Wg, const void* Wu, const void* Sg, const void* Su,
+                                 const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
+                                 int max_tiles_m, int N, int K, uint8_t* Hq, uint8_t* Hs, hipStream_t stream);
+// Down product on the scaled MFMA: o [rows, N] fp32 = Hq W_d^T (times Sd [G, N] for wfmt 1).
+hipError_t launch_gemm_down_mx(GemmKind kind, int wfmt, const uint8_t* Hq, const uint8_t* Hs, const void* Wd,
+                               const void* Sd, const int32_t* offsets, const int32_t* tstart, int G, int dense_rows,
+                               int max_tiles_m, int N, int K, float* O, hipStream_t stream);
+
 // ---- backward products (grouped_gemm_bwd.hip)
 // Gate/up product again with the gate/up tiles of `kind`: a_out, b_out [rows, N] fp32 (the
 // pre-activations) and hT [N, ldt] = h^T in dtype, row r of group g at column

@@ -34,13 +34,13 @@ GemmKind choose_kind(long long rows_total, int groups, int cap) {
 // 8- and 16-bit weights the tiles already fill the CUs, and the extra partial sums only cost
 // time.)  The combine sums the chunks' partial outputs.
 int down_ksplit(const moe_shape& s, GemmKind kind) {
-  if (kind != kGemmDecode || s.wfmt != MOE_W_MXFP4) return 1;
+  if (kind != kGemmDecode || s.wfmt != MOE_W_MXFP4 || s.afmt != MOE_A_NATIVE) return 1;
   return s.d_e % 128 == 0 && s.d_e / 128 >= 16 ? 2 : 1;
 }
 
 struct Layout {
   size_t p_part, hist, chunk_base, counts, kept, offsets, row_token, row_of, tstart1, tstart2, logits;
-  size_t x_perm, h, o, sh_h, sh_o, total;
+  size_t x_perm, xq, h, o, sh_h, sh_o, total;
   int ksplit;   // K chunks of the routed down product in the forward (partials at o + c * T*k*d)
 };
 
@@ -65,6 +65,9 @@ Layout layout(const moe_shape& s) {
   L.tstart2 = take((E + 1) * sizeof(int32_t));
   L.logits = take(router_logits_bytes(s.T, s.d, s.E));
   L.x_perm = take(R * (size_t)s.d * es);
+  // MXFP8 activations: x (or x_perm) as codes [R, d] then scales [R, d/32]; h and the shared
+  // expert's h as codes then scales inside their bf16-sized pieces (1 + 1/32 <= 2 bytes each)
+  L.xq = take(s.afmt == MOE_A_MXFP8 ? R * (size_t)s.d + R * (size_t)(s.d / 32) : 0);
   L.h = take(R * (size_t)s.d_e * es);
   L.ksplit = down_ksplit(s, choose_kind(std::max<long long>((long long)R, 1), s.E, s.capacity));
   L.o = take(R * (size_t)s.d * sizeof(float) * (size_t)L.ksplit);
@@ -141,6 +144,8 @@ moe_status check_shape(const moe_shape* s) {
   if ((long long)s->k > (long long)s->topk_group * (s->E / s->n_group)) return MOE_ERR_SHAPE;
   if (s->wfmt != MOE_W_NATIVE && s->wfmt != MOE_W_FP8_E4M3 && s->wfmt != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
   if (s->wfmt != MOE_W_NATIVE && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->afmt != MOE_A_NATIVE && s->afmt != MOE_A_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (s->afmt == MOE_A_MXFP8 && s->wfmt == MOE_W_NATIVE) return MOE_ERR_UNSUPPORTED;
   if (s->n_group > 64) return MOE_ERR_UNSUPPORTED;
   if (s->E > 1024 || s->k > 16) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 || s->d_e % 128 || s->d_e_shared % 128) return MOE_ERR_UNSUPPORTED;
@@ -151,6 +156,11 @@ moe_status check_shape(const moe_shape* s) {
   if ((long long)s->T * s->k * (long long)s->d * (s->dtype == MOE_BF16 ? 2 : 4) >= (1LL << 35))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// Rows per tile of the gate/up (gated) or down product for this shape's formats.
+int block_m(const moe_shape& s, GemmKind kind, bool gated) {
+  return s.afmt == MOE_A_MXFP8 ? gemm_block_m_mx(kind) : gemm_block_m(kind, s.dtype, gated, s.wfmt);
 }
 
 // Upper bound on the number of m-tiles over all groups.
@@ -191,6 +201,21 @@ const moe_wscales kNoScales = {nullptr, nullptr, nullptr};
 
 bool scales_ok(const moe_shape& s, const moe_wscales* sc) {
   return s.wfmt == MOE_W_NATIVE || (sc && sc->gate && sc->up && sc->down);
+}
+
+// The two products of the MXFP8-activation mode: A = MXFP8 rows (codes aq, scales as, row
+// a_rows[r] when given), h as MXFP8 in the piece at h (codes [rows, d_e] then scales).
+moe_status run_ffn_mx(const moe_shape& s, int G, const uint8_t* aq, const uint8_t* as, const int32_t* a_rows,
+                      const int32_t* offsets, const int32_t* tstart1, const int32_t* tstart2, GemmKind kind,
+                      int tiles1, int tiles2, int dense_rows, long long h_rows, int d_e, const void* wg,
+                      const void* wu, const void* wd, const moe_wscales& sc, void* h, float* o, hipStream_t st) {
+  uint8_t* hq = (uint8_t*)h;
+  uint8_t* hs = hq + (size_t)h_rows * (size_t)d_e;
+  MOE_HIP(launch_gemm_gateup_mx(kind, s.wfmt, aq, as, a_rows, wg, wu, sc.gate, sc.up, offsets, tstart1, G, dense_rows,
+                                tiles1, d_e, s.d, hq, hs, st));
+  MOE_HIP(launch_gemm_down_mx(kind, s.wfmt, hq, hs, wd, sc.down, offsets, tstart2, G, dense_rows, tiles2, s.d, d_e, o,
+                              st));
+  return MOE_OK;
 }
 
 moe_status run_ffn(const moe_shape& s, int G, const void* A, const int32_t* offsets, const int32_t* tstart1,
@@ -325,10 +350,19 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int3
   const long long R = (long long)s.T * s.k;
   if (R == 0) return MOE_OK;
   const GemmKind kind = choose_kind(R, s.E, s.capacity);
-  const int bm1 = gemm_block_m(kind, s.dtype, true, s.wfmt), bm2 = gemm_block_m(kind, s.dtype, false, s.wfmt);
+  const int bm1 = block_m(s, kind, true), bm2 = block_m(s, kind, false);
   int32_t* ts1 = at<int32_t>(ws, L.tstart1);
   int32_t* ts2 = at<int32_t>(ws, L.tstart2);
   MOE_HIP(launch_tile_sched(offsets, s.E, bm1, ts1, bm2, ts2, st));
+  if (s.afmt == MOE_A_MXFP8) {
+    // every row of x_perm is quantised (rows past offsets[E] are unspecified and never read)
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    uint8_t* xs = xq + (size_t)R * s.d;
+    MOE_HIP(launch_mxfp8_quantize(x_perm, (int)R, s.d, xq, xs, st));
+    return run_ffn_mx(s, s.E, xq, xs, nullptr, offsets, ts1, ts2, kind, max_m_tiles(R, s.E, -1, bm1),
+                      max_m_tiles(R, s.E, -1, bm2), 0, R, s.d_e, w_gate, w_up, w_down, *scales, at<void>(ws, L.h), o,
+                      st);
+  }
   return run_ffn(s, s.E, x_perm, offsets, ts1, ts2, kind, max_m_tiles(R, s.E, -1, bm1), max_m_tiles(R, s.E, -1, bm2),
                  0, s.d_e, w_gate, w_up, w_down, s.wfmt != MOE_W_NATIVE ? *scales : kNoScales, at<void>(ws, L.h), o,
                  st);
@@ -379,7 +413,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
 
   const long long R = (long long)s.T * s.k;
   const GemmKind kind = choose_kind(std::max<long long>(R, 1), s.E, s.capacity);
-  const int bm1 = gemm_block_m(kind, s.dtype, true, s.wfmt), bm2 = gemm_block_m(kind, s.dtype, false, s.wfmt);
+  const int bm1 = block_m(s, kind, true), bm2 = block_m(s, kind, false);
   const int nb = route_blocks(s.T);
   int32_t* ts1 = at<int32_t>(ws, L.tstart1);
   int32_t* ts2 = at<int32_t>(ws, L.tstart2);
@@ -420,7 +454,19 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
     MOE_HIP(launch_rank_gather(s.dtype, x, idx, s.T, s.d, s.k, s.E, s.capacity, at<int32_t>(ws, L.chunk_base),
                                offsets, row_token, row_of, nullptr, st));
   MOE_MARK(MOE_STAGE_GATE_UP);
-  if (s.T > 0) {
+  // MXFP8 activations: x is quantised once (per token row) for the routed and shared products
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  uint8_t* xs = xq + (size_t)R * s.d;
+  if (s.afmt == MOE_A_MXFP8 && s.T > 0) {
+    MOE_HIP(launch_mxfp8_quantize(x, s.T, s.d, xq, xs, st));
+    MOE_HIP(launch_gemm_gateup_mx(kind, s.wfmt, xq, xs, row_token, w_gate, w_up, sc.gate, sc.up, offsets, ts1, s.E, 0,
+                                  max_m_tiles(R, s.E, s.capacity, bm1), s.d_e, s.d, at<uint8_t>(ws, L.h),
+                                  at<uint8_t>(ws, L.h) + (size_t)R * s.d_e, st));
+    MOE_MARK(MOE_STAGE_DOWN);
+    MOE_HIP(launch_gemm_down_mx(kind, s.wfmt, at<uint8_t>(ws, L.h), at<uint8_t>(ws, L.h) + (size_t)R * s.d_e, w_down,
+                                sc.down, offsets, ts2, s.E, 0, max_m_tiles(R, s.E, s.capacity, bm2), s.d, s.d_e,
+                                at<float>(ws, L.o), st));
+  } else if (s.T > 0) {
     MOE_HIP(launch_gemm_gateup(kind, s.dtype, s.wfmt, x, row_token, w_gate, w_up, (const float*)sc.gate,
                                (const float*)sc.up, offsets, ts1, s.E, 0, max_m_tiles(R, s.E, s.capacity, bm1), s.d_e,
                                s.d, at<void>(ws, L.h), st));
@@ -431,7 +477,18 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
   }
   MOE_MARK(MOE_STAGE_SHARED_GATE_UP);
   const float* shared_out = nullptr;
-  if (s.d_e_shared > 0 && s.T > 0) {
+  if (s.d_e_shared > 0 && s.T > 0 && s.afmt == MOE_A_MXFP8) {
+    const GemmKind sk = choose_kind(s.T, 1, -1);
+    const int sbm = gemm_block_m_mx(sk);
+    uint8_t* shq = at<uint8_t>(ws, L.sh_h);
+    MOE_HIP(launch_gemm_gateup_mx(sk, s.wfmt, xq, xs, nullptr, ws_gate, ws_up, ssc.gate, ssc.up, nullptr, nullptr, 1,
+                                  s.T, (s.T + sbm - 1) / sbm, s.d_e_shared, s.d, shq,
+                                  shq + (size_t)s.T * s.d_e_shared, st));
+    MOE_MARK(MOE_STAGE_SHARED_DOWN);
+    MOE_HIP(launch_gemm_down_mx(sk, s.wfmt, shq, shq + (size_t)s.T * s.d_e_shared, ws_down, ssc.down, nullptr,
+                                nullptr, 1, s.T, (s.T + sbm - 1) / sbm, s.d, s.d_e_shared, at<float>(ws, L.sh_o), st));
+    shared_out = at<float>(ws, L.sh_o);
+  } else if (s.d_e_shared > 0 && s.T > 0) {
     const GemmKind sk = choose_kind(s.T, 1, -1);
     const int sbm1 = gemm_block_m(sk, s.dtype, true, s.wfmt), sbm2 = gemm_block_m(sk, s.dtype, false, s.wfmt);
     MOE_HIP(launch_gemm_gateup(sk, s.dtype, s.wfmt, x, nullptr, ws_gate, ws_up, (const float*)ssc.gate,
@@ -470,6 +527,15 @@ moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const void
   return moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, scales, shared_scales, y, idx,
                      gate, counts, kept, f, P, aux, offsets, row_token, row_of, ws, (size_t)MOE_STATIC_SCRATCH_BYTES,
                      stream, stage_events);
+}
+
+moe_status moe_mxfp8_quantize(int32_t rows, int32_t K, const void* x, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+  if (rows < 0 || K < 32 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_NULL;
+  MOE_HIP(launch_mxfp8_quantize(x, rows, K, codes, scales, (hipStream_t)stream));
+  return MOE_OK;
 }
 
 moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes) {

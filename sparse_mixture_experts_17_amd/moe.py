@@ -19,9 +19,16 @@ TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 def make_shape(T: int, d: int, d_e: int, E: int, k: int, capacity: int = -1, renormalize: bool = True,
                d_e_shared: int = 0, dtype: int = MOE_BF16, scoring: int = 0, n_group: int = 1,
-               topk_group: int = 1, wfmt: int = 0) -> MoeShape:
+               topk_group: int = 1, wfmt: int = 0, afmt: int = 0) -> MoeShape:
     return MoeShape(T, d, d_e, E, k, capacity, int(bool(renormalize)), d_e_shared, dtype, scoring, n_group,
-                    topk_group, wfmt)
+                    topk_group, wfmt, afmt)
+
+
+def moe_mxfp8_quantize(x, codes, scales, stream=None) -> None:
+    """MXFP8 rows of x [rows, K] (bf16) into codes [rows, K] and scales [rows, K/32] (uint8)."""
+    rows, K = x.shape
+    check("moe_mxfp8_quantize", lib().moe_mxfp8_quantize(rows, K, _ptr(x), _ptr(codes), _ptr(scales),
+                                                         _stream(stream)))
 
 
 def _scales(sc):

@@ -383,6 +383,77 @@ def pin_mxfp8_layer_bruteforce():
         assert 1e-3 < mo.rel_err(res.y, plain.y) < 0.3
 
 
+def pin_silu_range():
+    """SiLU's minimum sits where its derivative vanishes, and silu_range agrees with a dense scan
+    of random intervals (some holding the minimum)."""
+    assert abs(mo.silu_grad(np.float64(mo.SILU_ARGMIN))) < 1e-14
+    g = _rng(81)
+    lo = g.uniform(-4, 3, 300)
+    hi = lo + g.uniform(0, 2, 300)
+    mn, mx = mo.silu_range(lo, hi)
+    for i in range(300):
+        z = np.linspace(lo[i], hi[i], 20001)
+        v = mo.silu(z)
+        assert mn[i] <= v.min() + 1e-15 and abs(mn[i] - v.min()) < 1e-8
+        assert abs(mx[i] - v.max()) < 1e-15
+
+
+def pin_mxfp8_round_interval():
+    """Reachable MXFP8 values: a point interval gives the rounding itself; an element at a rounding
+    midpoint reaches both neighbours; and every row drawn inside the intervals (each element
+    independently, the block scale following the drawn maximum) rounds inside [qlo, qhi] --
+    with intervals that straddle midpoints, zero, and block maxima at powers of two."""
+    g = _rng(82)
+    v = g.standard_normal((6, 64)) * np.exp2(g.integers(-6, 6, (6, 1)))
+    qlo, qhi = mo.mxfp8_round_interval(v, v)
+    assert np.array_equal(qlo, mo.mxfp8_round_rows(v)) and np.array_equal(qhi, qlo)
+    row = np.zeros((1, 32))
+    row[0, 0] = 256.0                                  # scale 2^0
+    row[0, 1] = 1.0625                                 # midpoint of 1.0 and 1.125
+    lo, hi = mo.mxfp8_round_interval(row - 1e-9, row + 1e-9)
+    assert lo[0, 1] == 1.0 and hi[0, 1] == 1.125
+    for trial in range(40):
+        v = g.standard_normal((3, 64)) * np.exp2(g.integers(-4, 4, (3, 1)))
+        v[0, 3] = 2.0 ** g.integers(-3, 4)             # a block maximum right at a power of two
+        r = np.abs(v) * g.uniform(0, 0.05, v.shape) * (g.random(v.shape) < 0.5)
+        lo, hi = v - r, v + r
+        qlo, qhi = mo.mxfp8_round_interval(lo, hi)
+        for _ in range(25):
+            pt = lo + (hi - lo) * g.random(v.shape)
+            ends = g.random(v.shape)
+            pt = np.where(ends < 0.1, lo, np.where(ends > 0.9, hi, pt))     # some elements at an end
+            q = mo.mxfp8_round_rows(pt)
+            assert np.all(q >= qlo) and np.all(q <= qhi)
+        for ends in (lo, hi):                          # the end points themselves
+            q = mo.mxfp8_round_rows(ends)
+            assert np.all(q >= qlo) and np.all(q <= qhi)
+
+
+def pin_swiglu_mx_deviation():
+    """The MXFP8 SwiGLU deviation bound holds for products computed with errors up to eps times
+    the sum of the terms' magnitudes: random such errors in a and b, h rounded from float32,
+    the down product recomputed -- every output within the bound, and some h codes do flip."""
+    g = _rng(83)
+    m, d, de, eps = 24, 64, 96, 3e-3
+    X = mo.mxfp8_round_rows(g.standard_normal((m, d)))
+    wg, wu = g.standard_normal((de, d)) / 8, g.standard_normal((de, d)) / 8
+    wd = g.standard_normal((d, de)) / 10
+    hq, qlo, qhi, bound = mo.swiglu_mx_deviation(X, wg, wu, wd, eps)
+    a, b = X @ wg.T, X @ wu.T
+    A, B = np.abs(X) @ np.abs(wg).T, np.abs(X) @ np.abs(wu).T
+    o = hq @ wd.T
+    flips = 0
+    for _ in range(60):
+        ap = a + eps * A * g.uniform(-1, 1, a.shape)
+        bp = b + eps * B * g.uniform(-1, 1, b.shape)
+        hp = mo.mxfp8_round_rows((mo.silu(ap) * bp).astype(np.float32))
+        assert np.all(hp >= qlo) and np.all(hp <= qhi)
+        flips += int((hp != hq).sum())
+        assert np.all(np.abs(hp @ wd.T - o) <= bound)
+    assert flips > 0
+    assert np.all(bound >= 0)
+
+
 def pin_dispatch_invariants():
     g = _rng(6)
     for (T, E, k, cap) in [(50, 5, 2, -1), (50, 5, 2, 7), (33, 4, 3, 0), (64, 8, 1, 5), (0, 3, 2, 4)]:

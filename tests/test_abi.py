@@ -15,13 +15,13 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
     assert names == sorted(["moe_capacity", "moe_workspace_bytes", "moe_status_str", "moe_route", "moe_permute",
-                            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
+                            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_mxfp8_quantize",
                             "moe_backward_workspace_bytes",
                             "moe_backward"])
     lib = _lib.lib()
@@ -58,6 +58,7 @@ def _shape(**kw):
     (dict(n_group=8, topk_group=1, k=2), 2), (dict(E=256, n_group=128, topk_group=2), 3),
     (dict(wfmt=3), 3), (dict(wfmt=-1), 3), (dict(wfmt=1, dtype=moe.MOE_F32), 3),
     (dict(wfmt=2, dtype=moe.MOE_F32), 3),
+    (dict(afmt=2, wfmt=1, dtype=moe.MOE_BF16), 3), (dict(afmt=-1), 3), (dict(afmt=1, dtype=moe.MOE_BF16), 3),
 ])
 def test_shape_validation(kw, status):
     n = C.c_size_t()
@@ -96,7 +97,8 @@ def test_buffer_resources_cover_32bit_offsets():
 
 
 @pytest.mark.parametrize("kw", [dict(scoring=1), dict(n_group=4, topk_group=2), dict(E=256, k=8, n_group=64,
-                                                                                       topk_group=2, scoring=1)])
+                                                                                       topk_group=2, scoring=1),
+                                dict(afmt=1, wfmt=1, dtype=moe.MOE_BF16), dict(afmt=1, wfmt=2, dtype=moe.MOE_BF16)])
 def test_shape_validation_accepts_router_variants(kw):
     n = C.c_size_t()
     assert _lib.lib().moe_workspace_bytes(C.byref(_shape(**kw)), C.byref(n)) == 0

@@ -68,6 +68,21 @@ SMALL = [
     wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_large_d384", T=1600, d=384, d_e=256, E=4, k=2),
     wl.scaled(BASE["mixtral_prefill_mxfp4"], name="mxfp4_shared", T=300, d=512, d_e=256, E=64, k=6, d_e_shared=256),
+    # MXFP8 activations on the scaled FP8 MFMA, FP8 and MXFP4 weights, in every tile configuration
+    wl.scaled(BASE["mixtral_decode_fp8_mx"], name="mx_fp8_decode_tiles", T=16, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_decode_fp8_mx"], name="mx_mxfp4_decode_tiles", T=16, d=512, d_e=1024, E=8, k=2,
+              weights="mxfp4"),
+    wl.scaled(BASE["mixtral_prefill_fp8_mx"], name="mx_fp8_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_mxfp4_mx"], name="mx_mxfp4_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_fp8_mx"], name="mx_fp8_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_mxfp4_mx"], name="mx_mxfp4_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
+    wl.scaled(BASE["mixtral_prefill_fp8_mx"], name="mx_fp8_large_d384", T=1600, d=384, d_e=256, E=4, k=2),
+    wl.scaled(BASE["deepseek_v3_fp8_mx"], name="mx_fp8_deepseek_small", T=300, d=512, d_e=256, E=256, k=8,
+              d_e_shared=256),
+    wl.scaled(BASE["deepseek_v3_fp8_mx"], name="mx_mxfp4_shared_capacity", T=1100, d=256, d_e=128, E=32, k=4,
+              d_e_shared=384, capacity_factor=1.0, weights="mxfp4"),
+    wl.scaled(BASE["deepseek_v3_grouped"], name="mx_fp8_sigmoid_grouped", T=300, d=512, d_e=256, E=256, k=8,
+              d_e_shared=256, weights="fp8_e4m3", act="mxfp8"),
 ]
 
 
@@ -102,8 +117,9 @@ def test_forward_switch_raw_p():
 # Every element of y is compared at full size (the oracle streams the experts); the quantised
 # prefill and grouped-router variants of the large workloads are compared on 256 sampled tokens.
 FULL = ["tiny_fp32", "switch_capacity", "mixtral_decode", "mixtral_prefill", "deepseek_v3",
-        "mixtral_decode_fp8", "mixtral_decode_mxfp4"]
-SAMPLED = ["deepseek_v3_grouped", "mixtral_prefill_fp8", "deepseek_v3_fp8", "mixtral_prefill_mxfp4"]
+        "mixtral_decode_fp8", "mixtral_decode_mxfp4", "mixtral_decode_fp8_mx"]
+SAMPLED = ["deepseek_v3_grouped", "mixtral_prefill_fp8", "deepseek_v3_fp8", "mixtral_prefill_mxfp4",
+           "mixtral_prefill_fp8_mx", "mixtral_prefill_mxfp4_mx", "deepseek_v3_fp8_mx"]
 
 
 @needs_gpu
@@ -163,13 +179,17 @@ def _upload_i32(a):
 
 
 @needs_gpu
-@pytest.mark.parametrize("variant", ["softmax", "sigmoid_grouped", "fp8_weights", "mxfp4_weights", "many_experts"])
+@pytest.mark.parametrize("variant", ["softmax", "sigmoid_grouped", "fp8_weights", "mxfp4_weights", "many_experts",
+                                     "fp8_mxfp8_act", "mxfp4_mxfp8_act"])
 def test_split_calls_compose(variant):
     """moe_route -> moe_permute -> moe_expert_ffn (+ shared) -> moe_combine equals moe_forward."""
     extra = {"softmax": {}, "fp8_weights": dict(weights="fp8_e4m3"), "mxfp4_weights": dict(weights="mxfp4"),
              "sigmoid_grouped": dict(scoring="sigmoid", n_group=4, topk_group=2, router_bias_var=1e-3),
              # 256 experts: moe_route takes the logits-GEMM router path
-             "many_experts": dict(E=256, k=8)}[variant]
+             "many_experts": dict(E=256, k=8),
+             # moe_expert_ffn quantises x_perm itself; the fused call quantises x and gathers codes
+             "fp8_mxfp8_act": dict(weights="fp8_e4m3", act="mxfp8"),
+             "mxfp4_mxfp8_act": dict(weights="mxfp4", act="mxfp8")}[variant]
     kw = dict(name="split", T=211, d=256, d_e=128, E=16, k=3, d_e_shared=256, capacity_factor=1.1)
     kw.update(extra)
     w = wl.scaled(BASE["deepseek_v3"], **kw)
@@ -196,7 +216,7 @@ def test_split_calls_compose(variant):
     moe.moe_permute(shape, dev.x, idx, kept, offsets, row_token, row_of, x_perm, ws)
     o = torch.zeros((T * k, d), dtype=f32, device="cuda")
     moe.moe_expert_ffn(shape, x_perm, offsets, dev.w_gate, dev.w_up, dev.w_down, dev.scales, o, ws)
-    sshape = moe.make_shape(T, d, w.d_e_shared, 1, 1, dtype=shape.dtype, wfmt=shape.wfmt)
+    sshape = moe.make_shape(T, d, w.d_e_shared, 1, 1, dtype=shape.dtype, wfmt=shape.wfmt, afmt=shape.afmt)
     sws = torch.empty(moe.moe_workspace_bytes(sshape), dtype=torch.uint8, device="cuda")
     s_out = torch.zeros((T, d), dtype=f32, device="cuda")
     soff = _upload_i32([0, T])

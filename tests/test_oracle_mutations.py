@@ -13,7 +13,8 @@ from oracle import moe_oracle as mo
 
 _orig = {name: getattr(mo, name) for name in
          ["softmax", "top_k", "gates", "silu", "swiglu_ffn", "router_logits", "load_balance_stats",
-          "capacity", "dispatch", "near_ties", "near_ties_grouped", "sigmoid", "group_limited_top_k", "route", "e4m3_decode", "e4m3_encode", "mxfp8_quantize_rows", "mxfp8_round_rows",
+          "capacity", "dispatch", "near_ties", "near_ties_grouped", "sigmoid", "group_limited_top_k", "route", "e4m3_decode", "e4m3_encode", "mxfp8_quantize_rows", "mxfp8_round_rows", "silu_range",
+          "mxfp8_round_interval", "swiglu_mx_deviation",
           "dequantize_rows", "e2m1_decode", "e8m0_decode", "dequantize_mx_rows", "silu_grad",
           "swiglu_backward", "router_backward", "moe_backward"]}
 
@@ -362,6 +363,25 @@ def _mxr_identity(v, block=32):
     return np.asarray(v, np.float64)
 
 
+def _sr_no_interior(lo, hi):
+    sl, sh = mo.silu(np.asarray(lo, np.float64)), mo.silu(np.asarray(hi, np.float64))
+    return np.minimum(sl, sh), np.maximum(sl, sh)
+
+
+def _ri_one_scale(lo, hi, block=32):
+    lo = np.asarray(lo, np.float64)
+    hi = np.asarray(hi, np.float64)
+    mid = (lo + hi) / 2
+    q, sc = mo.mxfp8_quantize_rows(mid, block)
+    s = np.repeat(np.exp2(sc.astype(np.float64) - 127), block, axis=1)
+    return mo.e4m3_decode(mo.e4m3_encode(lo / s)) * s, mo.e4m3_decode(mo.e4m3_encode(hi / s)) * s
+
+
+def _dev_no_flips(X, w_g, w_u, w_d, eps):
+    hq, qlo, qhi, _ = _orig["swiglu_mx_deviation"](X, w_g, w_u, w_d, eps)
+    return hq, qlo, qhi, eps * (np.abs(hq) @ np.abs(np.asarray(w_d, np.float64)).T)
+
+
 MUTANTS = [
     ("softmax", _softmax_no_shift), ("softmax", _softmax_wrong_axis),
     ("top_k", _topk_high_index_wins), ("top_k", _topk_smallest), ("top_k", _topk_unsorted_slots),
@@ -384,6 +404,8 @@ MUTANTS = [
     ("e4m3_encode", _enc_ties_away), ("e4m3_encode", _enc_truncate), ("e4m3_encode", _enc_no_saturation),
     ("mxfp8_quantize_rows", _mxq_scale_minus7), ("mxfp8_quantize_rows", _mxq_row_scale),
     ("mxfp8_round_rows", _mxr_identity),
+    ("silu_range", _sr_no_interior), ("mxfp8_round_interval", _ri_one_scale),
+    ("swiglu_mx_deviation", _dev_no_flips),
     ("e2m1_decode", _e2m1_bias2), ("e2m1_decode", _e2m1_no_subnormal), ("e8m0_decode", _e8m0_bias128),
     ("dequantize_mx_rows", _mx_nibbles_swapped), ("dequantize_mx_rows", _mx_scales_transposed),
     ("silu_grad", _silu_grad_sigmoid), ("silu_grad", _silu_grad_sign),

@@ -61,6 +61,7 @@ class Workload:
     topk_group: int = 1        # groups a token may use
     weights: str = "native"    # expert weights: "native" (dtype), "fp8_e4m3" (codes + row scales) or
                                # "mxfp4" (E2M1 codes + E8M0 scales per 32 along the row)
+    act: str | None = None     # activations of the expert products: None (dtype) or "mxfp8"
     note: str = ""
 
 
@@ -92,6 +93,17 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
              note="Mixtral decode batch with MXFP4 expert weights (4-bit E2M1, E8M0 scale per 32)"),
     Workload("mixtral_prefill_mxfp4", T=4096, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="mxfp4",
              note="Mixtral prefill batch with MXFP4 expert weights"),
+    Workload("mixtral_prefill_fp8_mx", T=4096, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="fp8_e4m3",
+             act="mxfp8",
+             note="Mixtral prefill batch, FP8 E4M3 weights and MXFP8 activations (scaled FP8 MFMA)"),
+    Workload("mixtral_prefill_mxfp4_mx", T=4096, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="mxfp4",
+             act="mxfp8",
+             note="Mixtral prefill batch, MXFP4 weights and MXFP8 activations (scaled FP8 x FP4 MFMA)"),
+    Workload("mixtral_decode_fp8_mx", T=16, d=4096, d_e=14336, E=8, k=2, dtype="bf16", weights="fp8_e4m3",
+             act="mxfp8", note="Mixtral decode batch, FP8 E4M3 weights and MXFP8 activations"),
+    Workload("deepseek_v3_fp8_mx", T=4096, d=7168, d_e=2048, E=256, k=8, dtype="bf16", d_e_shared=2048,
+             weights="fp8_e4m3", act="mxfp8",
+             note="DeepSeek-V3-shaped layer, FP8 E4M3 weights and MXFP8 activations"),
 ]}
 
 
