@@ -11,7 +11,9 @@ rows into expert order) on the prefill routing as "secondary_permute", the backw
 of the prefill call as "secondary_backward", and decode with FP8 and MXFP4 expert weights
 as "secondary_fp8" and "secondary_mxfp4", and the two HBM-bound prefill-sized workloads -- the
 Switch top-1 layer with capacity factor 1.25 and the DeepSeek-V3-shaped layer with 256 routed
-experts and a shared expert -- as "secondary_switch" and "secondary_deepseek".  Every line
+experts and a shared expert -- as "secondary_switch" and "secondary_deepseek"; the prefill with
+MXFP8 activations on the scaled FP8 MFMA (FP8 and MXFP4 weights) as "secondary_prefill_fp8_mx"
+and "secondary_prefill_mxfp4_mx".  Every line
 carries routing health (dropped fraction, MaxVio, per-expert counts; with the CPU baseline, the
 oracle's near-tie tokens and how many the GPU routed differently).
 
@@ -34,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at Mixtral shape; % bf16 MFMA peak / % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (also the rate of FP8 x FP4 products)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -354,6 +357,26 @@ def streaming_line(info, kernel_name):
     }
 
 
+def mx_prefill_line(info, fmt):
+    """JSON object of a prefill run on the scaled FP8 MFMA (MXFP8 activations): tokens/s, stages and
+    the gate/up product against the dense FP8 MFMA peak."""
+    w = info["w"]
+    ms = info["total_ms"] / info["steps"]
+    work = layer_work(w, info["R_kept"], info["touched"])
+    gu = info["kernel_ms"]
+    tf = work["flops_gate_up"] / (gu / 1e3) / 1e12
+    return {
+        "workload": w.name, "value": w.T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+        "stages_ms": info["stages"], "ms_per_step_unmarked": info["plain_ms"],
+        "roofline": {"kernel": f"grouped_gemm_mx gate_up (MXFP8 x {fmt}, scaled MFMA)", "bound": "mfma",
+                     "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS,
+                     "traffic": measured_traffic(w.name, "gate_up"), "avg_ms": gu,
+                     "algorithmic": f"4*d*d_e FLOPs per kept row x {info['R_kept']} rows"},
+        "layer_tflops": work["flops_layer"] / (ms / 1e3) / 1e12,
+        "health": health(info),
+    }
+
+
 def secondary_line(dec, fmt):
     """JSON object of a decode run with quantised expert weights."""
     wd = dec["w"]
@@ -585,6 +608,14 @@ def main():
         torch.cuda.empty_cache()
         dec = run_gpu("mixtral_decode_mxfp4", max(a.steps, 20), a.warmup, graph=True)
         line["secondary_mxfp4"] = secondary_line(dec, "MXFP4")
+    if not a.no_secondary and w.name == "mixtral_prefill":
+        for key, name, fmt in (("secondary_prefill_fp8_mx", "mixtral_prefill_fp8_mx", "FP8"),
+                               ("secondary_prefill_mxfp4_mx", "mixtral_prefill_mxfp4_mx", "MXFP4")):
+            print(f"[bench] secondary: {name} (MXFP8 activations, scaled FP8 MFMA)", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+            sec = run_gpu(name, a.steps, a.warmup)
+            line[key] = mx_prefill_line(sec, fmt)
+            del sec
     routed = [(line, info, info["out"].idx.cpu().numpy())]
     if not a.no_secondary and w.name == "mixtral_prefill":
         for key, name, kern in (("secondary_switch", "switch_capacity", "grouped_gemm gate_up (stream tiles)"),
