@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondaries", default="decode,permute,backward,fp8,mxfp4,prefill_mx,switch,deepseek",
+                    help="comma-separated secondary lines to run after the Mixtral prefill line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the reference kernel for "
@@ -572,7 +574,8 @@ def main():
         "stage_rates": stage_rates(info),
         "health": health(info),
     }
-    if not a.no_secondary and w.name == "mixtral_prefill":
+    sec_on = set() if a.no_secondary or w.name != "mixtral_prefill" else set(a.secondaries.split(","))
+    if "decode" in sec_on:
         print("[bench] secondary: mixtral_decode on the same weights", file=sys.stderr, flush=True)
         dec = run_gpu("mixtral_decode", max(a.steps, 20), a.warmup, dev_weights=info["dev"], graph=True)
         wd = dec["w"]
@@ -589,26 +592,29 @@ def main():
             "layer_hbm_frac": dwork["bytes_layer"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
             "health": health(dec),
         }
-    if not a.no_secondary and w.name == "mixtral_prefill":
+    if "permute" in sec_on:
         print("[bench] secondary: moe_permute (split ABI) on the same routing", file=sys.stderr, flush=True)
         line["secondary_permute"] = run_permute(info, max(a.steps, 20), a.warmup)
         torch.cuda.empty_cache()
-    if not a.no_secondary and w.name == "mixtral_prefill":
+    if "backward" in sec_on:
         print("[bench] secondary: backward pass on the same inputs", file=sys.stderr, flush=True)
         line["secondary_backward"] = run_backward(info, a.steps, a.warmup)
         torch.cuda.empty_cache()
-    if not a.no_secondary and w.name == "mixtral_prefill":
-        print("[bench] secondary: mixtral_decode_fp8 (FP8 E4M3 expert weights)", file=sys.stderr, flush=True)
+    if sec_on & {"fp8", "mxfp4", "prefill_mx", "switch", "deepseek"}:
         del info["dev"]
         torch.cuda.empty_cache()
+    if "fp8" in sec_on:
+        print("[bench] secondary: mixtral_decode_fp8 (FP8 E4M3 expert weights)", file=sys.stderr, flush=True)
         dec = run_gpu("mixtral_decode_fp8", max(a.steps, 20), a.warmup)
         line["secondary_fp8"] = secondary_line(dec, "FP8")
         del dec
+    if "mxfp4" in sec_on:
         print("[bench] secondary: mixtral_decode_mxfp4 (MXFP4 expert weights)", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         dec = run_gpu("mixtral_decode_mxfp4", max(a.steps, 20), a.warmup, graph=True)
         line["secondary_mxfp4"] = secondary_line(dec, "MXFP4")
-    if not a.no_secondary and w.name == "mixtral_prefill":
+        del dec
+    if "prefill_mx" in sec_on:
         for key, name, fmt in (("secondary_prefill_fp8_mx", "mixtral_prefill_fp8_mx", "FP8"),
                                ("secondary_prefill_mxfp4_mx", "mixtral_prefill_mxfp4_mx", "MXFP4")):
             print(f"[bench] secondary: {name} (MXFP8 activations, scaled FP8 MFMA)", file=sys.stderr, flush=True)
@@ -617,10 +623,10 @@ def main():
             line[key] = mx_prefill_line(sec, fmt)
             del sec
     routed = [(line, info, info["out"].idx.cpu().numpy())]
-    if not a.no_secondary and w.name == "mixtral_prefill":
-        for key, name, kern in (("secondary_switch", "switch_capacity", "grouped_gemm gate_up (stream tiles)"),
-                                ("secondary_deepseek", "deepseek_v3",
-                                 "grouped_gemm gate_up (stream tiles, 256 routed experts)")):
+    for key, name, kern in (("secondary_switch", "switch_capacity", "grouped_gemm gate_up (stream tiles)"),
+                            ("secondary_deepseek", "deepseek_v3",
+                             "grouped_gemm gate_up (stream tiles, 256 routed experts)")):
+        if name.split("_")[0] in sec_on:
             print(f"[bench] secondary: {name}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
             sec = run_gpu(name, max(a.steps, 10), a.warmup)
