@@ -335,10 +335,15 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     // One K step from LDS stage s: 2 chunks of 64 bytes.  The A fragment of the next
     // subtile (and at the chunk boundary the next chunk's B fragments) is read before
     // the current subtile's MFMAs are issued, so LDS latency hides behind MFMA work.
-    auto compute = [&](const char* As, const char* Bs) {
+    // issue(0) and issue(1) start the global -> LDS loads of later steps (activations, then
+    // weights), each once per step and in that order; the native-weight path places them
+    // between its MFMAs (see the K loop).
+    auto compute = [&](const char* As, const char* Bs, auto&& issue) {
       const int ra = wm * Cfg::WTM + (lane & 15);
       const int rb = wn * Cfg::WTN + (lane & 15);
       if constexpr (WF == 2) {
+        issue(0);
+        issue(1);
         // MXFP4 weights: per 64-element sub-step u, an 8-byte LDS read per weight subtile gives
         // lane group q = lane >> 4 the codes of K elements 16q .. 16q+15 of the sub-step
         // (32 bytes of a row: pieces 2u and 2u+1), and one byte the scale of their block
@@ -379,6 +384,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         }
         return;
       } else if constexpr (WF == 1) {
+        issue(0);
+        issue(1);
         // FP8 weights: per 64-element sub-step u, one 16-byte LDS read per weight subtile gives
         // lane group q = lane >> 4 the codes of K elements 16q .. 16q+15 of the sub-step (piece
         // 4u + q of the row); the MFMA of half h takes 16q + 8h .. 16q + 8h + 7 from both
@@ -445,6 +452,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             }
           }
           a_cur = a_nxt;
+          if (kc == 0 && i == 0) issue(0);
+          if (kc == 0 && i == TM - 1) issue(1);
         }
       }
     };
@@ -467,13 +476,19 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           issue_a<Cfg>(a_slot(fs), (uint32_t)(ks + STAGES - 1) * KB_A, rsA, voffA, wave, lane);
           issue_w(fs, ks + STAGES - 1);
         }
-        compute(a_slot(slot), b_slot(slot));
+        compute(a_slot(slot), b_slot(slot), [](int) {});
         slot = slot + 1 == STAGES ? 0 : slot + 1;
       }
     } else {
       // Weights two K steps ahead, activations one.  Issue order A(0) B(0) B(1), then per
       // step A(ks+1) B(ks+2): when step ks is consumed the only newer loads than A(ks) are
       // those of B(ks+1), so waiting until at most LPS_B are outstanding lands A(ks), B(ks).
+      // Both slots were freed by the barrier at the top of step ks.  The loads start after
+      // the step's first MFMAs rather than straight after the barrier: all waves leave the
+      // barrier together, and a burst of global -> LDS loads there delays the LDS operand
+      // reads that the first MFMAs wait for (measured at the Mixtral prefill shape: activations
+      // after the first subtile row and weights after the first half, 1.56 ms against
+      // 1.70 ms for the gate/up product).
       if (nk > 0) {
         issue_a<Cfg>(a_slot(0), 0, rsA, voffA, wave, lane);
         issue_w(0, 0);
@@ -484,10 +499,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         if (ks + 1 < nk) wait_vmcnt<Cfg::LPS_B>();
         else wait_vmcnt<0>();
         block_barrier();                                // step ks visible; slots of ks-1 free
-        if (ks + 1 < nk) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * KB_A, rsA, voffA, wave, lane);
-        if (ks + 2 < nk)
-          issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
-        compute(a_slot(ks & 1), b_slot(bs));
+        compute(a_slot(ks & 1), b_slot(bs), [&](int part) {
+          if (part == 0) {
+            if (ks + 1 < nk) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * KB_A, rsA, voffA, wave, lane);
+          } else if (ks + 2 < nk) {
+            issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
+          }
+        });
         bs = bs == 2 ? 0 : bs + 1;
       }
     }
