@@ -231,10 +231,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_mx_kernel(GemmArgs a
     const bool up_w = NB == 2 && wave >= Cfg::NW / 2;           // this wave's weight share is W_u's
     const bool up_s = NB == 2 && wave * Cfg::PW_BS >= 4 * BN / 16;
     auto slot = [&](int s) { return lds + s * Cfg::SLOT; };
-    auto issue = [&](int s, int ks) {
+    // part 0: the activations and their scales, part 1: the weights and theirs, 2: both
+    auto issue = [&](int s, int ks, int part) {
       char* sl = slot(s);
-      mx_issue<Cfg::IT_A, Cfg::PW_A, 16>(sl, (uint32_t)ks * 128, rsA, voffA, wave, lane);
-      mx_issue<Cfg::IT_AS, Cfg::PW_AS, 4>(sl + Cfg::A_BYTES, (uint32_t)ks * 4, rsAS, voffAS, wave, lane);
+      if (part != 1) {
+        mx_issue<Cfg::IT_A, Cfg::PW_A, 16>(sl, (uint32_t)ks * 128, rsA, voffA, wave, lane);
+        mx_issue<Cfg::IT_AS, Cfg::PW_AS, 4>(sl + Cfg::A_BYTES, (uint32_t)ks * 4, rsAS, voffAS, wave, lane);
+      }
+      if (part == 0) return;
       mx_issue<Cfg::IT_B, Cfg::PW_B, 16>(sl + Cfg::A_BYTES + Cfg::AS_BYTES, (uint32_t)ks * Cfg::KB_B,
                                          up_w ? rsB1 : rsB0, voffB, wave, lane);
       if constexpr (Cfg::IT_BS > 0)
@@ -253,7 +257,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_mx_kernel(GemmArgs a
 
     // One stage = one 128-element K step: A fragments (two 16-byte pieces per lane) and their
     // scale words once, then per weight subtile its fragment and scale and the MFMAs.
-    auto compute = [&](const char* sl) {
+    // hook(0) and hook(1) run once each, in that order: after the first weight subtile's MFMAs
+    // and after the first half of them.
+    auto compute = [&](const char* sl, auto&& hook) {
       const char* As = sl;
       const char* ASs = sl + Cfg::A_BYTES;
       const char* Bs = sl + Cfg::A_BYTES + Cfg::AS_BYTES;
@@ -299,19 +305,32 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_mx_kernel(GemmArgs a
                                                                               0, sa[i], 0, sb);
             }
           }
+          if (m == 0 && j == 0) hook(0);
+          if (m * TN + j == (NB * TN / 2 > 1 ? NB * TN / 2 - 1 : 0)) hook(1);
         }
     };
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");           // previous tile's stores drained
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
-      if (p < nk) issue(p, p);
+      if (p < nk) issue(p, p, 2);
     int sl = 0;
     for (int ks = 0; ks < nk; ++ks) {
       wait_stage<Cfg::LPS, STAGES>(min(STAGES - 2, nk - 1 - ks));   // step ks has landed
       block_barrier();                                          // ... for every wave; slot ks-1 is free
-      if (ks + STAGES - 1 < nk) issue(sl == 0 ? STAGES - 1 : sl - 1, ks + STAGES - 1);
-      compute(slot(sl));
+      // With a ring of 3 or more the step's loads start between its MFMAs, activations first
+      // (MXFP4 prefill gate/up 0.975 -> 0.945 ms); a 2-slot ring needs them straight after the
+      // barrier to land within one step (FP8: 1.04 against 1.08 ms when spread).
+      const bool more = ks + STAGES - 1 < nk;
+      const int fs = sl == 0 ? STAGES - 1 : sl - 1;
+      if constexpr (STAGES >= 3) {
+        compute(slot(sl), [&](int part) {
+          if (more) issue(fs, ks + STAGES - 1, part);
+        });
+      } else {
+        if (more) issue(fs, ks + STAGES - 1, 2);
+        compute(slot(sl), [](int) {});
+      }
       sl = sl + 1 == STAGES ? 0 : sl + 1;
     }
     __syncthreads();                                            // LDS free for the next tile
