@@ -25,10 +25,8 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 
-# Per-source flags.  The large-tile GEMM keeps its accumulators in VGPRs (MFMA VGPR form)
-# and its operands in AGPRs; with the default heuristic its 4 x 48 accumulator tiles go
-# to AGPRs and every MFMA pays copies.
-FILE_FLAGS = {"grouped_gemm_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# Per-source extra flags (none at present; kept for sources that need their own).
+FILE_FLAGS = {}
 
 
 def sources():

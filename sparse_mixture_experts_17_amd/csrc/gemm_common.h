@@ -318,9 +318,8 @@ static hipError_t launch_kernel(const GemmArgs& a, int max_tiles_m, hipStream_t 
   return hipGetLastError();
 }
 
-// bf16 down projection with many rows per expert (4 waves, 192-row tiles; in
-// grouped_gemm_large.hip).
-hipError_t launch_gemm_large_bf16(const GemmArgs& a, int max_tiles_m, hipStream_t stream);
+// Rows per tile of the bf16 down projection with many rows per expert (the other large
+// tiles take 256).
 constexpr int kLargeBf16BlockM = 192;
 
 }  // namespace moe

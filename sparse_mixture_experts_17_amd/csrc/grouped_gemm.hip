@@ -36,10 +36,15 @@ template <typename T, bool GATED, int WF>
 static hipError_t dispatch_kind(GemmKind kind, GemmArgs a, int max_tiles_m, hipStream_t s) {
   switch (kind) {
     case kGemmLarge:
-      if constexpr (sizeof(T) == 2 && !GATED && WF == 0) return launch_gemm_large_bf16(a, max_tiles_m, s);
       // 8 waves; activations in a 2-deep ring, weights (the HBM stream) in a 3-deep one
       if constexpr (GATED) {
         return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);   // 64x(64+64) per wave
+      } else if constexpr (sizeof(T) == 2 && WF == 0) {
+        // bf16 down: 192-row tiles (48 x 128 per wave).  At the Mixtral prefill shape they make
+        // 2.94 rounds of the grid where 256-row tiles make 2.25 (measured 0.90-0.94 against
+        // 0.99-1.02 ms)
+        if (a.N % 256 == 0) return launch_cfg<T, kLargeBf16BlockM, 256, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);
+        return launch_cfg<T, kLargeBf16BlockM, 128, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);
       } else {
         if (a.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);
         return launch_cfg<T, 256, 128, 4, 2, GATED, 2, 3, WF>(a, max_tiles_m, s);

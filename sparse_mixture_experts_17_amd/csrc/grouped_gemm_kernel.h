@@ -7,8 +7,8 @@
 // stored [out, in], so both operands are read along the contraction dimension.
 //
 // One kernel template, three tile configurations:
-//   large   BM=256, BN=128 (gate/up) or 256 (down), 4x2 waves, 2 LDS stages -- many rows
-//           per expert (MFMA-bound)
+//   large   BM=256, BN=128 (gate/up) or 256 (down; bf16 BM=192), 4x2 waves, activations
+//           2 LDS stages and weights 3 -- many rows per expert (MFMA-bound)
 //   stream  BM=160, BN=128 (gate/up) or 256 (down), 2x4 waves, 3 LDS stages -- ~100-250
 //           rows per expert (weight streaming; an expert's m-tiles run side by side so
 //           its weight tile leaves HBM once)
