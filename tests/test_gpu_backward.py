@@ -32,6 +32,7 @@ CASES = [
     wl.scaled(BASE["mixtral_prefill"], name="bwd_large_tiles_n256", T=2000, d=512, d_e=512, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill"], name="bwd_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill"], name="bwd_large_d384", T=1600, d=384, d_e=256, E=4, k=2),
+    wl.scaled(BASE["mixtral_prefill"], name="bwd_large_short_k", T=1600, d=128, d_e=128, E=4, k=2),
     wl.scaled(BASE["mixtral_decode"], name="bwd_decode_tiles", T=16, d=512, d_e=1024, E=8, k=2),
     wl.scaled(BASE["deepseek_v3"], name="bwd_deepseek_small", T=300, d=512, d_e=256, E=256, k=8, d_e_shared=256),
     wl.scaled(BASE["deepseek_v3"], name="bwd_shared_large", T=1100, d=256, d_e=128, E=32, k=4, d_e_shared=384),

@@ -30,6 +30,9 @@ SMALL = [
     wl.scaled(BASE["mixtral_prefill"], name="mixtral_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill"], name="mixtral_stream_tiles", T=601, d=512, d_e=1024, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill"], name="large_tiles_d384", T=1600, d=384, d_e=256, E=4, k=2),
+    # the shortest contractions (two K steps per tile) through the large and stream rings
+    wl.scaled(BASE["mixtral_prefill"], name="large_tiles_short_k", T=1600, d=128, d_e=128, E=4, k=2),
+    wl.scaled(BASE["mixtral_prefill"], name="stream_tiles_short_k", T=601, d=128, d_e=128, E=8, k=2),
     wl.scaled(BASE["mixtral_decode"], name="mixtral_decode_small", T=16, d=512, d_e=1024, E=8, k=2),
     wl.scaled(BASE["deepseek_v3"], name="deepseek_small", T=300, d=512, d_e=256, E=256, k=8, d_e_shared=256),
     wl.scaled(BASE["deepseek_v3"], name="deepseek_shared_large", T=1100, d=256, d_e=128, E=32, k=4, d_e_shared=384),
@@ -77,6 +80,9 @@ SMALL = [
     wl.scaled(BASE["mixtral_prefill_fp8_mx"], name="mx_fp8_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill_mxfp4_mx"], name="mx_mxfp4_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
     wl.scaled(BASE["mixtral_prefill_fp8_mx"], name="mx_fp8_large_d384", T=1600, d=384, d_e=256, E=4, k=2),
+    # one K step (gate/up, d = 128) and two (down) per tile, 2- and 3-slot rings
+    wl.scaled(BASE["mixtral_prefill_fp8_mx"], name="mx_fp8_large_short_k", T=1600, d=128, d_e=256, E=4, k=2),
+    wl.scaled(BASE["mixtral_prefill_mxfp4_mx"], name="mx_mxfp4_large_short_k", T=1600, d=128, d_e=256, E=4, k=2),
     wl.scaled(BASE["deepseek_v3_fp8_mx"], name="mx_fp8_deepseek_small", T=300, d=512, d_e=256, E=256, k=8,
               d_e_shared=256),
     wl.scaled(BASE["deepseek_v3_fp8_mx"], name="mx_mxfp4_shared_capacity", T=1100, d=256, d_e=128, E=32, k=4,
