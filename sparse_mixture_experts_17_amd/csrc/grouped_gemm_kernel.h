@@ -507,18 +507,104 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       }
       if (nk > 1) issue_w(1, 1);
       int bs = 0;                                       // weight slot of step ks
-      for (int ks = 0; ks < nk; ++ks) {
-        if (ks + 1 < nk) wait_vmcnt<Cfg::LPS_B>();
-        else wait_vmcnt<0>();
-        block_barrier();                                // step ks visible; slots of ks-1 free
-        compute(a_slot(ks & 1), b_slot(bs), [&](int part) {
-          if (part == 0) {
-            if (ks + 1 < nk) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * KB_A, rsA, voffA, wave, lane);
-          } else if (ks + 2 < nk) {
-            issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
+      if constexpr (WF == 0 && EPI == 0 && sizeof(T) == 2) {
+        // Forward bf16 products with native weights: the barrier that makes step ks+1 visible is
+        // taken before step ks's last subtile row, and step ks+1's first fragments are read
+        // while that row's MFMAs run, so no step starts by waiting on LDS.  Every read of step
+        // ks is issued before that barrier (and completed by it), so the slots refilled at
+        // step ks+1 are free as in the loop below; the vmcnt accounting is the same.  (The
+        // backward epilogues keep the loop below: measured slower in this form; fp32 tiles
+        // too: they would spill registers in it.)
+        const int ra = wm * Cfg::WTM + (lane & 15);
+        const int rb = wn * Cfg::WTN + (lane & 15);
+        // swz(r + 16 i, c) = swz(r, c) + 2048 i: one lane offset per operand and chunk
+        const int oA0 = swz(ra, lane >> 4), oA1 = swz(ra, 4 + (lane >> 4));
+        const int oB0 = swz(rb, lane >> 4), oB1 = swz(rb, 4 + (lane >> 4));
+        auto rdA = [&](const char* As, int i, int kc) {
+          return *(const u32x4_t*)(As + (kc ? oA1 : oA0) + i * 2048);
+        };
+        // Gated: only the gate half of a step's first B fragments is read ahead (at the
+        // previous step's tail) and the up half at the top of the step's first subtile row;
+        // reading both ahead needs more than the 256 registers a wave has at 8 waves per CU.
+        auto rdBg = [&](const char* Bs, u32x4_t* b) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) b[j] = *(const u32x4_t*)(Bs + oB0 + j * 2048);
+        };
+        auto rdBu = [&](const char* Bs, u32x4_t* b) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) b[TN + j] = *(const u32x4_t*)(Bs + oB0 + BN * 128 + j * 2048);
+        };
+        auto rdB = [&](const char* Bs, u32x4_t* b, int kc) {
+          const char* p = Bs + (kc ? oB1 : oB0);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            b[j] = *(const u32x4_t*)(p + j * 2048);
+            if constexpr (GATED) b[TN + j] = *(const u32x4_t*)(p + BN * 128 + j * 2048);
           }
-        });
-        bs = bs == 2 ? 0 : bs + 1;
+        };
+        if (nk > 1) wait_vmcnt<Cfg::LPS_B>();
+        else wait_vmcnt<0>();
+        block_barrier();
+        u32x4_t b0[TN * NB], b1[TN * NB], a_cur, a_nxt;
+        if constexpr (GATED) rdBg(b_slot(0), b0);
+        else rdB(b_slot(0), b0, 0);
+        a_cur = rdA(a_slot(0), 0, 0);
+        for (int ks = 0; ks < nk; ++ks) {
+          const char* As = a_slot(ks & 1);
+          const char* Bs = b_slot(bs);
+          const int bsn = bs == 2 ? 0 : bs + 1;
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+              if (GATED && kc == 0 && i == 0) rdBu(Bs, b0);
+              if (i + 1 < TM) {
+                a_nxt = rdA(As, i + 1, kc);
+              } else if (kc == 0) {
+                rdB(Bs, b1, 1);
+                a_nxt = rdA(As, 0, 1);
+              } else if (ks + 1 < nk) {
+                // every LDS read of step ks is issued: make step ks+1 visible and start reading it
+                // while the last subtile row's MFMAs run
+                if (ks + 2 < nk) wait_vmcnt<Cfg::LPS_B>();
+                else wait_vmcnt<0>();
+                block_barrier();
+                if constexpr (GATED) rdBg(b_slot(bsn), b0);
+                else rdB(b_slot(bsn), b0, 0);
+                a_nxt = rdA(a_slot((ks + 1) & 1), 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              const u32x4_t* b = kc == 0 ? b0 : b1;
+              if (!Cfg::SKIP_ROWS || wm * Cfg::WTM + i * 16 < rows) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) Mfma<T>::step(acc0[i][j], a_cur, b[j]);
+                if constexpr (GATED) {
+#pragma unroll
+                  for (int j = 0; j < TN; ++j) Mfma<T>::step(acc1[i][j], a_cur, b[TN + j]);
+                }
+              }
+              a_cur = a_nxt;
+              if (kc == 0 && i == 0 && ks + 1 < nk)
+                issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * KB_A, rsA, voffA, wave, lane);
+              if (kc == 0 && i == TM - 1 && ks + 2 < nk) issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
+            }
+          }
+          bs = bsn;
+        }
+      } else {
+        for (int ks = 0; ks < nk; ++ks) {
+          if (ks + 1 < nk) wait_vmcnt<Cfg::LPS_B>();
+          else wait_vmcnt<0>();
+          block_barrier();                              // step ks visible; slots of ks-1 free
+          compute(a_slot(ks & 1), b_slot(bs), [&](int part) {
+            if (part == 0) {
+              if (ks + 1 < nk) issue_a<Cfg>(a_slot((ks + 1) & 1), (uint32_t)(ks + 1) * KB_A, rsA, voffA, wave, lane);
+            } else if (ks + 2 < nk) {
+              issue_w(bs == 0 ? 2 : bs - 1, ks + 2);
+            }
+          });
+          bs = bs == 2 ? 0 : bs + 1;
+        }
       }
     }
     __syncthreads();                                    // LDS free for the next tile
