@@ -244,6 +244,19 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
       float gr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) gr[q] = rl + q < rows && args.ep_g ? args.ep_g[row0 + rl + q] : 1.f;
+      // Every a and b of the subtile row is loaded before the first store: the compiler cannot
+      // tell the stores below from these loads, and interleaved it waits for each load in turn.
+      float av[Cfg::TN][4], bv[Cfg::TN][4];
+      static_for<0, Cfg::TN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const size_t o = (size_t)(row0 + rl + q) * N + col;
+          av[j][q] = rl + q < rows ? args.ep_a[o] : 0.f;
+          bv[j][q] = rl + q < rows ? args.ep_b[o] : 0.f;
+        }
+      });
       static_for<0, Cfg::TN>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         const int col = nt * Cfg::BN_ + wn * Cfg::WTN + j * 16 + (lane & 15);
@@ -252,8 +265,7 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
         for (int q = 0; q < 4; ++q) {
           if (rl + q < rows) {
             const int row = row0 + rl + q;
-            const size_t o = (size_t)row * N + col;
-            const float a = args.ep_a[o], b = args.ep_b[o], u = acc0[i][j][q];
+            const float a = av[j][q], b = bv[j][q], u = acc0[i][j][q];
             const float sg = sigmoid_fast(a);
             const float silu = a * sg;
             const float h = ElemOut<T>::to_f32(ElemOut<T>::from_f32(silu_mul(a, b)));
