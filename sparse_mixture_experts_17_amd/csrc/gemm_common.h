@@ -138,6 +138,16 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
   using T = typename Cfg::Elem;
   const int N = args.N;
   const int c0 = nt * Cfg::BN_ + wn * Cfg::WTN + (lane & 15);
+  // FP8 row scales of the lane's columns, loaded once: interleaved with the stores below, each
+  // load would wait for the one before (the compiler cannot tell them apart from the stores)
+  float s0[Cfg::WF_ == 1 ? Cfg::TN : 1], s1[Cfg::WF_ == 1 && Cfg::NB == 2 ? Cfg::TN : 1];
+  if constexpr (Cfg::WF_ == 1) {
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) {
+      s0[j] = args.S0[(size_t)g * N + c0 + j * 16];
+      if constexpr (Cfg::NB == 2) s1[j] = args.S1[(size_t)g * N + c0 + j * 16];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
@@ -147,14 +157,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const Acc& acc0
       const size_t o = (size_t)(row0 + r) * N + c0;
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j) {
-        const int col = c0 + j * 16;
         if constexpr (Cfg::WF_ == 1) {                   // row scales of FP8 weights
-          const size_t sc = (size_t)g * N + col;
           if constexpr (Cfg::NB == 2) {
-            const float h = silu_mul(acc0[i][j][q] * args.S0[sc], acc1[i][j][q] * args.S1[sc]);
+            const float h = silu_mul(acc0[i][j][q] * s0[j], acc1[i][j][q] * s1[j]);
             ((T*)args.C)[o + j * 16] = ElemOut<T>::from_f32(h);
           } else {
-            ((float*)args.C)[c_off + o + j * 16] = acc0[i][j][q] * args.S0[sc];
+            ((float*)args.C)[c_off + o + j * 16] = acc0[i][j][q] * s0[j];
           }
         } else if constexpr (Cfg::NB == 2) {
           ((T*)args.C)[o + j * 16] = ElemOut<T>::from_f32(silu_mul(acc0[i][j][q], acc1[i][j][q]));

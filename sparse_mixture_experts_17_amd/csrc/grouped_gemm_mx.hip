@@ -339,6 +339,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_mx_kernel(GemmArgs a
       // h = SiLU(a) * b as MXFP8: per row, the 32 columns of subtiles 2p and 2p+1 form one block
       uint8_t* Hq = (uint8_t*)args.C;
       const int cw = nt * BN + wn * Cfg::WTN;                   // first column of this wave
+      // FP8 row scales of the lane's columns, loaded once (interleaved with the stores, each
+      // load would wait for the one before)
+      float sg[WF == 1 ? TN : 1], su[WF == 1 ? TN : 1];
+      if constexpr (WF == 1) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const size_t sc = (size_t)g * N + cw + j * 16 + r16;
+          sg[j] = ((const float*)args.S0)[sc];
+          su[j] = ((const float*)args.S1)[sc];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -354,9 +365,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_mx_kernel(GemmArgs a
               const int j = 2 * p + e;
               float av = acc0[i][j][q], bv = acc1[i][j][q];
               if constexpr (WF == 1) {
-                const size_t sc = (size_t)g * N + cw + j * 16 + r16;
-                av *= ((const float*)args.S0)[sc];
-                bv *= ((const float*)args.S1)[sc];
+                av *= sg[j];
+                bv *= su[j];
               }
               h[e] = silu_mul(av, bv);
             }
