@@ -70,6 +70,26 @@ __device__ __forceinline__ void block_barrier() {
 // 16-byte reads of one piece by 16 consecutive rows).
 __device__ __forceinline__ int swz64(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
 
+// Largest g in [0, G) with tstart[g] <= mq, for nondecreasing tstart with tstart[0] = 0 <= mq
+// (empty groups repeat their successor's start, so g is the group holding m-tile mq).  A
+// 64-way search: each round every lane reads one candidate and a ballot picks the last one
+// not past mq, so up to 64 groups take one round of dependent loads and up to 4,096 two (a
+// binary search takes log2 G).  Every lane of the wave must be active.
+__device__ __forceinline__ int find_group(const int32_t* __restrict__ tstart, int G, int mq) {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  int base = 0, span = G;                              // the answer lies in [base, base + span)
+  while (span > 1) {
+    const int step = (span + kWave - 1) / kWave;       // candidates base, base + step, ...
+    const int idx = base + lane * step;
+    const bool ok = idx < base + span && tstart[idx] <= mq;
+    const unsigned long long m = __ballot(ok);         // a prefix of the lanes; lane 0 is set
+    const int end = base + span;
+    base += (63 - __builtin_clzll(m)) * step;
+    span = min(step, end - base);
+  }
+  return base;
+}
+
 struct TileCoord {
   int g, nt, row0, rows;   // group (expert), n-tile, first row, valid rows (<= BM)
 };
@@ -93,12 +113,7 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& args, int L, int
   const int mq = L / ntn;                              // any m-tile index in L's group range
   int g = 0, t0g = 0, t1g = mt_live;
   if (offsets) {
-    int a = 0, b = args.G - 1;                         // largest g with tstart[g] <= mq
-    while (a < b) {
-      int mid = (a + b + 1) >> 1;
-      if (tstart[mid] <= mq) a = mid; else b = mid - 1;
-    }
-    g = a;
+    g = find_group(tstart, args.G, mq);
     t0g = tstart[g];
     t1g = tstart[g + 1];
   }
