@@ -25,8 +25,10 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 
-# Per-source extra flags (none at present; kept for sources that need their own).
-FILE_FLAGS = {}
+# Per-source extra flags.  grouped_gemm.hip: the atomic that draws a dynamically scheduled
+# block's next tile runs on one lane and its result is used only after the tile's epilogue; the
+# atomic optimizer would rewrite it into a wave-wide form that reads the result back at once.
+FILE_FLAGS = {"grouped_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def sources():

@@ -40,6 +40,11 @@ struct GemmArgs {
   // a_rows like A), and of the gated product's MXFP8 output h [rows, N/32] (C then holds E4M3 codes)
   const uint8_t* a_scales = nullptr;
   uint8_t* c_scales = nullptr;
+  // Work counters of a dynamically scheduled product (kNumXcd ints, zero at launch), or NULL for
+  // the static walk.  Dynamic: a block's first tile is its static one; after that each block
+  // takes the next tile of its XCD's range from its XCD's counter, so blocks that drew cheap
+  // tiles (an expert's last, partly empty m-tile) take more of them.
+  int32_t* tile_ctr = nullptr;
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
@@ -336,9 +341,9 @@ __device__ __forceinline__ void store_dgrad(const GemmArgs& args, const Acc& acc
 template <typename Cfg, void (*KERN)(GemmArgs)>
 static hipError_t launch_kernel(const GemmArgs& a, int max_tiles_m, hipStream_t stream) {
   static const int occ = [] {
-    (void)hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+    (void)hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_ALLOC);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERN, Cfg::NT, Cfg::LDS) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERN, Cfg::NT, Cfg::LDS_ALLOC) != hipSuccess || n < 1) n = 1;
     return n;
   }();
   int dev = 0, cus = 256;
@@ -349,7 +354,7 @@ static hipError_t launch_kernel(const GemmArgs& a, int max_tiles_m, hipStream_t 
   long long grid = std::min<long long>(max_live, (long long)cus * occ);
   grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid < kNumXcd) grid = kNumXcd;
-  hipLaunchKernelGGL(KERN, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS, stream, a);
+  hipLaunchKernelGGL(KERN, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS_ALLOC, stream, a);
   return hipGetLastError();
 }
 

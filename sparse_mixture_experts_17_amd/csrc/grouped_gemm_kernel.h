@@ -70,6 +70,10 @@ struct GemmTile {
   static constexpr int A_SLOT = BM * ROWB, A_STAGE = KSUB * A_SLOT, B_SLOT = BROWS * ROWB_B + S_BYTES;
   static constexpr int B_BASE = STAGES * A_STAGE;
   static constexpr int LDS = STAGES * A_STAGE + BSTAGES * B_SLOT;
+  // Forward tiles with 16 bytes of LDS to spare can be scheduled dynamically (GemmArgs::tile_ctr):
+  // the block's next tile index passes from its first thread to the others there.
+  static constexpr bool DYN = EPI == 0 && LDS + 16 <= 160 * 1024;
+  static constexpr int LDS_ALLOC = LDS + (DYN ? 16 : 0);
   static constexpr int NW = WM * WN;
   // 16-byte global -> LDS pieces per K step: activations, weights, MXFP4 scales.  Each wave
   // loads a contiguous equal share of every kind (PW_* pieces, IT_* instructions of up to 64
@@ -262,7 +266,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   constexpr uint32_t KB_B = Cfg::ROWB_B;              // weight bytes per row per stage
   constexpr uint32_t KB_A = 128 * KSUB;               // activation bytes per row per stage
 
-  for (int L = lo + j0; L < hi; L += bpx) {
+  // Dynamic scheduling: the ticket for the block's next tile is drawn after the K loop and
+  // read once the epilogue's stores are issued; each tile waits for its predecessor's stores
+  // to drain anyway, so the atomic's round trip hides behind them.
+  const bool dyn = Cfg::DYN && args.tile_ctr != nullptr;
+  int* ticket = (int*)(lds + Cfg::LDS);
+  for (int L = lo + j0, Lnext = 0; L < hi; L = Lnext) {
     // consecutive work items are the K chunks of one output tile
     const int chunk = ksp > 1 ? L % ksp : 0;
     int g, nt, row0, rows, nk = nks;
@@ -608,6 +617,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       }
     }
     __syncthreads();                                    // LDS free for the next tile
+    int nxt = 0;
+    if (dyn && tid == 0) nxt = atomicAdd(args.tile_ctr + xcd, 1);
 
     if constexpr (EPI == 1)
       store_save_ab<Cfg>(args, acc0, acc1, wm, wn, lane, g, nt, row0, rows);
@@ -615,6 +626,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       store_dgrad<Cfg>(args, acc0, wm, wn, lane, g, nt, row0, rows);
     else
       store_tile<Cfg>(args, acc0, acc1, wm, wn, lane, g, nt, row0, rows, c_off);
+    if (dyn) {
+      // tiles [lo, lo + bpx) are the blocks' first ones; tickets number the rest in order
+      if (tid == 0) *ticket = nxt;
+      __syncthreads();
+      Lnext = lo + bpx + *ticket;
+    } else {
+      Lnext = L + bpx;
+    }
   }
 }
 

@@ -118,6 +118,7 @@ struct MxTile {
   static constexpr int B_BYTES = BROWS * KB_B, BS_BYTES = WF == 2 ? 4 * BROWS : 0;
   static constexpr int SLOT = A_BYTES + AS_BYTES + B_BYTES + BS_BYTES;
   static constexpr int LDS = STAGES * SLOT;
+  static constexpr int LDS_ALLOC = LDS;
   // global -> LDS pieces per stage: activation codes (16 B), activation scales (4 B per row),
   // weight codes (16 B), MXFP4 weight scales (16 B = one block's scales of 16 rows)
   static constexpr int P_A = BM * 8, P_AS = BM, P_B = BROWS * PPR_B, P_BS = BS_BYTES / 16;

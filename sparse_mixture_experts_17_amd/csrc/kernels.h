@@ -10,6 +10,8 @@ namespace moe {
 
 // Tokens per router block; also the chunk size of the dispatch counting sort.
 constexpr int kRouteTokens = 16;
+// Work counters of a dynamically scheduled grouped GEMM: one per XCD.
+constexpr int kTileCtrInts = 8;
 
 inline int route_blocks(int T) { return (T + kRouteTokens - 1) / kRouteTokens; }
 
@@ -103,9 +105,12 @@ hipError_t launch_gemm_gateup(GemmKind kind, int dtype, int wfmt, const void* A,
                               int N, int K, void* H, hipStream_t stream);
 
 // Down projection:  o[r, n] = H_e W_d[e]^T, fp32 out (times Sd[e, n] for FP8 weights).
+// tile_ctr: kTileCtrInts ints of workspace for dynamic tile scheduling (zeroed by this call, on
+// `stream`), or NULL; only the large bf16 tiles use it.
 hipError_t launch_gemm_down(GemmKind kind, int dtype, int wfmt, const void* H, const void* Wd, const float* Sd,
                             const int32_t* offsets, const int32_t* tstart, int G, int dense_rows, int max_tiles_m,
-                            int N, int K, float* O, int ksplit, size_t split_stride, hipStream_t stream);
+                            int N, int K, float* O, int ksplit, size_t split_stride, hipStream_t stream,
+                            int32_t* tile_ctr = nullptr);
 
 // ---- FP8 products with MXFP8 activations (grouped_gemm_mx.hip)
 // OCP MXFP8 of the rows of x [rows, K] (bf16): codes [rows, K] E4M3, scales [rows, K/32] E8M0,

@@ -40,7 +40,7 @@ int down_ksplit(const moe_shape& s, GemmKind kind) {
 
 struct Layout {
   size_t p_part, hist, chunk_base, counts, kept, offsets, row_token, row_of, tstart1, tstart2, logits;
-  size_t x_perm, xq, h, o, sh_h, sh_o, total;
+  size_t x_perm, xq, h, o, sh_h, sh_o, tctr, total;
   int ksplit;   // K chunks of the routed down product in the forward (partials at o + c * T*k*d)
 };
 
@@ -73,6 +73,7 @@ Layout layout(const moe_shape& s) {
   L.o = take(R * (size_t)s.d * sizeof(float) * (size_t)L.ksplit);
   L.sh_h = take((size_t)s.T * (size_t)s.d_e_shared * es);
   L.sh_o = take(s.d_e_shared > 0 ? (size_t)s.T * (size_t)s.d * sizeof(float) : 0);
+  L.tctr = take(kTileCtrInts * sizeof(int32_t));   // work counters of the routed down product
   L.total = off;
   return L;
 }
@@ -81,7 +82,7 @@ Layout layout(const moe_shape& s) {
 // expert's rows from a 64-aligned column (ldt bounds the padded total).
 struct BwdLayout {
   size_t poff, koff_dense, ts1, ts2, g_row, wdT, wguT, dyb, a, b, hT, dab, dabT, part, dr, dX, xT, doT;
-  size_t swdT, swguT, sa, sb, shT, sdab, sdabT, sdX, sdyT, sxT, dwr_part, logits, total;
+  size_t swdT, swguT, sa, sb, shT, sdab, sdabT, sdX, sdyT, sxT, dwr_part, logits, tctr, total;
   int ldt, ldts, npart;
   GemmKind kind, skind;
 };
@@ -129,6 +130,7 @@ BwdLayout bwd_layout(const moe_shape& s) {
   L.sxT = take(des > 0 ? d * ldts * es : 0);
   L.dwr_part = take(dwr_workspace_bytes(s.T, s.d, s.E));
   L.logits = take(router_logits_bytes(s.T, s.d, s.E));
+  L.tctr = take(kTileCtrInts * sizeof(int32_t));   // work counters of the routed dX product
   L.total = off;
   return L;
 }
@@ -473,7 +475,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* w_r, c
     MOE_MARK(MOE_STAGE_DOWN);
     MOE_HIP(launch_gemm_down(kind, s.dtype, s.wfmt, at<void>(ws, L.h), w_down, (const float*)sc.down, offsets, ts2, s.E, 0,
                              max_m_tiles(R, s.E, s.capacity, bm2), s.d, s.d_e, at<float>(ws, L.o), L.ksplit,
-                             (size_t)R * s.d, st));
+                             (size_t)R * s.d, st, at<int32_t>(ws, L.tctr)));
   }
   MOE_MARK(MOE_STAGE_SHARED_GATE_UP);
   const float* shared_out = nullptr;
@@ -625,7 +627,7 @@ moe_status moe_backward(const moe_shape* shape, const void* x, const void* w_r, 
   MOE_MARK(MOE_BSTAGE_DX_EXPERT);
   if (T > 0)
     MOE_HIP(launch_gemm_down(kind, s.dtype, 0, dab, wguT, nullptr, offsets, ts2, E, 0, tiles2, d, 2 * de, dX, 1, 0,
-                             st));
+                             st, at<int32_t>(ws, L.tctr)));
   MOE_MARK(MOE_BSTAGE_WGRAD_DOWN);
   MOE_HIP(launch_gather_t(0, s.dtype, dy, d, row_token, g_row, offsets, poff, E, 0, L.ldt, at<void>(ws, L.doT), L.ldt,
                           st));
