@@ -24,6 +24,8 @@ CASES = [
     wl.scaled(BASE["deepseek_v3"], name="graph_many_experts", T=300, d=512, d_e=256, E=256, k=8, d_e_shared=256),
     # MXFP4 decode with the down product in two K chunks
     wl.scaled(BASE["mixtral_decode_mxfp4"], name="graph_mxfp4_ksplit", T=16, d=384, d_e=2048, E=8, k=2),
+    # large tiles: the down product scheduled from work counters that a kernel in the graph zeroes
+    wl.scaled(BASE["mixtral_prefill"], name="graph_large_tiles", T=2000, d=256, d_e=384, E=8, k=2),
 ]
 FIELDS = ["y", "idx", "gate", "counts", "kept", "f", "P", "aux", "offsets", "row_of"]
 
