@@ -727,27 +727,26 @@ __global__ __launch_bounds__(256) void rank_gather_kernel(const T* __restrict__ 
   const int total_all = n * P;
   const int lo = (int)((long long)total_all * blockIdx.y / gridDim.y);
   const int total = (int)((long long)total_all * (blockIdx.y + 1) / gridDim.y);
+  // The U loads of an iteration are unconditional, so they are all in flight together (a load
+  // under a condition waits for the ones before it): a piece past the end re-reads the last
+  // one, and a dropped token's piece is read too, and neither is stored.
   constexpr int U = 4;
+  if (total <= lo) return;
   for (int base = lo + tid; base < total; base += 256 * U) {
     u32x4_t v[U];
-    int dst[U];
+    long long dst[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int it = base + u * 256;
-      dst[u] = -1;
-      if (it < total) {
-        const int item = it / P, piece = it - item * P;
-        const int row = s_row[item];
-        if (row >= 0) {
-          const int t = t0 + item / k;
-          v[u] = *((const u32x4_t*)((const char*)x + (size_t)t * d * sizeof(T)) + piece);
-          dst[u] = row * P + piece;   // in 16-byte units
-        }
-      }
+      const int it = min(base + u * 256, total - 1);
+      const int item = it / P, piece = it - item * P;
+      const int t = t0 + item / k;
+      v[u] = *((const u32x4_t*)((const char*)x + (size_t)t * d * sizeof(T)) + piece);
+      const int row = s_row[item];
+      dst[u] = base + u * 256 < total && row >= 0 ? (long long)row * P + piece : -1;   // 16-byte units
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (dst[u] >= 0) ((u32x4_t*)x_perm)[(size_t)dst[u]] = v[u];
+      if (dst[u] >= 0) ((u32x4_t*)x_perm)[dst[u]] = v[u];
   }
 }
 
